@@ -1,0 +1,66 @@
+"""Run a whole workload through the oracle (test infrastructure).
+
+The step order follows "Continuous batching: Qwen3.8-27B at 301 tok/s ..."
+(lucebox blog) §Chunked prefill is a slot phase: the step's tokens are
+appended to each slot's paged KV, then every packed row attends over its
+slot's history.  The pool starts filled with NaN so that any read of an
+unwritten position shows up in the result.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .block_pool import BlockPool
+from .attention import append_reference, paged_attention
+
+NAN_BITS = {"f32": (np.uint32, 0x7FC00000, np.float32), "bf16": (np.uint16, 0x7FC0, np.uint16)}
+
+
+def poisoned_pool(w):
+    utype, bits, store = NAN_BITS[w.dtype]
+    shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    return np.full(shape, bits, dtype=utype).view(store)
+
+
+def apply_ops(pool: BlockPool, ops):
+    for op in ops:
+        if op[0] == "acquire":
+            pool.acquire(op[1])
+        elif op[0] == "release":
+            pool.release(op[1])
+        elif op[0] == "truncate":
+            pool.truncate(op[1], op[2])
+        else:
+            raise ValueError(op)
+
+
+def place_history(w, alloc: BlockPool, pk, pv):
+    """Acquire every history slot and append its prior tokens (not attended)."""
+    for slot, _, _ in w.history:
+        alloc.acquire(slot)
+    entries = [(slot, len(k)) for slot, k, _ in w.history if len(k) > 0]
+    if entries:
+        meta = alloc.lower_step(entries)
+        hk = np.concatenate([k for _, k, _ in w.history if len(k) > 0])
+        hv = np.concatenate([v for _, _, v in w.history if len(v) > 0])
+        pk, pv = append_reference(pk, pv, meta["slot_mapping"], hk, hv, w.block_size)
+    return pk, pv
+
+
+def run_workload(w, steps=None):
+    """Returns a list with, per step: dict(meta=..., out=fp64 [T][Hq][D])."""
+    alloc = BlockPool(w.num_blocks, w.block_size, w.max_slots, w.max_blocks_per_seq, w.free_order)
+    pk, pv = poisoned_pool(w), poisoned_pool(w)
+    pk, pv = place_history(w, alloc, pk, pv)
+    results = []
+    for i, st in enumerate(w.steps):
+        if steps is not None and i not in steps:
+            break
+        apply_ops(alloc, st.ops)
+        meta = alloc.lower_step([(s.slot, s.n) for s in st.segments])
+        pk, pv = append_reference(pk, pv, meta["slot_mapping"], st.k_new, st.v_new, w.block_size)
+        out = paged_attention(st.q, pk, pv, w.dtype, w.block_size, meta["block_tables"],
+                              meta["context_lens"], meta["row_to_slot"], meta["query_start"],
+                              meta["query_len"], w.scale)
+        results.append(dict(meta=meta, out=out))
+    return results, (pk, pv)

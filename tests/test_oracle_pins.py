@@ -1,0 +1,427 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+* brute force: a scalar loop with math.exp over hand-placed tiny pools;
+* a library routine: torch CPU scaled_dot_product_attention in fp64 with its
+  own lower-right causal mask and its own GQA grouping;
+* closed forms (one key, constant V, q = 0, a dominant key, GQA twins);
+* invariants from the pages (physical placement, chunking, slot reuse);
+* the pages' worked block-table example (tests/golden/).
+A last group plants plausible mistakes in the oracle and checks that the pins
+above catch each one.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from torch.nn.attention.bias import causal_lower_right
+
+import oracle
+from oracle import attention as pa
+from oracle.block_pool import BlockPool, NoSpace, pool_blocks_for_tokens
+from oracle.step import run_workload
+from workloads import bf16_bits_from_f32, make_custom, make_workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------- helpers
+def logical_kv(w):
+    """Per slot: the logical [L][Hkv][D] K and V after step 0 (history + new)."""
+    out = {}
+    st = w.steps[0]
+    row = 0
+    news = {}
+    for seg in st.segments:
+        news[seg.slot] = (st.k_new[row:row + seg.n], st.v_new[row:row + seg.n])
+        row += seg.n
+    for slot, hk, hv in w.history:
+        nk, nv = news.get(slot, (hk[:0], hv[:0]))
+        out[slot] = (np.concatenate([hk, nk]), np.concatenate([hv, nv]))
+    return out
+
+
+def sdpa_reference(w):
+    """torch CPU fp64 SDPA over each sequence's logical K/V (no paging)."""
+    kv = logical_kv(w)
+    st = w.steps[0]
+    q = pa.decode_values(st.q, w.dtype)
+    out = np.empty_like(q)
+    row = 0
+    for seg in st.segments:
+        k, v = kv[seg.slot]
+        L = len(k)
+        qt = torch.from_numpy(q[row:row + seg.n]).permute(1, 0, 2)[None]              # [1][Hq][n][D]
+        kt = torch.from_numpy(pa.decode_values(k, w.dtype)).permute(1, 0, 2)[None]     # [1][Hkv][L][D]
+        vt = torch.from_numpy(pa.decode_values(v, w.dtype)).permute(1, 0, 2)[None]
+        o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=causal_lower_right(seg.n, L),
+                                           scale=w.scale, enable_gqa=True)
+        out[row:row + seg.n] = o[0].permute(1, 0, 2).numpy()
+        row += seg.n
+    return out
+
+
+def brute_force(q, k, v, scale, n_rows, L):
+    """Scalar loops: row i of n sits at position L-n+i; head h reads KV head
+    h*Hkv//Hq... written as the group index of h among Hq/Hkv equal groups."""
+    hq, d = q.shape[1], q.shape[2]
+    hkv = k.shape[1]
+    per = hq // hkv
+    out = np.zeros((n_rows, hq, d))
+    for i in range(n_rows):
+        last = L - n_rows + i
+        for h in range(hq):
+            g = 0
+            while (g + 1) * per <= h:
+                g += 1
+            scores = []
+            for j in range(last + 1):
+                acc = 0.0
+                for e in range(d):
+                    acc += float(q[i, h, e]) * float(k[j, g, e])
+                scores.append(acc * scale)
+            mx = max(scores)
+            ws = [math.exp(s - mx) for s in scores]
+            tot = sum(ws)
+            for e in range(d):
+                out[i, h, e] = sum(ws[j] * float(v[j, g, e]) for j in range(last + 1)) / tot
+    return out
+
+
+def run_step0(w):
+    res, pools = run_workload(w, steps={0})
+    return res[0], pools
+
+
+# --------------------------------------------------------------- decoding
+def test_bf16_decode_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x4049, 0x0000, 0x8000], dtype=np.uint16)
+    vals = pa.decode_values(bits, "bf16")
+    assert list(vals) == [1.0, -2.0, 0.25, 3.140625, 0.0, -0.0]
+
+
+def test_bf16_rounding_ties_to_even():
+    # 1 + 2^-8 is a tie between 1.0 and 1 + 2^-7 -> even mantissa (1.0).
+    # 1 + 3*2^-8 is a tie between 1+2^-7 and 1+2^-6 -> even (1 + 2^-6).
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20], dtype=np.float32)
+    got = pa.decode_values(bf16_bits_from_f32(x), "bf16")
+    assert list(got) == [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7]
+
+
+# --------------------------------------------------------------- brute force
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_tiny(seed):
+    """Two sequences in a 6-block pool (block size 2) placed by hand at
+    shuffled blocks; one decode row and one 3-row causal segment."""
+    rng = np.random.default_rng(seed)
+    bs, hq, hkv, d = 2, 2, 1, 4
+    lens = {0: 5, 1: 4}
+    nrows = {0: 1, 1: 3}
+    pool_k = np.full((6, hkv, bs, d), np.nan, dtype=np.float32)
+    pool_v = np.full((6, hkv, bs, d), np.nan, dtype=np.float32)
+    tables = np.zeros((2, 3), dtype=np.int32)
+    phys = rng.permutation(6)
+    logical = {}
+    used = 0
+    for s in (0, 1):
+        L = lens[s]
+        k = rng.standard_normal((L, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((L, hkv, d)).astype(np.float32)
+        logical[s] = (k, v)
+        for j in range(-(-L // bs)):
+            tables[s, j] = phys[used]
+            used += 1
+        for p in range(L):
+            pool_k[tables[s, p // bs], :, p % bs, :] = k[p]
+            pool_v[tables[s, p // bs], :, p % bs, :] = v[p]
+    q = rng.standard_normal((4, hq, d)).astype(np.float32)
+    scale = 0.37
+    out = pa.paged_attention(q, pool_k, pool_v, "f32", bs, tables, np.array([5, 4]),
+                             np.array([0, 1]), np.array([0, 1]), np.array([1, 3]), scale)
+    ref0 = brute_force(q[0:1], *logical[0], scale, 1, 5)
+    ref1 = brute_force(q[1:4], *logical[1], scale, 3, 4)
+    np.testing.assert_allclose(out[0:1], ref0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out[1:4], ref1, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------- library routine
+MIXED = [(3, 40, 1), (0, 16, 1), (5, 0, 37), (1, 33, 20), (2, 15, 1), (4, 63, 2)]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 8, 2, 64), ("bf16", 6, 2, 32), ("bf16", 5, 1, 16),
+                                            ("f32", 4, 4, 8)])
+def test_paged_equals_contiguous_sdpa(dtype, hq, hkv, d):
+    w = make_custom(MIXED, dtype=dtype, hq=hq, hkv=hkv, d=d, seed=11)
+    r, _ = run_step0(w)
+    np.testing.assert_allclose(r["out"], sdpa_reference(w), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["1", "1+1", "2"])
+def test_configs_equal_contiguous_sdpa(name):
+    w = make_workload(name)
+    r, _ = run_step0(w)
+    np.testing.assert_allclose(r["out"], sdpa_reference(w), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------- closed forms
+def _single(seq_len, n, q, k, v, scale=0.5, bs=4):
+    """Place one sequence contiguously (identity table) and attend."""
+    hkv, d = k.shape[1], k.shape[2]
+    nb = -(-seq_len // bs)
+    pk = np.full((nb + 1, hkv, bs, d), np.nan)
+    pv = np.full((nb + 1, hkv, bs, d), np.nan)
+    for p in range(seq_len):
+        pk[p // bs, :, p % bs] = k[p]
+        pv[p // bs, :, p % bs] = v[p]
+    table = np.arange(nb + 1, dtype=np.int32)[None]
+    return pa.paged_attention(q.astype(np.float32), pk.astype(np.float32), pv.astype(np.float32), "f32", bs,
+                              table, np.array([seq_len]), np.array([0]), np.array([0]), np.array([n]), scale)
+
+
+def test_closed_form_single_key_is_v0():
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((1, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((1, 2, 8)).astype(np.float32)
+    q = rng.standard_normal((1, 4, 8)).astype(np.float32)
+    out = _single(1, 1, q, k, v)
+    for h in range(4):
+        assert np.array_equal(out[0, h], v[0, h // 2].astype(np.float64))
+
+
+def test_closed_form_constant_v_and_zero_q():
+    rng = np.random.default_rng(4)
+    L = 23
+    k = rng.standard_normal((L, 1, 8)).astype(np.float32)
+    c = rng.standard_normal(8).astype(np.float32)
+    v_const = np.broadcast_to(c, (L, 1, 8)).copy()
+    q = rng.standard_normal((3, 2, 8)).astype(np.float32)
+    out = _single(L, 3, q, k, v_const)
+    np.testing.assert_allclose(out, np.broadcast_to(c.astype(np.float64), out.shape), rtol=0, atol=1e-14)
+    # q = 0: every visible key weighs the same, so the output is the mean of visible V.
+    v = rng.standard_normal((L, 1, 8)).astype(np.float32)
+    out0 = _single(L, 3, np.zeros((3, 2, 8), np.float32), k, v)
+    for i in range(3):
+        vis = L - 3 + i + 1
+        np.testing.assert_allclose(out0[i, 0], v[:vis, 0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_closed_form_dominant_key():
+    rng = np.random.default_rng(5)
+    L = 30
+    k = (0.01 * rng.standard_normal((L, 1, 8))).astype(np.float32)
+    v = rng.standard_normal((L, 1, 8)).astype(np.float32)
+    q = np.zeros((1, 1, 8), np.float32)
+    q[0, 0, 0] = 10.0
+    k[17, 0, 0] = 40.0            # score 400 * scale above the others
+    out = _single(L, 1, q, k, v, scale=1.0)
+    np.testing.assert_allclose(out[0, 0], v[17, 0], rtol=0, atol=1e-12)
+
+
+def test_closed_form_gqa_twins_identical():
+    w = make_custom([(0, 50, 1), (1, 20, 5)], dtype="bf16", hq=8, hkv=2, d=16, seed=9)
+    st = w.steps[0]
+    st.q[:, 1] = st.q[:, 0]          # heads 0 and 1 share KV head 0
+    st.q[:, 5] = st.q[:, 4]          # heads 4 and 5 share KV head 1
+    r, _ = run_step0(w)
+    assert np.array_equal(r["out"][:, 1], r["out"][:, 0])
+    assert np.array_equal(r["out"][:, 5], r["out"][:, 4])
+
+
+# --------------------------------------------------------------- invariants
+def test_block_permutation_invariance_bitwise():
+    w1 = make_custom(MIXED, dtype="bf16", hq=4, hkv=2, d=32, seed=21)
+    w2 = make_custom(MIXED, dtype="bf16", hq=4, hkv=2, d=32, seed=21)
+    w2.free_order = np.random.default_rng(99).permutation(w2.num_blocks).astype(np.int32)
+    r1, _ = run_step0(w1)
+    r2, _ = run_step0(w2)
+    assert not np.array_equal(r1["meta"]["block_tables"], r2["meta"]["block_tables"])
+    assert np.array_equal(r1["out"], r2["out"])
+
+
+def _prompt_in_chunks(chunks, total, seed=31, bs=16, hq=4, hkv=2, d=16):
+    """One prompt of `total` tokens attended in the given chunk sizes; returns
+    the concatenated rows."""
+    rng = np.random.default_rng(seed)
+    k = bf16_bits_from_f32(rng.standard_normal((total, hkv, d), dtype=np.float32))
+    v = bf16_bits_from_f32(rng.standard_normal((total, hkv, d), dtype=np.float32))
+    q = bf16_bits_from_f32(rng.standard_normal((total, hq, d), dtype=np.float32))
+    nb = -(-total // bs) + 3
+    alloc = BlockPool(nb, bs, 1, nb, rng.permutation(nb))
+    pk = np.full((nb, hkv, bs, d), 0x7FC0, np.uint16)
+    pv = pk.copy()
+    alloc.acquire(0)
+    outs, pos = [], 0
+    for c in chunks:
+        meta = alloc.lower_step([(0, c)])
+        pk, pv = pa.append_reference(pk, pv, meta["slot_mapping"], k[pos:pos + c], v[pos:pos + c], bs)
+        outs.append(pa.paged_attention(q[pos:pos + c], pk, pv, "bf16", bs, meta["block_tables"],
+                                       meta["context_lens"], meta["row_to_slot"], meta["query_start"],
+                                       meta["query_len"], 0.25))
+        pos += c
+    return np.concatenate(outs)
+
+
+def test_chunking_invariance():
+    """One 96-row prompt segment equals the same prompt in three 32-row steps
+    (lucebox blog §Chunked prefill: C[0:512], C[512:1024], ...), and a row
+    split as 95 rows + one decode row."""
+    whole = _prompt_in_chunks([96], 96)
+    np.testing.assert_allclose(_prompt_in_chunks([32, 32, 32], 96), whole, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(_prompt_in_chunks([50, 45, 1], 96), whole, rtol=0, atol=1e-13)
+
+
+def test_segment_order_and_slot_relabel_invariance():
+    base = [(0, 40, 1), (3, 25, 7), (7, 10, 1)]
+    w1 = make_custom(base, seed=41, d=16)
+    r1, _ = run_step0(w1)
+    # Same data, slots relabelled (0,3,7) -> (0,2,7) as in the lucebox blog's
+    # compact-batch example; outputs are identical.
+    w2 = make_custom(base, seed=41, d=16)
+    w2.history = [(2 if s == 3 else s, k, v) for s, k, v in w2.history]
+    for seg in w2.steps[0].segments:
+        seg.slot = 2 if seg.slot == 3 else seg.slot
+    r2, _ = run_step0(w2)
+    assert np.array_equal(r1["out"], r2["out"])
+
+
+def test_free_and_reuse_isolation():
+    """Release one slot, reuse its blocks for a new prompt; the other slots'
+    replayed rows and their pool bytes are unchanged (lucebox blog §Paged KV:
+    blocks of a finished sequence go to a new request without moving others)."""
+    from workloads.configs import Segment, Step
+    w = make_custom([(0, 30, 4), (1, 50, 4), (2, 20, 4)], seed=51, d=16, pool_slack=1.0, num_blocks=40)
+    s1 = w.steps[0]
+    rng = np.random.default_rng(52)
+    nk = bf16_bits_from_f32(rng.standard_normal((40, 2, 16), dtype=np.float32))
+    nq = bf16_bits_from_f32(rng.standard_normal((40, 4, 16), dtype=np.float32))
+    ops = [("release", 1), ("truncate", 0, 30), ("truncate", 2, 20), ("acquire", 1)]
+    segs = [Segment(0, 4), Segment(1, 40), Segment(2, 4)]
+    w.steps.append(Step(ops=ops, segments=segs,
+                        k_new=np.concatenate([s1.k_new[0:4], nk, s1.k_new[8:12]]),
+                        v_new=np.concatenate([s1.v_new[0:4], nk, s1.v_new[8:12]]),
+                        q=np.concatenate([s1.q[0:4], nq, s1.q[8:12]])))
+    res, _ = run_workload(w)
+    a, b = res[0], res[1]
+    assert np.array_equal(b["out"][0:4], a["out"][0:4])
+    assert np.array_equal(b["out"][44:48], a["out"][8:12])
+    old1 = set(a["meta"]["block_tables"][1][: -(-54 // 16)].tolist())
+    new1 = b["meta"]["block_tables"][1][: -(-40 // 16)].tolist()
+    assert set(new1) <= old1 | set(range(40))
+    assert new1[0] == a["meta"]["block_tables"][1][0]         # LIFO: first freed block first
+
+
+# --------------------------------------------------------------- append
+def test_append_matches_token_loop_and_leaves_other_bytes():
+    rng = np.random.default_rng(61)
+    nb, hkv, bs, d = 9, 3, 16, 8
+    pk = rng.integers(0, 2 ** 16, size=(nb, hkv, bs, d), dtype=np.uint16)
+    pv = rng.integers(0, 2 ** 16, size=(nb, hkv, bs, d), dtype=np.uint16)
+    sm = rng.choice(nb * bs, size=37, replace=False).astype(np.int32)
+    kn = rng.integers(0, 2 ** 16, size=(37, hkv, d), dtype=np.uint16)
+    vn = rng.integers(0, 2 ** 16, size=(37, hkv, d), dtype=np.uint16)
+    k2, v2 = pa.append_reference(pk, pv, sm, kn, vn, bs)
+    ek, ev = pk.copy(), pv.copy()
+    touched = np.zeros((nb, bs), bool)
+    for t in range(37):
+        blk, off = int(sm[t]) // bs, int(sm[t]) % bs
+        touched[blk, off] = True
+        for h in range(hkv):
+            for e in range(d):
+                ek[blk, h, off, e] = kn[t, h, e]
+                ev[blk, h, off, e] = vn[t, h, e]
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+    assert np.array_equal(k2.transpose(0, 2, 1, 3)[~touched], pk.transpose(0, 2, 1, 3)[~touched])
+    k3, v3 = pa.append_reference(k2, v2, sm, kn, vn, bs)           # idempotent
+    assert np.array_equal(k3, k2) and np.array_equal(v3, v2)
+
+
+# --------------------------------------------------------------- block pool
+def _golden_tables():
+    rows = {}
+    with open(os.path.join(GOLDEN, "worked_block_tables.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                key, *vals = line.split()
+                rows[key] = [int(x) for x in vals]
+    return rows
+
+
+def test_worked_block_table_example():
+    g = _golden_tables()
+    order = g["A"] + g["B"] + g["free"]
+    alloc = BlockPool(10, 16, 4, 8, order)
+    alloc.acquire(0)
+    alloc.reserve(0, 4 * 16)
+    alloc.acquire(1)
+    alloc.reserve(1, 2 * 16)
+    assert alloc.tables[0] == g["A"] and alloc.tables[1] == g["B"]
+    assert list(reversed(alloc.free)) == g["free"]
+    alloc.release(1)
+    alloc.acquire(2)
+    alloc.reserve(2, 2 * 16)
+    assert alloc.tables[2] == g["after_B_finishes_new_request"]
+    assert alloc.tables[0] == g["A"]
+
+
+def test_reserve_is_all_or_nothing():
+    alloc = BlockPool(10, 16, 4, 16, np.arange(10))
+    alloc.acquire(0)
+    alloc.acquire(1)
+    alloc.reserve(0, 100)                       # 7 blocks
+    before = (list(alloc.free), {k: list(v) for k, v in alloc.tables.items()}, dict(alloc.lengths))
+    with pytest.raises(NoSpace):
+        alloc.reserve(1, 4 * 16)                # needs 4, 3 free
+    with pytest.raises(NoSpace):
+        alloc.lower_step([(0, 13), (1, 49)])    # 0 + 4 blocks > 3 free
+    assert before == (list(alloc.free), {k: list(v) for k, v in alloc.tables.items()}, dict(alloc.lengths))
+
+
+def test_slot_mapping_roundtrip_and_uniqueness():
+    """Every appended token lands at a distinct pool position, and walking the
+    block table gives the tokens back in logical order."""
+    w = make_custom(MIXED, dtype="f32", hq=2, hkv=1, d=4, seed=71)
+    r, (pk, _) = run_step0(w)
+    kv = logical_kv(w)
+    ctx, tables = r["meta"]["context_lens"], r["meta"]["block_tables"]
+    for slot, (k, _) in kv.items():
+        got = pa.gather_sequence(pk, tables[slot], int(ctx[slot]), w.block_size)
+        assert np.array_equal(got, k)
+    sm = r["meta"]["slot_mapping"]
+    assert len(set(sm.tolist())) == len(sm)
+
+
+def test_pool_rounding_to_whole_blocks():
+    assert pool_blocks_for_tokens(98304, 16) == 6144
+    assert pool_blocks_for_tokens(100, 16) == 7
+    assert pool_blocks_for_tokens(0, 16) == 0
+
+
+# --------------------------------------------------------------- planted mistakes
+def _pins_fail(monkeypatch_target, name, bad):
+    w = make_custom(MIXED, dtype="f32", hq=8, hkv=2, d=16, seed=81)
+    orig = getattr(monkeypatch_target, name)
+    setattr(monkeypatch_target, name, bad)
+    try:
+        r, _ = run_step0(w)
+        out = r["out"]
+    except (IndexError, ValueError):
+        return True                      # the mistake cannot even run
+    finally:
+        setattr(monkeypatch_target, name, orig)
+    ref = sdpa_reference(w)
+    return not np.allclose(out, ref, rtol=0, atol=1e-12, equal_nan=False)
+
+
+def test_planted_mistakes_are_caught():
+    assert _pins_fail(pa, "kv_head_for", lambda h, g: h % 2)                     # wrong GQA map
+    assert _pins_fail(pa, "visible", lambda pos, L: np.arange(L)[None] < pos[:, None])   # off by one
+    assert _pins_fail(pa, "visible", lambda pos, L: np.ones((len(pos), L), bool))        # no causal mask
+    assert _pins_fail(pa, "block_and_offset", lambda s, bs: (s % bs, s // bs))          # swapped
+    orig_gather = pa.gather_sequence
+    assert _pins_fail(pa, "gather_sequence",
+                      lambda pool, t, L, bs: orig_gather(pool, np.roll(np.asarray(t), 1), L, bs))
+    orig_attend = pa.attend_rows
+    assert _pins_fail(pa, "attend_rows", lambda q, k, v, s, p: orig_attend(q, k, v, 1.0, p))  # scale dropped
+    assert _pins_fail(pa, "attend_rows", lambda q, k, v, s, p: orig_attend(q, v, k, s, p))    # K/V swapped

@@ -1,0 +1,225 @@
+/*
+ * pagedkv.h - C ABI for the paged-KV mixed step on AMD MI355X (gfx950).
+ *
+ * The problem these calls solve is stated in "Continuous batching: Qwen3.8-27B
+ * at 301 tok/s across five clients, up to 1.97x llama.cpp" (lucebox blog):
+ *   - §Paged KV and paged attention: attention KV lives in fixed-size
+ *     physical blocks of one shared pool; each sequence owns a block table
+ *     mapping its logical token positions to physical blocks; attention walks
+ *     that table in logical order with no gather or relocation of the cache;
+ *     a finished sequence's blocks return to the pool without moving others;
+ *     an explicit pool size is rounded to whole blocks.
+ *   - §Keeping track of each request: every admitted request owns a stable
+ *     sequence slot (block table + state); the compact batch names slots
+ *     through an explicit row-to-slot map.
+ *   - §Chunked prefill is a slot phase: each selected prompt chunk appends
+ *     directly to its slot's paged KV.
+ *   - §Packing unequal prompt chunks together: prompt chunks and decode rows
+ *     share one packed token axis; per-query causal positions and block-table
+ *     metadata let both attend in one pass.
+ *   - §Admission and step planning are different decisions: KV capacity is
+ *     reserved atomically.
+ * mlxcel user guide "연속 배칭" (continuous batching), §Paged KV 캐시와
+ * 프리픽스 공유: decode reserves its blocks before the forward pass.
+ *
+ * Conventions
+ *   - All integers are int32 unless stated.  Pointers marked "device" are HIP
+ *     device pointers; "host" pointers are ordinary process memory.
+ *   - The caller owns every buffer (pool, inputs, outputs, workspace).  The
+ *     library never allocates or frees device memory and keeps no mutable
+ *     global state.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream).  Argument errors are returned before
+ *     anything is launched; launch failures return PKV_ERR_HIP; faults show
+ *     up at the caller's next synchronisation.
+ *   - Kernels do not validate metadata values.  They never access memory
+ *     outside the buffers described below, whatever the metadata holds, but
+ *     the result of invalid metadata is unspecified.  pkv_validate_step checks
+ *     host copies of the metadata against every rule stated here.
+ *
+ * Pool layout (the pages leave the layout to the backend): K and V are two
+ * separate device arrays, each [num_blocks][num_kv_heads][block_size][head_dim],
+ * row-major, element type `dtype`.  One (block, KV head) tile of K or V is one
+ * contiguous span of block_size * head_dim elements.  A flat pool token slot
+ * s = block * block_size + offset names position `offset` of block `block`.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* a pointer, size or metadata value is invalid      */
+  PKV_ERR_UNSUPPORTED = -2, /* valid but not built: see "Supported shapes"        */
+  PKV_ERR_NO_SPACE = -3,    /* allocator: not enough free blocks; state unchanged */
+  PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required         */
+  PKV_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed         */
+  PKV_ERR_STATE = -6        /* allocator: slot not in the required state          */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* The shared KV pool.  Supported shapes: block_size 16; head_dim 64 or 128;
+ * dtype PKV_F32 or PKV_BF16. */
+typedef struct {
+  void *k;              /* device [num_blocks][num_kv_heads][block_size][head_dim] */
+  void *v;              /* device, same shape and dtype as k                        */
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;        /* pkv_dtype */
+} pkv_pool;
+
+/* ------------------------------------------------------------------ device */
+
+/* KV append (lucebox blog §Chunked prefill is a slot phase: a chunk appends
+ * directly to its slot's paged KV).  For every token t < num_tokens and every
+ * KV head h, copies k_new[t][h][:] to K[s / bs][h][s % bs][:] and v_new[t][h][:]
+ * to V[...] where s = slot_mapping[t].  A bit-exact copy: no conversion.
+ *   slot_mapping  device int32 [num_tokens]; flat pool token slots.  Entries
+ *                 must be distinct (a repeat is a write race); an entry outside
+ *                 [0, num_blocks * block_size) is skipped (nothing written).
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], pool dtype.
+ * num_tokens == 0 is a no-op.  Returns PKV_OK, PKV_ERR_INVALID_ARG,
+ * PKV_ERR_UNSUPPORTED or PKV_ERR_HIP. */
+int pkv_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
+                  int32_t num_tokens, const pkv_pool *pool, void *stream);
+
+/* Mixed-step paged attention (lucebox blog §Paged KV and paged attention and
+ * §Packing unequal prompt chunks together).  The packed batch has
+ * num_segments segments; segment b owns rows [query_start[b],
+ * query_start[b] + query_len[b]) of q_packed and out, and the stable sequence
+ * slot s = row_to_slot[b].  That slot holds L = context_lens[s] tokens in the
+ * pool (this step's appended tokens included) listed by block_tables[s][0 ..
+ * ceil(L / block_size)).  Row i of the segment sits at position
+ * L - query_len[b] + i and attends to the slot's tokens 0 .. L - query_len[b] + i
+ * (causal inside the chunk; a decode row, query_len 1, sees all L).  Query head
+ * h reads KV head h / (num_q_heads / num_kv_heads).  For each row and head:
+ *     out = sum_j softmax_j(scale * q . K_j) V_j
+ * accumulated in fp32.
+ *   q_packed      device [total_q][num_q_heads][head_dim], pool dtype.
+ *   row_to_slot, query_start, query_len   device int32 [num_segments].
+ *                 query_len >= 1; segments cover disjoint rows; a slot appears
+ *                 in at most one segment; query_len <= L.
+ *   context_lens  device int32 [num_slots], indexed by slot.
+ *   block_tables  device int32 [num_slots][max_blocks_per_seq], by slot.
+ *   max_query_len, max_context_len   host upper bounds over the segments
+ *                 (used for grid and workspace sizing only; a value smaller
+ *                 than the truth gives unspecified results).
+ *   scale         softmax scale (1/sqrt(head_dim) for standard attention).
+ *   out           device [total_q][num_q_heads][head_dim]; out_dtype PKV_F32,
+ *                 or PKV_BF16 when the pool is bf16 (rounded to nearest even).
+ *   workspace     device scratch of at least pkv_paged_attend_workspace_bytes
+ *                 bytes (may be NULL when that is 0); contents on entry ignored.
+ * Rows not covered by any segment are not written.  Returns PKV_OK,
+ * PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (shape not built: num_q_heads /
+ * num_kv_heads > 8, head_dim not 64/128, block_size not 16, query_len > 1 with
+ * an fp32 pool beyond the simple path's limits), PKV_ERR_WORKSPACE or
+ * PKV_ERR_HIP. */
+int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
+                     const int32_t *row_to_slot, const int32_t *query_start,
+                     const int32_t *query_len, int32_t num_segments,
+                     const int32_t *context_lens, const int32_t *block_tables,
+                     int32_t num_slots, int32_t max_blocks_per_seq,
+                     int32_t max_query_len, int32_t max_context_len,
+                     const pkv_pool *pool, float scale,
+                     void *out, int32_t out_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace pkv_paged_attend needs for these bounds and this pool
+ * (split-context partial results).  Pure host arithmetic; returns 0 when no
+ * workspace is needed and (size_t)-1 for invalid arguments. */
+size_t pkv_paged_attend_workspace_bytes(int32_t num_segments, int32_t total_q,
+                                        int32_t num_q_heads, int32_t max_query_len,
+                                        int32_t max_context_len, const pkv_pool *pool);
+
+/* Tokens per split-context partition used by the decode path (a constant of
+ * the build, so a row's reduction order depends on its own length only). */
+int32_t pkv_decode_partition_tokens(void);
+
+/* Static text for a status code. */
+const char *pkv_status_str(int status);
+
+/* -------------------------------------------------------- host allocator */
+
+/* A host-only block-pool allocator with stable sequence slots (lucebox blog
+ * §Keeping track of each request, §Paged KV and paged attention, §Admission
+ * and step planning are different decisions).  It touches no device memory.
+ * Blocks are handed out in the order of `free_order` (a permutation of
+ * [0, num_blocks); NULL = ascending); blocks released by a slot go back on
+ * top of the free list in table order, so they are reused first.  Not
+ * thread-safe: one allocator per scheduler. */
+typedef struct pkv_alloc pkv_alloc;
+
+int pkv_alloc_create(int32_t num_blocks, int32_t block_size, int32_t max_slots,
+                     int32_t max_blocks_per_seq, const int32_t *free_order /* host or NULL */,
+                     pkv_alloc **out /* host */);
+void pkv_alloc_destroy(pkv_alloc *alloc);
+
+/* Mark `slot` in use with an empty table (PKV_ERR_STATE if already in use). */
+int pkv_slot_acquire(pkv_alloc *alloc, int32_t slot);
+/* Return all of the slot's blocks to the pool and free the slot. */
+int pkv_slot_release(pkv_alloc *alloc, int32_t slot);
+/* Shrink the slot to new_len tokens (rejected speculative drafts); blocks no
+ * longer needed return to the pool. */
+int pkv_slot_truncate(pkv_alloc *alloc, int32_t slot, int32_t new_len);
+/* Grow the slot's table so it can hold total_tokens; all or nothing
+ * (PKV_ERR_NO_SPACE leaves every table and the free list unchanged). */
+int pkv_reserve(pkv_alloc *alloc, int32_t slot, int32_t total_tokens);
+
+/* Lower one step.  entry_slots / entry_new_tokens (host, [num_entries]) name,
+ * in packed order, the slots that advance and how many new tokens each
+ * appends (1 for a decode row, the chunk length for a prompt chunk, the draft
+ * count for speculative verification).  Reserves the blocks the step needs
+ * (all or nothing over the whole step), advances each slot's length, and
+ * writes these host arrays:
+ *   slot_mapping  [sum of entry_new_tokens] (capacity slot_mapping_cap):
+ *                 position p of slot s maps to
+ *                 block_tables[s][p / block_size] * block_size + p % block_size;
+ *   query_start, query_len, row_to_slot   [num_entries];
+ *   context_lens  [max_slots]   tokens per slot after this step (0 if unused);
+ *   block_tables  [max_slots][max_blocks_per_seq]   (unused entries 0).
+ * Any output pointer may be NULL to skip it.  Returns PKV_OK,
+ * PKV_ERR_INVALID_ARG (bad slot, repeated slot, n < 1, table overflow, small
+ * capacity), PKV_ERR_STATE (slot not acquired) or PKV_ERR_NO_SPACE. */
+int pkv_lower_step(pkv_alloc *alloc, int32_t num_entries, const int32_t *entry_slots,
+                   const int32_t *entry_new_tokens, int32_t *slot_mapping,
+                   int32_t slot_mapping_cap, int32_t *query_start, int32_t *query_len,
+                   int32_t *row_to_slot, int32_t *context_lens, int32_t *block_tables);
+
+/* Current state: free block count; a slot's token count and block count
+ * (-1 / PKV_ERR_STATE if not in use); copy of a slot's table (host out). */
+int32_t pkv_free_blocks(const pkv_alloc *alloc);
+int pkv_slot_info(const pkv_alloc *alloc, int32_t slot, int32_t *num_tokens, int32_t *num_blocks);
+int pkv_slot_table(const pkv_alloc *alloc, int32_t slot, int32_t *table, int32_t capacity);
+
+/* An explicit pool size in tokens rounded up to whole blocks (lucebox blog
+ * §Paged KV and paged attention).  Returns -1 for negative tokens or
+ * block_size <= 0. */
+int64_t pkv_pool_blocks_for_tokens(int64_t tokens, int32_t block_size);
+
+/* Check host copies of one step's metadata against every rule stated for
+ * pkv_kv_append and pkv_paged_attend (tiling of the packed rows, slot ranges
+ * and uniqueness, query_len <= L, table capacity, block ids in the pool,
+ * slot_mapping range and uniqueness).  slot_mapping may be NULL.  Returns
+ * PKV_OK or PKV_ERR_INVALID_ARG; *bad_index (host, may be NULL) receives the
+ * index of the first offending entry. */
+int pkv_validate_step(int32_t total_q, int32_t num_segments, const int32_t *row_to_slot,
+                      const int32_t *query_start, const int32_t *query_len,
+                      int32_t num_slots, const int32_t *context_lens,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      int32_t num_blocks, int32_t block_size,
+                      const int32_t *slot_mapping, int32_t num_tokens, int32_t *bad_index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

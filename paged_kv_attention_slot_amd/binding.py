@@ -1,0 +1,287 @@
+"""ctypes binding for libpagedkv.so: argument marshalling only.
+
+Every computation runs in the library (HIP kernels for append and attention,
+C++ for the block-pool allocator and the step lowering).  PyTorch supplies
+device memory and the current stream; nothing else from it is used here.
+Importing this module does not load the library; the first call does, and
+fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pagedkv.h")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_NO_SPACE = -3
+PKV_ERR_WORKSPACE = -4
+PKV_ERR_HIP = -5
+PKV_ERR_STATE = -6
+PKV_F32 = 0
+PKV_BF16 = 1
+
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("k", _p), ("v", _p), ("num_blocks", _i32), ("block_size", _i32),
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32)]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+class NoSpace(PagedKVError):
+    pass
+
+
+_LIB = None
+
+_SIGNATURES = {
+    "pkv_kv_append": (_i32, [_p, _p, _p, _i32, ctypes.POINTER(PoolDesc), _p]),
+    "pkv_paged_attend": (_i32, [_p, _i32, _i32, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
+                                ctypes.POINTER(PoolDesc), ctypes.c_float, _p, _i32, _p, ctypes.c_size_t, _p]),
+    "pkv_paged_attend_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc)]),
+    "pkv_decode_partition_tokens": (_i32, []),
+    "pkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_alloc_create": (_i32, [_i32, _i32, _i32, _i32, _pi32, ctypes.POINTER(_p)]),
+    "pkv_alloc_destroy": (None, [_p]),
+    "pkv_slot_acquire": (_i32, [_p, _i32]),
+    "pkv_slot_release": (_i32, [_p, _i32]),
+    "pkv_slot_truncate": (_i32, [_p, _i32, _i32]),
+    "pkv_reserve": (_i32, [_p, _i32, _i32]),
+    "pkv_lower_step": (_i32, [_p, _i32, _pi32, _pi32, _pi32, _i32, _pi32, _pi32, _pi32, _pi32, _pi32]),
+    "pkv_free_blocks": (_i32, [_p]),
+    "pkv_slot_info": (_i32, [_p, _i32, _pi32, _pi32]),
+    "pkv_slot_table": (_i32, [_p, _i32, _pi32, _i32]),
+    "pkv_pool_blocks_for_tokens": (ctypes.c_int64, [ctypes.c_int64, _i32]),
+    "pkv_validate_step": (_i32, [_i32, _i32, _pi32, _pi32, _pi32, _i32, _pi32, _pi32, _i32, _i32, _i32,
+                                 _pi32, _i32, _pi32]),
+}
+
+
+def lib():
+    """Load libpagedkv.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_attention_slot_amd.build` (there is no fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def header_symbols():
+    """Function names declared in include/pagedkv.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_str(status: int) -> str:
+    try:
+        return lib().pkv_status_str(int(status)).decode()
+    except Exception:  # library not loadable: still give a message
+        return "status"
+
+
+def _check(status, what):
+    if status != PKV_OK:
+        if status == PKV_ERR_NO_SPACE:
+            raise NoSpace(status, what)
+        raise PagedKVError(status, what)
+
+
+def _ptr_i32(a):
+    """Host int32 numpy array (contiguous) -> ctypes pointer, or NULL."""
+    if a is None:
+        return None
+    assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_pi32)
+
+
+# --------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def pkv_dtype_of(tdtype) -> int:
+    torch = _torch()
+    if tdtype == torch.bfloat16:
+        return PKV_BF16
+    if tdtype == torch.float32:
+        return PKV_F32
+    raise ValueError(f"unsupported dtype {tdtype}")
+
+
+def current_stream_handle(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+class KVPool:
+    """The shared pool: K and V, each [num_blocks][num_kv_heads][16][head_dim]."""
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim, dtype, block_size=16, device="cuda", poison=True):
+        torch = _torch()
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.k = torch.empty(shape, dtype=dtype, device=device)
+        self.v = torch.empty(shape, dtype=dtype, device=device)
+        if poison:
+            self.k.fill_(float("nan"))
+            self.v.fill_(float("nan"))
+        self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size = num_blocks, num_kv_heads, head_dim, block_size
+        self.dtype = dtype
+
+    def desc(self) -> PoolDesc:
+        return PoolDesc(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.block_size,
+                        self.num_kv_heads, self.head_dim, pkv_dtype_of(self.dtype))
+
+
+def kv_append(slot_mapping, k_new, v_new, pool: KVPool, stream=None):
+    """Scatter k_new/v_new [T][Hkv][D] into the pool at slot_mapping [T] (device int32)."""
+    t = int(slot_mapping.shape[0])
+    d = pool.desc()
+    st = lib().pkv_kv_append(_dptr(slot_mapping), _dptr(k_new), _dptr(v_new), t, ctypes.byref(d),
+                             stream if stream is not None else current_stream_handle())
+    _check(st, "pkv_kv_append")
+
+
+def workspace_bytes(num_segments, total_q, num_q_heads, max_query_len, max_context_len, pool: KVPool) -> int:
+    d = pool.desc()
+    n = lib().pkv_paged_attend_workspace_bytes(num_segments, total_q, num_q_heads, max_query_len,
+                                               max_context_len, ctypes.byref(d))
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID_ARG, "pkv_paged_attend_workspace_bytes")
+    return int(n)
+
+
+def paged_attend(q_packed, row_to_slot, query_start, query_len, context_lens, block_tables, pool: KVPool,
+                 scale, *, max_query_len, max_context_len, out, workspace=None, stream=None):
+    """Mixed-step paged attention; all tensors on the device, metadata int32.
+    `out` [total_q][Hq][D] is float32 or the pool dtype."""
+    total_q, hq = int(q_packed.shape[0]), int(q_packed.shape[1])
+    nseg = int(row_to_slot.shape[0])
+    num_slots, maxb = int(block_tables.shape[0]), int(block_tables.shape[1])
+    d = pool.desc()
+    ws_ptr = _dptr(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().pkv_paged_attend(_dptr(q_packed), total_q, hq, _dptr(row_to_slot), _dptr(query_start),
+                                _dptr(query_len), nseg, _dptr(context_lens), _dptr(block_tables), num_slots, maxb,
+                                int(max_query_len), int(max_context_len), ctypes.byref(d), float(scale),
+                                _dptr(out), pkv_dtype_of(out.dtype), ws_ptr, ws_bytes,
+                                stream if stream is not None else current_stream_handle())
+    _check(st, "pkv_paged_attend")
+    return out
+
+
+def decode_partition_tokens() -> int:
+    return int(lib().pkv_decode_partition_tokens())
+
+
+def pool_blocks_for_tokens(tokens: int, block_size: int) -> int:
+    return int(lib().pkv_pool_blocks_for_tokens(int(tokens), int(block_size)))
+
+
+def validate_step(meta: dict, total_q, num_blocks, block_size, max_blocks_per_seq, num_tokens=None):
+    """Check host metadata arrays; returns (ok, bad_index)."""
+    bad = ctypes.c_int32(-1)
+    sm = meta.get("slot_mapping")
+    st = lib().pkv_validate_step(int(total_q), len(meta["row_to_slot"]), _ptr_i32(meta["row_to_slot"]),
+                                 _ptr_i32(meta["query_start"]), _ptr_i32(meta["query_len"]),
+                                 len(meta["context_lens"]), _ptr_i32(meta["context_lens"]),
+                                 _ptr_i32(meta["block_tables"]), int(max_blocks_per_seq), int(num_blocks),
+                                 int(block_size), _ptr_i32(sm), int(num_tokens if num_tokens is not None else
+                                                                   (len(sm) if sm is not None else 0)),
+                                 ctypes.byref(bad))
+    return st == PKV_OK, int(bad.value)
+
+
+class BlockAllocator:
+    """Host block-pool allocator (C++), see pkv_alloc_* in include/pagedkv.h."""
+
+    def __init__(self, num_blocks, block_size, max_slots, max_blocks_per_seq, free_order=None):
+        self._lib = lib()
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.max_slots, self.max_blocks_per_seq = int(max_slots), int(max_blocks_per_seq)
+        order = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        h = ctypes.c_void_p()
+        _check(self._lib.pkv_alloc_create(self.num_blocks, self.block_size, self.max_slots,
+                                          self.max_blocks_per_seq, _ptr_i32(order), ctypes.byref(h)),
+               "pkv_alloc_create")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_alloc_destroy(h)
+            self._h = None
+
+    def acquire(self, slot):
+        _check(self._lib.pkv_slot_acquire(self._h, int(slot)), "pkv_slot_acquire")
+
+    def release(self, slot):
+        _check(self._lib.pkv_slot_release(self._h, int(slot)), "pkv_slot_release")
+
+    def truncate(self, slot, new_len):
+        _check(self._lib.pkv_slot_truncate(self._h, int(slot), int(new_len)), "pkv_slot_truncate")
+
+    def reserve(self, slot, total_tokens):
+        _check(self._lib.pkv_reserve(self._h, int(slot), int(total_tokens)), "pkv_reserve")
+
+    def free_blocks(self) -> int:
+        return int(self._lib.pkv_free_blocks(self._h))
+
+    def slot_info(self, slot):
+        n, b = ctypes.c_int32(), ctypes.c_int32()
+        st = self._lib.pkv_slot_info(self._h, int(slot), ctypes.byref(n), ctypes.byref(b))
+        return (int(n.value), int(b.value)) if st == PKV_OK else None
+
+    def slot_table(self, slot):
+        info = self.slot_info(slot)
+        if info is None:
+            return None
+        out = np.zeros(max(info[1], 1), dtype=np.int32)
+        _check(self._lib.pkv_slot_table(self._h, int(slot), _ptr_i32(out), len(out)), "pkv_slot_table")
+        return out[:info[1]].tolist()
+
+    def lower_step(self, entries, out=None):
+        """entries: [(slot, n_new)] in packed order -> dict of host int32 arrays.
+        `out` may supply preallocated arrays (same keys) to fill in place."""
+        slots = np.ascontiguousarray([e[0] for e in entries], dtype=np.int32)
+        news = np.ascontiguousarray([e[1] for e in entries], dtype=np.int32)
+        t = int(news.sum()) if len(news) else 0
+        n = len(entries)
+        if out is None:
+            out = dict(slot_mapping=np.empty(t, np.int32), query_start=np.empty(n, np.int32),
+                       query_len=np.empty(n, np.int32), row_to_slot=np.empty(n, np.int32),
+                       context_lens=np.empty(self.max_slots, np.int32),
+                       block_tables=np.empty((self.max_slots, self.max_blocks_per_seq), np.int32))
+        st = self._lib.pkv_lower_step(self._h, n, _ptr_i32(slots), _ptr_i32(news), _ptr_i32(out["slot_mapping"]),
+                                      len(out["slot_mapping"]), _ptr_i32(out["query_start"]),
+                                      _ptr_i32(out["query_len"]), _ptr_i32(out["row_to_slot"]),
+                                      _ptr_i32(out["context_lens"]), _ptr_i32(out["block_tables"]))
+        _check(st, "pkv_lower_step")
+        return out

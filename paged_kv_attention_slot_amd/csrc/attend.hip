@@ -1,0 +1,140 @@
+// C-ABI entry points for the device side: argument checks, workspace sizing
+// and kernel dispatch on the caller's stream.
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+namespace {
+
+bool pool_ok(const pkv_pool *p) {
+  if (!p || !p->k || !p->v) return false;
+  if (p->num_blocks <= 0 || p->num_kv_heads <= 0 || p->block_size <= 0 || p->head_dim <= 0) return false;
+  return p->dtype == PKV_F32 || p->dtype == PKV_BF16;
+}
+
+bool pool_supported(const pkv_pool *p) {
+  return p->block_size == kBlockTokens && (p->head_dim == 64 || p->head_dim == 128);
+}
+
+// Multi-row segments go to the bf16 MFMA kernel when that shape is built;
+// otherwise (fp32 pools) they take the decode path row by row.
+bool multirow_on_decode_path(int32_t dtype, int32_t head_dim, int32_t group, int32_t max_query_len) {
+  return max_query_len > 1 && !chunk_supported(dtype, head_dim, group);
+}
+
+struct WorkspaceLayout {
+  int64_t rows = 0, part_max = 0;
+  size_t acc_bytes = 0, ml_bytes = 0;
+  size_t total() const { return acc_bytes + ml_bytes; }
+};
+
+WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_query_len, int32_t max_context_len, int32_t dtype, int32_t group) {
+  WorkspaceLayout w;
+  w.part_max = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
+  if (w.part_max <= 1) {
+    w.part_max = 1;
+    return w;
+  }
+  w.rows = multirow_on_decode_path(dtype, head_dim, group, max_query_len) ? total_q : num_segments;
+  const int64_t n = w.rows * num_q_heads * w.part_max;
+  w.acc_bytes = static_cast<size_t>(n) * head_dim * sizeof(float);
+  w.acc_bytes = (w.acc_bytes + 255) & ~static_cast<size_t>(255);
+  w.ml_bytes = static_cast<size_t>(n) * 2 * sizeof(float);
+  return w;
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+int pkv_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new, int32_t num_tokens,
+                  const pkv_pool *pool, void *stream) {
+  if (!pool_ok(pool) || num_tokens < 0) return PKV_ERR_INVALID_ARG;
+  if (!pool_supported(pool)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!slot_mapping || !k_new || !v_new) return PKV_ERR_INVALID_ARG;
+  return launch_kv_append(slot_mapping, k_new, v_new, num_tokens, *pool, static_cast<hipStream_t>(stream));
+}
+
+size_t pkv_paged_attend_workspace_bytes(int32_t num_segments, int32_t total_q, int32_t num_q_heads,
+                                        int32_t max_query_len, int32_t max_context_len, const pkv_pool *pool) {
+  if (!pool || num_segments < 0 || total_q < 0 || num_q_heads <= 0 || max_query_len < 0 || max_context_len < 0 ||
+      pool->head_dim <= 0)
+    return static_cast<size_t>(-1);
+  if (pool->num_kv_heads <= 0 || num_q_heads % pool->num_kv_heads != 0) return static_cast<size_t>(-1);
+  return workspace_layout(num_segments, total_q, num_q_heads, pool->head_dim, max_query_len, max_context_len,
+                          pool->dtype, num_q_heads / pool->num_kv_heads)
+      .total();
+}
+
+int32_t pkv_decode_partition_tokens(void) { return kDecodePartitionTokens; }
+
+int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int32_t *row_to_slot,
+                     const int32_t *query_start, const int32_t *query_len, int32_t num_segments,
+                     const int32_t *context_lens, const int32_t *block_tables, int32_t num_slots,
+                     int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_context_len,
+                     const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  if (!pool_ok(pool) || total_q < 0 || num_segments < 0 || num_q_heads <= 0 || num_slots <= 0 ||
+      max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (out_dtype != PKV_F32 && !(out_dtype == PKV_BF16 && pool->dtype == PKV_BF16)) return PKV_ERR_INVALID_ARG;
+  if (!pool_supported(pool) || num_q_heads / pool->num_kv_heads > 8) return PKV_ERR_UNSUPPORTED;
+  if (num_segments == 0 || total_q == 0) return PKV_OK;
+  if (!q_packed || !row_to_slot || !query_start || !query_len || !context_lens || !block_tables || !out)
+    return PKV_ERR_INVALID_ARG;
+  if (max_query_len > total_q) max_query_len = total_q;
+
+  const int32_t group = num_q_heads / pool->num_kv_heads;
+  const bool multirow = multirow_on_decode_path(pool->dtype, pool->head_dim, group, max_query_len);
+  const WorkspaceLayout ws = workspace_layout(num_segments, total_q, num_q_heads, pool->head_dim, max_query_len,
+                                              max_context_len, pool->dtype, group);
+  if (ws.total() > 0 && (!workspace || workspace_bytes < ws.total())) return PKV_ERR_WORKSPACE;
+
+  AttendArgs a{};
+  a.q = q_packed;
+  a.out = out;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.row_to_slot = row_to_slot;
+  a.query_start = query_start;
+  a.query_len = query_len;
+  a.context_lens = context_lens;
+  a.block_tables = block_tables;
+  a.part_acc = ws.total() ? static_cast<float *>(workspace) : nullptr;
+  a.part_ml = ws.total() ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.acc_bytes) : nullptr;
+  a.num_segments = num_segments;
+  a.num_slots = num_slots;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = pool->num_blocks;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.total_q = total_q;
+  a.part_max = static_cast<int32_t>(ws.part_max);
+  a.multirow = multirow ? 1 : 0;
+  a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_query_len > 1 && !multirow) {
+    const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, s);
+    if (st != PKV_OK) return st;
+  }
+  return launch_decode(a, pool->dtype, pool->head_dim, max_context_len, max_query_len, s);
+}
+
+}  // extern "C"

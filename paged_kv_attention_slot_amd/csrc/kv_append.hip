@@ -1,0 +1,75 @@
+// KV append: scatter this step's new K/V rows into the shared block pool.
+//
+// "Continuous batching: Qwen3.8-27B at 301 tok/s ..." (lucebox blog),
+// §Chunked prefill is a slot phase: each selected chunk appends directly to
+// its slot's paged KV.  The flat pool token slot s = slot_mapping[t] names
+// position s % block_size of physical block s / block_size.
+//
+// The work is a pure byte copy in 16-byte units.  Thread c handles unit c of
+// the packed source [T][Hkv][row16] (row16 = head_dim * elem_bytes / 16), so
+// reads are perfectly coalesced; each (token, head) destination row is one
+// contiguous head_dim * elem_bytes span of a (block, head) tile, so writes
+// coalesce per row.  Entries outside the pool are skipped.
+#include "pagedkv.h"
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+template <int ROW16>
+__global__ __launch_bounds__(256) void kv_append_kernel(const int32_t *__restrict__ slot_mapping,
+                                                        const uint4 *__restrict__ k_new,
+                                                        const uint4 *__restrict__ v_new,
+                                                        uint4 *__restrict__ pool_k,
+                                                        uint4 *__restrict__ pool_v, int32_t num_tokens,
+                                                        int32_t num_kv_heads, int64_t pool_slots) {
+  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * ROW16;
+  const int64_t total = per_token * num_tokens;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < total;
+       c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = c / per_token;
+    const int64_t rem = c - t * per_token;
+    const int64_t h = rem / ROW16;
+    const int64_t w = rem - h * ROW16;
+    const int64_t s = slot_mapping[t];
+    if (s < 0 || s >= pool_slots) continue;
+    const int64_t blk = s / kBlockTokens;
+    const int64_t off = s - blk * kBlockTokens;
+    const int64_t dst = ((blk * num_kv_heads + h) * kBlockTokens + off) * ROW16 + w;
+    pool_k[dst] = k_new[c];
+    pool_v[dst] = v_new[c];
+  }
+}
+
+int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
+                     int32_t num_tokens, const pkv_pool &pool, hipStream_t stream) {
+  const int row16 = pool.head_dim * (pool.dtype == PKV_F32 ? 4 : 2) / 16;
+  const int64_t units = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * row16;
+  const int threads = 256;
+  int64_t blocks = (units + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  const int64_t pool_slots = static_cast<int64_t>(pool.num_blocks) * pool.block_size;
+  auto *pk = static_cast<uint4 *>(pool.k);
+  auto *pv = static_cast<uint4 *>(pool.v);
+  auto *kn = static_cast<const uint4 *>(k_new);
+  auto *vn = static_cast<const uint4 *>(v_new);
+  switch (row16) {
+    case 8:
+      kv_append_kernel<8><<<dim3(blocks), dim3(threads), 0, stream>>>(slot_mapping, kn, vn, pk, pv, num_tokens,
+                                                                     pool.num_kv_heads, pool_slots);
+      break;
+    case 16:
+      kv_append_kernel<16><<<dim3(blocks), dim3(threads), 0, stream>>>(slot_mapping, kn, vn, pk, pv, num_tokens,
+                                                                      pool.num_kv_heads, pool_slots);
+      break;
+    case 32:
+      kv_append_kernel<32><<<dim3(blocks), dim3(threads), 0, stream>>>(slot_mapping, kn, vn, pk, pv, num_tokens,
+                                                                      pool.num_kv_heads, pool_slots);
+      break;
+    default:
+      return PKV_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace pkv

@@ -1,0 +1,60 @@
+// Internal launch interfaces between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+constexpr int kBlockTokens = 16;  // tokens per pool block (the only block size built)
+
+// Tokens per split-context partition of the decode path.  A multiple of the
+// block size and at most 64 blocks (one block-table entry per lane).
+constexpr int32_t kDecodePartitionTokens = 512;
+
+struct AttendArgs {
+  const void *q;
+  void *out;
+  const void *k;
+  const void *v;
+  const int32_t *row_to_slot;
+  const int32_t *query_start;
+  const int32_t *query_len;
+  const int32_t *context_lens;
+  const int32_t *block_tables;
+  float *part_acc;   // [part_rows][Hq][part_max][D]
+  float *part_ml;    // [part_rows][Hq][part_max][2]  (running max in log2 units, sum)
+  int32_t num_segments;
+  int32_t num_slots;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t total_q;
+  int32_t part_max;     // partitions per row the workspace holds
+  int32_t multirow;     // 0: decode path takes query_len == 1 segments only; 1: every row
+  int32_t out_bf16;
+  float scale;          // softmax scale
+  float scale_log2;     // scale * log2(e)
+};
+
+int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
+                     int32_t num_tokens, const pkv_pool &pool, hipStream_t stream);
+
+// Decode path (one query row per work item; split-context partitions) and the
+// partition reduce.  `max_query_len`/`max_context_len` size the grid only.
+int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len,
+                  int32_t max_query_len, hipStream_t stream);
+
+// Multi-row segments (query_len > 1) on bf16 MFMA tiles.  chunk_supported()
+// tells whether this shape is built; otherwise multi-row segments take the
+// decode path row by row.
+bool chunk_supported(int32_t dtype, int32_t head_dim, int32_t group);
+int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, int32_t max_context_len,
+                 hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace pkv

@@ -1,0 +1,226 @@
+"""CPU tests of libpagedkv.so: it loads without a GPU, exports every symbol
+the header declares, and its C++ allocator / step lowering / validator agree
+bit-exactly with the oracle's plain allocator (no device calls here)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_slot_amd as pk
+from oracle.block_pool import BlockPool, NoSpace as OracleNoSpace
+from workloads import make_workload
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = pk.lib()
+    names = pk.header_symbols()
+    assert "pkv_kv_append" in names and "pkv_paged_attend" in names
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert pk.decode_partition_tokens() % 16 == 0
+
+
+def test_status_strings():
+    lib = pk.lib()
+    for st in range(0, -7, -1):
+        assert lib.pkv_status_str(st)
+    assert lib.pkv_status_str(-3).decode() == "not enough free KV blocks"
+
+
+def test_device_entry_points_reject_bad_arguments_without_gpu():
+    """Argument errors are returned before anything touches a device."""
+    lib = pk.lib()
+    d = pk.binding.PoolDesc(0, 0, 10, 16, 2, 64, 1)            # NULL k/v
+    assert lib.pkv_kv_append(None, None, None, 4, ctypes.byref(d), None) == pk.binding.PKV_ERR_INVALID_ARG
+    d2 = pk.binding.PoolDesc(16, 16, 10, 8, 2, 64, 1)          # block size 8 not built
+    assert lib.pkv_kv_append(None, None, None, 4, ctypes.byref(d2), None) == pk.binding.PKV_ERR_UNSUPPORTED
+    d3 = pk.binding.PoolDesc(16, 16, 10, 16, 2, 96, 1)         # head_dim 96 not built
+    assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1, 1, 1, ctypes.byref(d3), 1.0, 16, 0,
+                                None, 0, None) == pk.binding.PKV_ERR_UNSUPPORTED
+    d4 = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, 1)
+    # 3 query heads over 2 KV heads
+    assert lib.pkv_paged_attend(16, 1, 3, 16, 16, 16, 1, 16, 16, 1, 1, 1, 1, ctypes.byref(d4), 1.0, 16, 0,
+                                None, 0, None) == pk.binding.PKV_ERR_INVALID_ARG
+    # 18 query heads over 2 KV heads: G = 9 > 8
+    assert lib.pkv_paged_attend(16, 1, 18, 16, 16, 16, 1, 16, 16, 1, 1, 1, 1, ctypes.byref(d4), 1.0, 16, 0,
+                                None, 0, None) == pk.binding.PKV_ERR_UNSUPPORTED
+    # bf16 output from an fp32 pool
+    d5 = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, 0)
+    assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1, 1, 1, ctypes.byref(d5), 1.0, 16, 1,
+                                None, 0, None) == pk.binding.PKV_ERR_INVALID_ARG
+    # decode rows with a long context need workspace; none given
+    assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1000, 1, 5000, ctypes.byref(d4), 1.0, 16, 0,
+                                None, 0, None) == pk.binding.PKV_ERR_WORKSPACE
+
+
+def test_workspace_sizing():
+    d = pk.binding.PoolDesc(16, 16, 10, 16, 8, 128, 1)
+    lib = pk.lib()
+    pt = pk.decode_partition_tokens()
+    assert lib.pkv_paged_attend_workspace_bytes(64, 64, 32, 1, pt, ctypes.byref(d)) == 0
+    n = lib.pkv_paged_attend_workspace_bytes(64, 64, 32, 1, 4 * pt, ctypes.byref(d))
+    acc = 64 * 32 * 4 * 128 * 4
+    assert n == ((acc + 255) // 256) * 256 + 64 * 32 * 4 * 2 * 4
+
+
+def _random_ops(seed, n_ops=300):
+    rng = np.random.default_rng(seed)
+    nb, bs, slots, maxb = 64, 16, 8, 12
+    order = rng.permutation(nb).astype(np.int32)
+    ours = pk.BlockAllocator(nb, bs, slots, maxb, order)
+    ref = BlockPool(nb, bs, slots, maxb, order)
+    live = set()
+    for _ in range(n_ops):
+        kind = rng.integers(0, 5)
+        if kind == 0 and len(live) < slots:
+            s = int(rng.choice([x for x in range(slots) if x not in live]))
+            ours.acquire(s)
+            ref.acquire(s)
+            live.add(s)
+        elif kind == 1 and live:
+            s = int(rng.choice(sorted(live)))
+            ours.release(s)
+            ref.release(s)
+            live.discard(s)
+        elif kind == 2 and live:
+            s = int(rng.choice(sorted(live)))
+            L = ref.lengths[s]
+            nl = int(rng.integers(0, L + 1))
+            ours.truncate(s, nl)
+            ref.truncate(s, nl)
+        elif kind == 3 and live:
+            s = int(rng.choice(sorted(live)))
+            tot = int(rng.integers(0, maxb * bs + 1))
+            try:
+                ref.reserve(s, tot)
+                ok = True
+            except OracleNoSpace:
+                ok = False
+            if ok:
+                ours.reserve(s, tot)
+            else:
+                with pytest.raises(pk.NoSpace):
+                    ours.reserve(s, tot)
+        elif kind == 4 and live:
+            chosen = [int(x) for x in rng.permutation(sorted(live))[: rng.integers(1, len(live) + 1)]]
+            entries = []
+            for s in chosen:
+                room = maxb * bs - ref.lengths[s]
+                if room >= 1:
+                    entries.append((s, int(rng.integers(1, min(room, 40) + 1))))
+            if not entries:
+                continue
+            try:
+                want = ref.lower_step(entries)
+                ok = True
+            except OracleNoSpace:
+                ok = False
+            if ok:
+                got = ours.lower_step(entries)
+                for k in want:
+                    assert np.array_equal(got[k], want[k]), k
+            else:
+                with pytest.raises(pk.NoSpace):
+                    ours.lower_step(entries)
+        # full state comparison after every op
+        assert ours.free_blocks() == ref.free_count()
+        for s in range(slots):
+            if s in live:
+                assert ours.slot_table(s) == ref.tables[s]
+                assert ours.slot_info(s)[0] == ref.lengths[s]
+            else:
+                assert ours.slot_info(s) is None
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_allocator_and_lowering_match_oracle(seed):
+    _random_ops(seed)
+
+
+def test_allocator_matches_oracle_on_config_workloads():
+    for name in ["1", "2", "4b", "5"]:
+        w = make_workload(name)
+        ours = pk.BlockAllocator(w.num_blocks, w.block_size, w.max_slots, w.max_blocks_per_seq, w.free_order)
+        ref = BlockPool(w.num_blocks, w.block_size, w.max_slots, w.max_blocks_per_seq, w.free_order)
+        for slot, _, _ in w.history:
+            ours.acquire(slot)
+            ref.acquire(slot)
+        ent = [(s, len(k)) for s, k, _ in w.history if len(k)]
+        a, b = ours.lower_step(ent), ref.lower_step(ent)
+        assert all(np.array_equal(a[k], b[k]) for k in b)
+        for st in w.steps:
+            for op in st.ops:
+                getattr(ours, op[0])(*op[1:])
+                {"acquire": ref.acquire, "release": ref.release, "truncate": ref.truncate}[op[0]](*op[1:])
+            ent = [(s.slot, s.n) for s in st.segments]
+            a, b = ours.lower_step(ent), ref.lower_step(ent)
+            assert all(np.array_equal(a[k], b[k]) for k in b)
+            ok, bad = pk.validate_step(a, int(a["query_len"].sum()), w.num_blocks, w.block_size,
+                                       w.max_blocks_per_seq)
+            assert ok, bad
+
+
+def test_worked_example_through_cpp_allocator():
+    order = [7, 2, 9, 4, 1, 8, 0, 3, 5, 6]
+    al = pk.BlockAllocator(10, 16, 4, 8, order)
+    al.acquire(0)
+    al.reserve(0, 64)
+    al.acquire(1)
+    al.reserve(1, 32)
+    assert al.slot_table(0) == [7, 2, 9, 4] and al.slot_table(1) == [1, 8]
+    al.release(1)
+    al.acquire(2)
+    al.reserve(2, 32)
+    assert al.slot_table(2) == [1, 8] and al.slot_table(0) == [7, 2, 9, 4]
+
+
+def test_state_errors():
+    al = pk.BlockAllocator(4, 16, 2, 4)
+    with pytest.raises(pk.PagedKVError):
+        al.release(0)                       # not acquired
+    al.acquire(0)
+    with pytest.raises(pk.PagedKVError):
+        al.acquire(0)                       # twice
+    with pytest.raises(pk.PagedKVError):
+        al.lower_step([(0, 1), (0, 1)])     # same slot twice in one step
+    with pytest.raises(pk.PagedKVError):
+        al.lower_step([(1, 1)])             # slot 1 not acquired
+    with pytest.raises(pk.PagedKVError):
+        al.reserve(0, 5 * 16)               # beyond the table capacity
+    with pytest.raises(pk.NoSpace):
+        al.acquire(1) or al.lower_step([(0, 40), (1, 40)])   # 3 + 3 blocks > 4
+
+
+def test_pool_rounding():
+    assert pk.pool_blocks_for_tokens(98304, 16) == 6144
+    assert pk.pool_blocks_for_tokens(24576, 16) == 1536
+    assert pk.pool_blocks_for_tokens(1, 16) == 1
+    assert pk.pool_blocks_for_tokens(-1, 16) == -1
+
+
+def _meta():
+    return dict(row_to_slot=np.array([2, 0], np.int32), query_start=np.array([0, 3], np.int32),
+                query_len=np.array([3, 1], np.int32), context_lens=np.array([20, 0, 5, 0], np.int32),
+                block_tables=np.array([[1, 2], [0, 0], [3, 0], [0, 0]], np.int32),
+                slot_mapping=np.array([50, 51, 52, 36], np.int32))
+
+
+def test_validator_accepts_good_and_names_each_rule():
+    ok, _ = pk.validate_step(_meta(), 4, 4, 16, 2)
+    assert ok
+    cases = [
+        ("row_to_slot", np.array([2, 2], np.int32), 1),          # slot twice
+        ("row_to_slot", np.array([2, 9], np.int32), 1),          # slot out of range
+        ("query_start", np.array([0, 2], np.int32), 1),          # overlapping rows
+        ("query_len", np.array([3, 2], np.int32), 1),            # beyond total_q
+        ("query_len", np.array([6, 1], np.int32), 0),            # query_len > L (L = 5)
+        ("context_lens", np.array([40, 0, 5, 0], np.int32), 1),  # table capacity 2 blocks
+        ("block_tables", np.array([[1, 7], [0, 0], [3, 0], [0, 0]], np.int32), 1),   # block not in pool
+        ("slot_mapping", np.array([50, 51, 50, 36], np.int32), 2),   # duplicate
+        ("slot_mapping", np.array([50, 51, 52, 64], np.int32), 3),   # outside the pool
+    ]
+    for key, val, bad_idx in cases:
+        m = _meta()
+        m[key] = val
+        ok, bad = pk.validate_step(m, 4, 4, 16, 2)
+        assert not ok and bad == bad_idx, (key, val, bad)

@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV mixed step on one MI355X.
+
+Default workload: 64 decode sequences (bf16, 32 query / 8 KV heads, head_dim
+128, block size 16), context lengths lognormal with median 2048 clipped to
+[16, 32768], slots drawn from 0..127, block tables fragmented by a seeded
+random free order.  A step is the whole hot path: host reservation and
+lowering of the step plan, one async copy of the metadata, kv_append of the
+64 new tokens, and paged attention (decode kernel + split-context reduce).
+Each timed step is a real decode step: every sequence grows by one token.
+
+Prints one JSON line:
+  value        = decode KV bytes read per step x steps / wall time  (GB/s)
+  ms_per_step  = wall time / steps (host lowering included)
+  roofline     = the attention launch (decode + reduce) timed with HIP events
+                 on the stream it runs on, against MI355X peak HBM bandwidth
+  cpu_baseline = the CPU oracle on a bounded sample of the same step
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=64)
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    return ap.parse_args()
+
+
+def decode_bytes(w, lens, elem):
+    """Algorithmic bytes of the decode rows: K and V of every cached token
+    once, plus Q in, fp32 O out and the block-table entries walked."""
+    hkv, hq, d = w.num_kv_heads, w.num_q_heads, w.head_dim
+    kv = sum(2 * L * hkv * d * elem for L in lens)
+    other = sum(hq * d * elem + hq * d * 4 + 4 * (-(-L // 16)) for L in lens)
+    return kv, kv + other
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_attention_slot_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, sample_rows, repeats):
+    """Time the oracle (numpy fp64) on the first `sample_rows` decode rows of
+    the step: block-table walk + fp64 attention, best of `repeats`.  Setup is
+    not timed."""
+    import numpy as np
+    from oracle.attention import paged_attention
+    from oracle.step import place_history, poisoned_pool
+    from oracle.block_pool import BlockPool
+    from oracle.attention import append_reference
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    alloc = BlockPool(w.num_blocks, w.block_size, w.max_slots, w.max_blocks_per_seq, w.free_order)
+    pk_, pv_ = place_history(w, alloc, poisoned_pool(w), poisoned_pool(w))
+    st = w.steps[0]
+    meta = alloc.lower_step([(s.slot, s.n) for s in st.segments])
+    pk_, pv_ = append_reference(pk_, pv_, meta["slot_mapping"], st.k_new, st.v_new, w.block_size)
+    rows = min(sample_rows, len(st.segments))
+    dt = float("inf")
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        paged_attention(st.q[:rows], pk_, pv_, w.dtype, w.block_size, meta["block_tables"], meta["context_lens"],
+                        meta["row_to_slot"][:rows], meta["query_start"][:rows], meta["query_len"][:rows], w.scale)
+        dt = min(dt, time.perf_counter() - t0)
+    lens = [int(meta["context_lens"][s]) for s in meta["row_to_slot"][:rows]]
+    kv, _ = decode_bytes(w, lens, w.elem_bytes)
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy fp64 oracle over the first {rows} of {len(st.segments)} decode rows of one step "
+                      f"({sum(lens)} cached tokens), best of {repeats}: {dt:.2f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
+              "mode", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import paged_kv_attention_slot_amd as pk
+    from workloads import make_workload
+    from workloads.drive import make_engine, place_history, step_tensors
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    w = make_workload(args.config)
+    st = w.steps[0]
+    if any(s.n != 1 for s in st.segments):
+        raise SystemExit("the timed decode loop needs a decode-only config")
+    total_steps = args.warmup + args.steps
+    w.max_blocks_per_seq += -(-total_steps // 16) + 1
+    eng = make_engine(pk.PagedKVEngine, w, device=dev)
+    place_history(eng, w, device=dev)
+    k_new, v_new, q = step_tensors(w, 0, device=dev)
+    entries = [(s.slot, s.n) for s in st.segments]
+    # rolling decode headroom for every step of the run, reserved up front
+    for slot, hk, _ in w.history:
+        eng.reserve(slot, len(hk) + total_steps)
+    out = torch.empty((len(entries), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    kv_total, alg_total, lens_hist = 0, 0, []
+
+    def one_step(i_timed):
+        meta = eng.lower(entries)
+        eng.append(meta, k_new, v_new)
+        if i_timed is not None:
+            ev_a[i_timed].record(stream)
+        eng.attend(meta, q, w.scale, out=out)
+        if i_timed is not None:
+            ev_b[i_timed].record(stream)
+        return meta
+
+    for _ in range(args.warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        meta = one_step(i)
+        lens = meta.host["context_lens"][meta.host["row_to_slot"]].tolist()
+        kv, alg = decode_bytes(w, lens, w.elem_bytes)
+        kv_total += kv
+        alg_total += alg
+        lens_hist.append(sum(lens))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attend_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    attend_avg_s = sum(attend_ms) / len(attend_ms) / 1e3
+    achieved = alg_total / args.steps / attend_avg_s / 1e9
+    src = source_hash("decode.hip")
+    traffic = measured_traffic("decode_config3", src)
+    line = {
+        "metric": "paged-attn decode KV GB/s (% HBM peak); mixed-step latency at 64 seqs",
+        "value": round(kv_total / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"config {w.name}: {w.description}", "decode_rows": len(entries),
+                   "heads_q_kv": [w.num_q_heads, w.num_kv_heads], "head_dim": w.head_dim, "block_size": 16,
+                   "cached_tokens_per_step": int(sum(lens_hist) / len(lens_hist)),
+                   "decode_partition_tokens": pk.decode_partition_tokens()},
+        "pct_hbm_peak": round(100.0 * kv_total / wall / 1e9 / HBM_PEAK_GBS, 2),
+        "attend_ms_avg": round(attend_avg_s * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "pkv decode_kernel + reduce_kernel (one paged_attend launch)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows, args.cpu_repeats)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,9 @@ import re
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PKV_LIBRARY may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libpagedkv.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pagedkv.h")
 
 PKV_OK = 0
@@ -282,6 +284,6 @@ class BlockAllocator:
         st = self._lib.pkv_lower_step(self._h, n, _ptr_i32(slots), _ptr_i32(news), _ptr_i32(out["slot_mapping"]),
                                       len(out["slot_mapping"]), _ptr_i32(out["query_start"]),
                                       _ptr_i32(out["query_len"]), _ptr_i32(out["row_to_slot"]),
-                                      _ptr_i32(out["context_lens"]), _ptr_i32(out["block_tables"]))
+                                      _ptr_i32(out.get("context_lens")), _ptr_i32(out.get("block_tables")))
         _check(st, "pkv_lower_step")
         return out

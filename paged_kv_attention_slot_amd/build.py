@@ -48,30 +48,41 @@ def _run(cmd, verbose):
     return res
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile every source and link the library.  `defines` (NAME=VALUE)
+    override tuning constants; `out`/`build_dir` place a variant build."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    inc = ["-I", INCLUDE, "-I", CSRC]
+    bdir = build_dir or BUILD_DIR
+    lib_path = out or LIB_PATH
+    os.makedirs(bdir, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", CSRC] + [f"-D{d}" for d in defines]
     cmds = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         objs.append(obj)
         cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         objs.append(obj)
         cmds.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for fut in [ex.submit(_run, c, verbose) for c in cmds]:
             fut.result()
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    path = build(verbose="--verbose" in sys.argv)
-    print(path)
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="NAME=VALUE tuning override")
+    ap.add_argument("--out", default=None, help="write the library here instead of the package")
+    ap.add_argument("--build-dir", default=None)
+    a = ap.parse_args()
+    print(build(verbose=a.verbose, defines=a.defines, out=a.out, build_dir=a.build_dir))

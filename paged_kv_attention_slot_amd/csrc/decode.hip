@@ -22,6 +22,7 @@
 // reduce kernel, in partition order.  The reduction order of a row depends
 // only on its own context length.
 #include <cfloat>
+#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -164,19 +165,32 @@ __global__ __launch_bounds__(64) void decode_kernel(AttendArgs a) {
   const int r = lane / LPR;
   const int c = lane % LPR;
 
-  const int u0 = units_of(a, lane);
+  // Lane b keeps segment b's metadata (first 64 segments) so work items do
+  // not re-read it from memory.
+  const SegInfo mine = seg_info(a, lane);
+  const int u0 = mine.ok && (a.multirow || mine.n == 1) ? (a.multirow ? mine.n : 1) * num_parts(mine.L) : 0;
   const int incl0 = wave_inclusive_scan(u0);
   int total = __shfl(incl0, kWave - 1);
   for (int c0 = kWave; c0 < a.num_segments; c0 += kWave) total += wave_sum_int(units_of(a, c0 + lane));
   const int64_t items = static_cast<int64_t>(total) * a.num_kv_heads;
+  const float c_log2 = a.scale_log2;
 
   for (int64_t f = blockIdx.x; f < items; f += gridDim.x) {
     const int unit = static_cast<int>(f / a.num_kv_heads);
     const int g = static_cast<int>(f - static_cast<int64_t>(unit) * a.num_kv_heads);
     int b, rest;
     locate(a, unit, u0, incl0, &b, &rest);
-    const SegInfo si = seg_info(a, b);
-    if (!si.ok) continue;
+    SegInfo si;
+    if (b >= 0 && b < kWave) {
+      si.slot = __builtin_amdgcn_readlane(mine.slot, b);
+      si.L = __builtin_amdgcn_readlane(mine.L, b);
+      si.n = __builtin_amdgcn_readlane(mine.n, b);
+      si.row0 = __builtin_amdgcn_readlane(mine.row0, b);
+      si.ok = true;
+    } else {
+      si = seg_info(a, b);
+      if (!si.ok) continue;
+    }
     const int np = num_parts(si.L);
     const int i = a.multirow ? rest / np : 0;
     const int part = a.multirow ? rest - i * np : rest;
@@ -186,6 +200,8 @@ __global__ __launch_bounds__(64) void decode_kernel(AttendArgs a) {
     const int tok1 = min(limit, tok0 + PT);
     const int hq0 = g * G;
 
+    // Online-softmax state of this lane row: running max m (already scaled by
+    // scale * log2 e), running sum l, unnormalised output acc.
     float m[G], l[G], acc[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -217,13 +233,13 @@ __global__ __launch_bounds__(64) void decode_kernel(AttendArgs a) {
         const uint4 *kp = reinterpret_cast<const uint4 *>(kbase + off);
         const uint4 *vp = reinterpret_cast<const uint4 *>(vbase + off);
 #pragma unroll
-        for (int x = 0; x < NL; ++x) t.k[x] = kp[x * kWave + lane];
+        for (int x = 0; x < NL; ++x) t.k[x] = stream_load(kp + x * kWave + lane);
 #pragma unroll
-        for (int x = 0; x < NL; ++x) t.v[x] = vp[x * kWave + lane];
+        for (int x = 0; x < NL; ++x) t.v[x] = stream_load(vp + x * kWave + lane);
       };
-      auto compute_tile = [&](const Tile<NL> &t, int jj) {
+      auto compute_tile = [&](const Tile<NL> &t, int jj, auto partial_tag) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
         const int tokbase = (j0 + jj) * kBlockTokens;
-        const bool partial = tokbase + kBlockTokens > tok1;
         float s[NL][G];
 #pragma unroll
         for (int x = 0; x < NL; ++x)
@@ -231,55 +247,76 @@ __global__ __launch_bounds__(64) void decode_kernel(AttendArgs a) {
           for (int h = 0; h < G; ++h) s[x][h] = group_sum<LPR>(dot16<T>(t.k[x], q[h]));
         bool valid[NL];
 #pragma unroll
-        for (int x = 0; x < NL; ++x) valid[x] = !partial || (tokbase + x * TPL + r < tok1);
+        for (int x = 0; x < NL; ++x) valid[x] = !PARTIAL || (tokbase + x * TPL + r < tok1);
+        if constexpr (PARTIAL) {
 #pragma unroll
-        for (int x = 0; x < NL; ++x)
+          for (int x = 0; x < NL; ++x)
 #pragma unroll
-          for (int h = 0; h < G; ++h) s[x][h] = valid[x] ? s[x][h] * a.scale_log2 : -INFINITY;
+            for (int h = 0; h < G; ++h) s[x][h] = valid[x] ? s[x][h] : -INFINITY;
+        }
+        // Raise the running max only when this tile exceeds it (rare after
+        // the first tiles); the rescale is skipped for the whole wave otherwise.
+        float mnew[G];
+        bool raise = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float bm = s[0][h];
 #pragma unroll
           for (int x = 1; x < NL; ++x) bm = fmaxf(bm, s[x][h]);
-          const float mn = fmaxf(m[h], bm);
-          const float alpha = fast_exp2(m[h] - mn);
-          m[h] = mn;
-          l[h] *= alpha;
+          mnew[h] = fmaxf(m[h], bm * c_log2);
+          raise |= mnew[h] > m[h];
+        }
+        if (__ballot(raise) != 0) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          for (int h = 0; h < G; ++h) {
+            const float alpha = fast_exp2(m[h] - mnew[h]);
+            m[h] = mnew[h];
+            l[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          }
         }
 #pragma unroll
         for (int x = 0; x < NL; ++x) {
           float vf[EPL];
           unpack16<T, EPL>(t.v[x], vf);
-          if (partial && !valid[x]) {
+          if constexpr (PARTIAL) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) vf[e] = 0.f;   // select, never multiply a poisoned value
+            for (int e = 0; e < EPL; ++e) vf[e] = valid[x] ? vf[e] : 0.f;   // select, never multiply poison
           }
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float p = fast_exp2(s[x][h] - m[h]);
+            const float p = fast_exp2(fmaf(s[x][h], c_log2, -m[h]));
             l[h] += p;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
           }
         }
       };
+      auto compute_any = [&](const Tile<NL> &t, int jj) {
+        if ((j0 + jj + 1) * kBlockTokens > tok1)
+          compute_tile(t, jj, std::true_type{});
+        else
+          compute_tile(t, jj, std::false_type{});
+      };
 
-      // Three tiles in flight.  Out-of-range prefetches re-read the last
-      // tile (a cache hit) so the number of outstanding loads is static.
-      Tile<NL> t0, t1, t2;
-      load_tile(t0, 0);
-      load_tile(t1, min(1, nb - 1));
-      for (int jj = 0; jj < nb; jj += 3) {
-        load_tile(t2, min(jj + 2, nb - 1));
-        compute_tile(t0, jj);
-        if (jj + 1 >= nb) break;
-        load_tile(t0, min(jj + 3, nb - 1));
-        compute_tile(t1, jj + 1);
-        if (jj + 2 >= nb) break;
-        load_tile(t1, min(jj + 4, nb - 1));
-        compute_tile(t2, jj + 2);
+      // kDecodeStages tiles in flight; the scheduling barriers keep each
+      // prefetch ahead of the compute it overlaps.  Out-of-range prefetches
+      // re-read the last tile (a cache hit) so the count of outstanding loads
+      // is static.
+      constexpr int S = kDecodeStages;
+      Tile<NL> t[S];
+#pragma unroll
+      for (int st = 0; st < S - 1; ++st) load_tile(t[st], min(st, nb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      for (int jj = 0; jj < nb; jj += S) {
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+          if (jj + st >= nb) break;
+          load_tile(t[(st + S - 1) % S], min(jj + st + S - 1, nb - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          compute_any(t[st], jj + st);
+        }
       }
     }
 
@@ -399,7 +436,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
 
 template <typename T, int D, int G>
 int launch_decode_t(const AttendArgs &a, int64_t items_bound, hipStream_t stream) {
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * kDecodeWavesPerCU;
   const int64_t grid = items_bound < cap ? items_bound : cap;
   if (grid <= 0) return PKV_OK;
   decode_kernel<T, D, G><<<dim3(static_cast<unsigned>(grid)), dim3(kWave), 0, stream>>>(a);

@@ -22,6 +22,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 16-byte load of data read once (K/V tiles): marked nontemporal so it
+// streams past the caches instead of displacing reused lines.
+typedef unsigned int pkv_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const uint4 *p) {
+#if PKV_STREAM_LOADS
+  const pkv_u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const pkv_u32x4 *>(p));
+  return make_uint4(r.x, r.y, r.z, r.w);
+#else
+  return *p;
+#endif
+}
+
 // Cross-lane moves inside a 16-lane DPP row.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {

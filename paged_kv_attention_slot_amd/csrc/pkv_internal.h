@@ -12,7 +12,24 @@ constexpr int kBlockTokens = 16;  // tokens per pool block (the only block size 
 
 // Tokens per split-context partition of the decode path.  A multiple of the
 // block size and at most 64 blocks (one block-table entry per lane).
-constexpr int32_t kDecodePartitionTokens = 512;
+#ifndef PKV_DECODE_PARTITION_TOKENS
+#define PKV_DECODE_PARTITION_TOKENS 512
+#endif
+constexpr int32_t kDecodePartitionTokens = PKV_DECODE_PARTITION_TOKENS;
+
+// K/V tiles each decode wavefront keeps in flight, and the decode grid size
+// in wavefronts per compute unit.
+#ifndef PKV_DECODE_STAGES
+#define PKV_DECODE_STAGES 1
+#endif
+#ifndef PKV_DECODE_WAVES_PER_CU
+#define PKV_DECODE_WAVES_PER_CU 16
+#endif
+#ifndef PKV_STREAM_LOADS
+#define PKV_STREAM_LOADS 1
+#endif
+constexpr int kDecodeStages = PKV_DECODE_STAGES;
+constexpr int kDecodeWavesPerCU = PKV_DECODE_WAVES_PER_CU;
 
 struct AttendArgs {
   const void *q;

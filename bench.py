@@ -55,6 +55,57 @@ def decode_bytes(w, lens, elem):
     return kv, kv + other
 
 
+def chunk_flops(w, segments, lens):
+    """Causal-visible flops of the multi-row segments: q.k and p.v over the
+    keys each row sees, 2 flops per multiply-add each."""
+    tot = 0
+    for seg, L in zip(segments, lens):
+        if seg.n > 1:
+            visible = sum(L - seg.n + i + 1 for i in range(seg.n))
+            tot += 4 * w.head_dim * w.num_q_heads * visible
+    return tot
+
+
+def run_mixed(args, w, pk, torch, dev):
+    """Replay one mixed step (append + attend with fixed metadata) and time
+    it; for the chunk-bearing configs."""
+    from workloads.drive import make_engine, place_history, step_tensors
+    eng = make_engine(pk.PagedKVEngine, w, device=dev)
+    place_history(eng, w, device=dev)
+    st = w.steps[0]
+    k_new, v_new, q = step_tensors(w, 0, device=dev)
+    meta = eng.lower([(s.slot, s.n) for s in st.segments])
+    out = torch.empty((meta.total_q, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        eng.append(meta, k_new, v_new)
+        eng.attend(meta, q, w.scale, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        eng.append(meta, k_new, v_new)
+        ev[i][0].record(stream)
+        eng.attend(meta, q, w.scale, out=out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    att = sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
+    lens = [int(meta.host["context_lens"][s.slot]) for s in st.segments]
+    dec_lens = [L for s, L in zip(st.segments, lens) if s.n == 1]
+    kv, alg = decode_bytes(w, dec_lens, w.elem_bytes)
+    fl = chunk_flops(w, st.segments, lens)
+    return {"metric": f"mixed-step latency, config {w.name}", "value": round(wall / args.steps * 1e3, 4),
+            "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall / args.steps * 1e3, 4), "attend_ms_avg": round(att * 1e3, 4),
+            "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": f"config {w.name}: {w.description}", "decode_rows": len(dec_lens),
+                       "chunk_rows": int(sum(s.n for s in st.segments if s.n > 1))},
+            "decode_kv_bytes": kv, "chunk_causal_flops": fl,
+            "attend_tflops_if_all_chunk": round(fl / att / 1e12, 2),
+            "roofline_step_ms": round((alg / HBM_PEAK_GBS / 1e9 + fl / BF16_PEAK_TFLOPS / 1e12) * 1e3, 4)}
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -127,7 +178,8 @@ def main():
     w = make_workload(args.config)
     st = w.steps[0]
     if any(s.n != 1 for s in st.segments):
-        raise SystemExit("the timed decode loop needs a decode-only config")
+        print(json.dumps(run_mixed(args, w, pk, torch, dev)), flush=True)
+        return
     total_steps = args.warmup + args.steps
     w.max_blocks_per_seq += -(-total_steps // 16) + 1
     eng = make_engine(pk.PagedKVEngine, w, device=dev)

@@ -43,31 +43,6 @@ struct Geo {
   static constexpr int kTileBytes = kBlockTokens * kRowBytes;
 };
 
-struct SegInfo {
-  int slot, L, n, row0;
-  bool ok;
-};
-
-// Segment b's metadata, with every value that could send a kernel out of
-// bounds rejected or clamped.
-__device__ __forceinline__ SegInfo seg_info(const AttendArgs &a, int b) {
-  SegInfo s{0, 0, 0, 0, false};
-  if (b < 0 || b >= a.num_segments) return s;
-  const int n = a.query_len[b];
-  const int slot = a.row_to_slot[b];
-  const int r0 = a.query_start[b];
-  if (n < 1 || slot < 0 || slot >= a.num_slots || r0 < 0 || r0 > a.total_q - n) return s;
-  int L = a.context_lens[slot];
-  L = min(L, a.max_blocks * kBlockTokens);
-  if (L < n) return s;
-  s.slot = slot;
-  s.L = L;
-  s.n = n;
-  s.row0 = r0;
-  s.ok = true;
-  return s;
-}
-
 __device__ __forceinline__ int num_parts(int L) {
   return (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
 }

@@ -58,7 +58,7 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int lane = threadIdx.x & (kWave - 1);  // works for any wave of a multi-wave block
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     int o = __shfl_up(v, d);
@@ -77,6 +77,66 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d);
   return v;
+}
+
+struct SegInfo {
+  int slot, L, n, row0;
+  bool ok;
+};
+
+// Segment b's metadata, with every value that could send a kernel out of
+// bounds rejected or clamped.
+__device__ __forceinline__ SegInfo seg_info(const AttendArgs &a, int b) {
+  SegInfo s{0, 0, 0, 0, false};
+  if (b < 0 || b >= a.num_segments) return s;
+  const int n = a.query_len[b];
+  const int slot = a.row_to_slot[b];
+  const int r0 = a.query_start[b];
+  if (n < 1 || slot < 0 || slot >= a.num_slots || r0 < 0 || r0 > a.total_q - n) return s;
+  int L = a.context_lens[slot];
+  L = min(L, a.max_blocks * kBlockTokens);
+  if (L < n) return s;
+  s.slot = slot;
+  s.L = L;
+  s.n = n;
+  s.row0 = r0;
+  s.ok = true;
+  return s;
+}
+
+// Work units are numbered segment by segment; units_fn(b) gives segment b's
+// count (0 past the end).  Each wavefront runs these on its own.
+template <typename F>
+__device__ __forceinline__ int count_units(int num_segments, F units_fn) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int total = 0;
+  for (int c0 = 0; c0 < num_segments; c0 += kWave) {
+    int u = units_fn(c0 + lane);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) u += __shfl_xor(u, d);
+    total += u;
+  }
+  return total;
+}
+
+template <typename F>
+__device__ __forceinline__ int find_unit(int num_segments, int unit, F units_fn, int *rest) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int base = 0;
+  for (int c0 = 0; c0 < num_segments; c0 += kWave) {
+    const int u = units_fn(c0 + lane);
+    const int incl = wave_inclusive_scan(u);
+    const int ct = __shfl(incl, kWave - 1);
+    if (unit < base + ct) {
+      const unsigned long long mask = __ballot(base + incl > unit);
+      const int bl = __ffsll(static_cast<long long>(mask)) - 1;
+      *rest = unit - (base + __shfl(incl, bl) - __shfl(u, bl));
+      return c0 + bl;
+    }
+    base += ct;
+  }
+  *rest = 0;
+  return -1;
 }
 
 }  // namespace pkv

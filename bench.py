@@ -7,13 +7,17 @@ Default workload: 64 decode sequences (bf16, 32 query / 8 KV heads, head_dim
 random free order.  A step is the whole hot path: host reservation and
 lowering of the step plan, one async copy of the metadata, kv_append of the
 64 new tokens, and paged attention (decode kernel + split-context reduce).
+The device half is one library call (pkv_mixed_step): the append kernel also
+stages the step's metadata from pinned host memory, then attention runs.
 Each timed step is a real decode step: every sequence grows by one token.
 
 Prints one JSON line:
   value        = decode KV bytes read per step x steps / wall time  (GB/s)
   ms_per_step  = wall time / steps (host lowering included)
-  roofline     = the attention launch (decode + reduce) timed with HIP events
-                 on the stream it runs on, against MI355X peak HBM bandwidth
+  roofline     = the attention launch (decode kernel + partition reduce),
+                 replayed 20 times on the last step's metadata after the timed
+                 steps, each call bracketed by HIP events on its stream;
+                 algorithmic bytes per call / mean duration vs 8 TB/s
   cpu_baseline = the CPU oracle on a bounded sample of the same step
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
@@ -21,6 +25,7 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -43,6 +48,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB device buffer 3 times (a plain copy of known size for counter scaling)")
     return ap.parse_args()
 
 
@@ -82,6 +89,8 @@ def run_mixed(args, w, pk, torch, dev):
         eng.append(meta, k_new, v_new)
         eng.attend(meta, q, w.scale, out=out)
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(args.steps):
         eng.append(meta, k_new, v_new)
@@ -90,6 +99,7 @@ def run_mixed(args, w, pk, torch, dev):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     att = sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
     lens = [int(meta.host["context_lens"][s.slot]) for s in st.segments]
     dec_lens = [L for s, L in zip(st.segments, lens) if s.n == 1]
@@ -167,8 +177,15 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
               "mode", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda:0")     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 2, "launches": 3}))
+        return
     import paged_kv_attention_slot_amd as pk
     from workloads import make_workload
     from workloads.drive import make_engine, place_history, step_tensors
@@ -191,36 +208,44 @@ def main():
         eng.reserve(slot, len(hk) + total_steps)
     out = torch.empty((len(entries), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    kv_total, alg_total, lens_hist = 0, 0, []
+    kv_total, lens_hist = 0, []
 
-    def one_step(i_timed):
-        meta = eng.lower(entries)
-        eng.append(meta, k_new, v_new)
-        if i_timed is not None:
-            ev_a[i_timed].record(stream)
-        eng.attend(meta, q, w.scale, out=out)
-        if i_timed is not None:
-            ev_b[i_timed].record(stream)
+    def one_step():
+        _, meta = eng.fused_step(entries, k_new, v_new, q, w.scale, out=out)
         return meta
 
     for _ in range(args.warmup):
-        one_step(None)
+        one_step()
     torch.cuda.synchronize()
+    metas = []
+    gc.collect()
+    gc.disable()            # no collector pauses inside the timed region
     t0 = time.perf_counter()
     for i in range(args.steps):
-        meta = one_step(i)
+        metas.append(one_step())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gc.enable()
+    for meta in metas:
         lens = meta.host["context_lens"][meta.host["row_to_slot"]].tolist()
         kv, alg = decode_bytes(w, lens, w.elem_bytes)
         kv_total += kv
-        alg_total += alg
         lens_hist.append(sum(lens))
+    # Roofline of the attention launch (decode kernel + partition reduce):
+    # replay it on the last step's metadata, each call bracketed by HIP events
+    # recorded on the stream the kernels run on.
+    last = metas[-1]
+    lens = last.host["context_lens"][last.host["row_to_slot"]].tolist()
+    _, alg_attend = decode_bytes(w, lens, w.elem_bytes)
+    reps = 20
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a_, b_ in ev:
+        a_.record(stream)
+        eng.attend(last, q, w.scale, out=out)
+        b_.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    attend_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
-    attend_avg_s = sum(attend_ms) / len(attend_ms) / 1e3
-    achieved = alg_total / args.steps / attend_avg_s / 1e9
+    attend_avg_s = sum(a_.elapsed_time(b_) for a_, b_ in ev) / reps / 1e3
+    achieved = alg_attend / attend_avg_s / 1e9
     src = source_hash("decode.hip")
     traffic = measured_traffic("decode_config3", src)
     line = {

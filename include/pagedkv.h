@@ -133,6 +133,40 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
                      void *out, int32_t out_dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* One step's device half in two kernel launches (lucebox blog §Chunked prefill
+ * is a slot phase: the chunk appends to the slot's paged KV, then every packed
+ * row attends over it).  The step's metadata, already lowered into pinned host
+ * memory that the device can read (hipHostMalloc), is copied to device memory
+ * by the append kernel itself - no separate copy call - and the attention
+ * kernels read the device copy.  Equivalent to copying host_meta to dev_meta,
+ * then pkv_kv_append, then pkv_paged_attend, on `stream`.
+ *   host_meta     pinned host int32 [meta_len]; must stay unchanged until the
+ *                 step's kernels have run (record an event after the call).
+ *   dev_meta      device int32 [meta_len], overwritten.
+ *   *_off         offsets (in int32) of each array inside host_meta/dev_meta:
+ *                 slot_mapping [num_tokens], query_start / query_len /
+ *                 row_to_slot [num_segments], context_lens [num_slots].
+ *   block_tables  device, as for pkv_paged_attend (kept on the device across
+ *                 steps; only changed tables need re-sending).
+ * Other arguments as for pkv_kv_append and pkv_paged_attend; same status codes. */
+typedef struct {
+  const int32_t *host_meta;
+  int32_t *dev_meta;
+  int32_t meta_len;
+  int32_t slot_mapping_off, query_start_off, query_len_off, row_to_slot_off, context_lens_off;
+  int32_t num_tokens, num_segments, num_slots, total_q, num_q_heads;
+  int32_t max_blocks_per_seq, max_query_len, max_context_len;
+  const void *k_new, *v_new, *q_packed;
+  const int32_t *block_tables;
+  float scale;
+  void *out;
+  int32_t out_dtype;
+  void *workspace;
+  size_t workspace_bytes;
+} pkv_step_desc;
+
+int pkv_mixed_step(const pkv_step_desc *step, const pkv_pool *pool, void *stream);
+
 /* Bytes of workspace pkv_paged_attend needs for these bounds and this pool
  * (split-context partial results).  Pure host arithmetic; returns 0 when no
  * workspace is needed and (size_t)-1 for invalid arguments. */

@@ -39,6 +39,17 @@ class PoolDesc(ctypes.Structure):
                 ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32)]
 
 
+class StepDesc(ctypes.Structure):
+    _fields_ = [("host_meta", _p), ("dev_meta", _p), ("meta_len", _i32),
+                ("slot_mapping_off", _i32), ("query_start_off", _i32), ("query_len_off", _i32),
+                ("row_to_slot_off", _i32), ("context_lens_off", _i32),
+                ("num_tokens", _i32), ("num_segments", _i32), ("num_slots", _i32), ("total_q", _i32),
+                ("num_q_heads", _i32), ("max_blocks_per_seq", _i32), ("max_query_len", _i32),
+                ("max_context_len", _i32), ("k_new", _p), ("v_new", _p), ("q_packed", _p),
+                ("block_tables", _p), ("scale", ctypes.c_float), ("out", _p), ("out_dtype", _i32),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class PagedKVError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
@@ -57,6 +68,7 @@ _SIGNATURES = {
                                 ctypes.POINTER(PoolDesc), ctypes.c_float, _p, _i32, _p, ctypes.c_size_t, _p]),
     "pkv_paged_attend_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc)]),
     "pkv_decode_partition_tokens": (_i32, []),
+    "pkv_mixed_step": (_i32, [ctypes.POINTER(StepDesc), ctypes.POINTER(PoolDesc), _p]),
     "pkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_alloc_create": (_i32, [_i32, _i32, _i32, _i32, _pi32, ctypes.POINTER(_p)]),
     "pkv_alloc_destroy": (None, [_p]),
@@ -156,25 +168,25 @@ class KVPool:
             self.v.fill_(float("nan"))
         self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size = num_blocks, num_kv_heads, head_dim, block_size
         self.dtype = dtype
+        self._desc = PoolDesc(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.block_size,
+                              self.num_kv_heads, self.head_dim, pkv_dtype_of(self.dtype))
+        self._desc_ref = ctypes.byref(self._desc)
 
     def desc(self) -> PoolDesc:
-        return PoolDesc(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.block_size,
-                        self.num_kv_heads, self.head_dim, pkv_dtype_of(self.dtype))
+        return self._desc
 
 
 def kv_append(slot_mapping, k_new, v_new, pool: KVPool, stream=None):
     """Scatter k_new/v_new [T][Hkv][D] into the pool at slot_mapping [T] (device int32)."""
     t = int(slot_mapping.shape[0])
-    d = pool.desc()
-    st = lib().pkv_kv_append(_dptr(slot_mapping), _dptr(k_new), _dptr(v_new), t, ctypes.byref(d),
+    st = lib().pkv_kv_append(_dptr(slot_mapping), _dptr(k_new), _dptr(v_new), t, pool._desc_ref,
                              stream if stream is not None else current_stream_handle())
     _check(st, "pkv_kv_append")
 
 
 def workspace_bytes(num_segments, total_q, num_q_heads, max_query_len, max_context_len, pool: KVPool) -> int:
-    d = pool.desc()
     n = lib().pkv_paged_attend_workspace_bytes(num_segments, total_q, num_q_heads, max_query_len,
-                                               max_context_len, ctypes.byref(d))
+                                               max_context_len, pool._desc_ref)
     if n == ctypes.c_size_t(-1).value:
         raise PagedKVError(PKV_ERR_INVALID_ARG, "pkv_paged_attend_workspace_bytes")
     return int(n)
@@ -187,16 +199,20 @@ def paged_attend(q_packed, row_to_slot, query_start, query_len, context_lens, bl
     total_q, hq = int(q_packed.shape[0]), int(q_packed.shape[1])
     nseg = int(row_to_slot.shape[0])
     num_slots, maxb = int(block_tables.shape[0]), int(block_tables.shape[1])
-    d = pool.desc()
     ws_ptr = _dptr(workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().pkv_paged_attend(_dptr(q_packed), total_q, hq, _dptr(row_to_slot), _dptr(query_start),
                                 _dptr(query_len), nseg, _dptr(context_lens), _dptr(block_tables), num_slots, maxb,
-                                int(max_query_len), int(max_context_len), ctypes.byref(d), float(scale),
+                                int(max_query_len), int(max_context_len), pool._desc_ref, float(scale),
                                 _dptr(out), pkv_dtype_of(out.dtype), ws_ptr, ws_bytes,
                                 stream if stream is not None else current_stream_handle())
     _check(st, "pkv_paged_attend")
     return out
+
+
+def mixed_step(desc: StepDesc, pool: KVPool, stream):
+    """pkv_mixed_step: staged-metadata append + paged attention (two launches)."""
+    _check(lib().pkv_mixed_step(ctypes.byref(desc), pool._desc_ref, stream), "pkv_mixed_step")
 
 
 def decode_partition_tokens() -> int:

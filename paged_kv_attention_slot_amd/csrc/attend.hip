@@ -137,4 +137,26 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
   return launch_decode(a, pool->dtype, pool->head_dim, max_context_len, max_query_len, s);
 }
 
+int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
+  if (!d || !pool_ok(pool) || !d->host_meta || !d->dev_meta || d->meta_len < 0 || d->num_tokens < 0 ||
+      d->num_segments < 0 || d->num_slots <= 0)
+    return PKV_ERR_INVALID_ARG;
+  auto in_meta = [&](int32_t off, int64_t n) { return off >= 0 && off + n <= d->meta_len; };
+  if (!in_meta(d->slot_mapping_off, d->num_tokens) || !in_meta(d->query_start_off, d->num_segments) ||
+      !in_meta(d->query_len_off, d->num_segments) || !in_meta(d->row_to_slot_off, d->num_segments) ||
+      !in_meta(d->context_lens_off, d->num_slots))
+    return PKV_ERR_INVALID_ARG;
+  if (!pool_supported(pool)) return PKV_ERR_UNSUPPORTED;
+  if (d->num_tokens > 0 && (!d->k_new || !d->v_new)) return PKV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int st = launch_kv_append(d->host_meta + d->slot_mapping_off, d->k_new, d->v_new, d->num_tokens, *pool, s,
+                                  d->host_meta, d->dev_meta, d->meta_len);
+  if (st != PKV_OK) return st;
+  const int32_t *m = d->dev_meta;
+  return pkv_paged_attend(d->q_packed, d->total_q, d->num_q_heads, m + d->row_to_slot_off, m + d->query_start_off,
+                          m + d->query_len_off, d->num_segments, m + d->context_lens_off, d->block_tables,
+                          d->num_slots, d->max_blocks_per_seq, d->max_query_len, d->max_context_len, pool, d->scale,
+                          d->out, d->out_dtype, d->workspace, d->workspace_bytes, stream);
+}
+
 }  // extern "C"

@@ -16,58 +16,70 @@
 
 namespace pkv {
 
+struct AppendArgs {
+  const int32_t *slot_mapping;
+  const uint4 *k_new;
+  const uint4 *v_new;
+  uint4 *pool_k;
+  uint4 *pool_v;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int64_t pool_slots;
+  // Optional: copy stage_len int32 of step metadata from stage_src (pinned
+  // host memory the device can read) to stage_dst (device) in the same pass.
+  const int32_t *stage_src;
+  int32_t *stage_dst;
+  int32_t stage_len;
+};
+
 template <int ROW16>
-__global__ __launch_bounds__(256) void kv_append_kernel(const int32_t *__restrict__ slot_mapping,
-                                                        const uint4 *__restrict__ k_new,
-                                                        const uint4 *__restrict__ v_new,
-                                                        uint4 *__restrict__ pool_k,
-                                                        uint4 *__restrict__ pool_v, int32_t num_tokens,
-                                                        int32_t num_kv_heads, int64_t pool_slots) {
-  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * ROW16;
-  const int64_t total = per_token * num_tokens;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < total;
-       c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = tid; i < a.stage_len; i += nthreads) a.stage_dst[i] = a.stage_src[i];
+  const int64_t per_token = static_cast<int64_t>(a.num_kv_heads) * ROW16;
+  const int64_t total = per_token * a.num_tokens;
+  for (int64_t c = tid; c < total; c += nthreads) {
     const int64_t t = c / per_token;
     const int64_t rem = c - t * per_token;
     const int64_t h = rem / ROW16;
     const int64_t w = rem - h * ROW16;
-    const int64_t s = slot_mapping[t];
-    if (s < 0 || s >= pool_slots) continue;
+    const int64_t s = a.slot_mapping[t];
+    if (s < 0 || s >= a.pool_slots) continue;
     const int64_t blk = s / kBlockTokens;
     const int64_t off = s - blk * kBlockTokens;
-    const int64_t dst = ((blk * num_kv_heads + h) * kBlockTokens + off) * ROW16 + w;
-    pool_k[dst] = k_new[c];
-    pool_v[dst] = v_new[c];
+    const int64_t dst = ((blk * a.num_kv_heads + h) * kBlockTokens + off) * ROW16 + w;
+    a.pool_k[dst] = a.k_new[c];
+    a.pool_v[dst] = a.v_new[c];
   }
 }
 
-int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
-                     int32_t num_tokens, const pkv_pool &pool, hipStream_t stream) {
+int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new, int32_t num_tokens,
+                     const pkv_pool &pool, hipStream_t stream, const int32_t *stage_src, int32_t *stage_dst,
+                     int32_t stage_len) {
   const int row16 = pool.head_dim * (pool.dtype == PKV_F32 ? 4 : 2) / 16;
   const int64_t units = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * row16;
   const int threads = 256;
-  int64_t blocks = (units + threads - 1) / threads;
+  int64_t blocks = ((units > stage_len ? units : stage_len) + threads - 1) / threads;
+  if (blocks < 1) blocks = 1;
   if (blocks > 65536) blocks = 65536;
-  const int64_t pool_slots = static_cast<int64_t>(pool.num_blocks) * pool.block_size;
-  auto *pk = static_cast<uint4 *>(pool.k);
-  auto *pv = static_cast<uint4 *>(pool.v);
-  auto *kn = static_cast<const uint4 *>(k_new);
-  auto *vn = static_cast<const uint4 *>(v_new);
+  AppendArgs a;
+  a.slot_mapping = slot_mapping;
+  a.k_new = static_cast<const uint4 *>(k_new);
+  a.v_new = static_cast<const uint4 *>(v_new);
+  a.pool_k = static_cast<uint4 *>(pool.k);
+  a.pool_v = static_cast<uint4 *>(pool.v);
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = pool.num_kv_heads;
+  a.pool_slots = static_cast<int64_t>(pool.num_blocks) * pool.block_size;
+  a.stage_src = stage_src;
+  a.stage_dst = stage_dst;
+  a.stage_len = stage_src && stage_dst ? stage_len : 0;
   switch (row16) {
-    case 8:
-      kv_append_kernel<8><<<dim3(blocks), dim3(threads), 0, stream>>>(slot_mapping, kn, vn, pk, pv, num_tokens,
-                                                                     pool.num_kv_heads, pool_slots);
-      break;
-    case 16:
-      kv_append_kernel<16><<<dim3(blocks), dim3(threads), 0, stream>>>(slot_mapping, kn, vn, pk, pv, num_tokens,
-                                                                      pool.num_kv_heads, pool_slots);
-      break;
-    case 32:
-      kv_append_kernel<32><<<dim3(blocks), dim3(threads), 0, stream>>>(slot_mapping, kn, vn, pk, pv, num_tokens,
-                                                                      pool.num_kv_heads, pool_slots);
-      break;
-    default:
-      return PKV_ERR_UNSUPPORTED;
+    case 8: kv_append_kernel<8><<<dim3(blocks), dim3(threads), 0, stream>>>(a); break;
+    case 16: kv_append_kernel<16><<<dim3(blocks), dim3(threads), 0, stream>>>(a); break;
+    case 32: kv_append_kernel<32><<<dim3(blocks), dim3(threads), 0, stream>>>(a); break;
+    default: return PKV_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -57,8 +57,11 @@ struct AttendArgs {
   float scale_log2;     // scale * log2(e)
 };
 
+// KV append; optionally also copies stage_len int32 of step metadata from
+// device-readable pinned host memory to a device buffer in the same launch.
 int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
-                     int32_t num_tokens, const pkv_pool &pool, hipStream_t stream);
+                     int32_t num_tokens, const pkv_pool &pool, hipStream_t stream,
+                     const int32_t *stage_src = nullptr, int32_t *stage_dst = nullptr, int32_t stage_len = 0);
 
 // Decode path (one query row per work item; split-context partitions) and the
 // partition reduce.  `max_query_len`/`max_context_len` size the grid only.

@@ -9,8 +9,11 @@ all on the caller's current stream.  It plays the role the lucebox blog
 scheduler: it owns the slots' block tables and lowers the selected prompt
 chunks and decode rows into the packed layout the kernels read.
 
-Metadata travels in one pinned host buffer per step (two buffers used in
-turn, each reused only after its previous copy has finished).  The device
+Metadata travels in one pinned host buffer per step, copied on the step's
+own stream (so stream order protects the device copy).  A ring of buffers
+is used in turn; a host buffer is rewritten only after the copy that last
+read it has finished, which with a ring this deep has always happened
+already - the host never sleeps on the GPU inside the step loop.  The device
 block tables are re-sent only when a table changed (a block was reserved,
 released or truncated); slots that reserved decode headroom ahead of time
 (§Admission and step planning: capacity for the prompt and rolling decode
@@ -33,22 +36,27 @@ class StepMeta:
     query_len: object
     row_to_slot: object
     context_lens: object      # device int32 [max_slots]
+    stream: object            # handle of the stream the step was lowered on
     total_q: int
     max_query_len: int
     max_context_len: int
 
 
 class _Staging:
-    """A pinned host int32 buffer, its device twin and the event of its last copy."""
+    """A pinned host int32 buffer, its device twin, and the event recorded
+    after the copy that last read the host buffer."""
 
     def __init__(self, torch, device, n):
         self.host = torch.empty(n, dtype=torch.int32, pin_memory=True)
         self.dev = torch.empty(n, dtype=torch.int32, device=device)
         self.np = self.host.numpy()
-        self.event = None
+        self.copied = torch.cuda.Event()
+        self.used = False
 
 
 class PagedKVEngine:
+    STAGING_RING = 8
+
     def __init__(self, *, num_blocks, num_kv_heads, num_q_heads, head_dim, dtype, max_slots,
                  max_blocks_per_seq, free_order=None, device="cuda", poison=True):
         import torch
@@ -65,6 +73,8 @@ class PagedKVEngine:
         self._staging = []
         self._turn = 0
         self._workspace = None
+        self._ws_key = None
+        self._ws_bytes = 0
 
     # -- slot lifecycle (host allocator) --------------------------------
     def acquire(self, slot):
@@ -86,13 +96,13 @@ class PagedKVEngine:
     # -- one step ---------------------------------------------------------
     def _stage(self, n):
         torch = self.torch
-        if len(self._staging) < 2 or self._staging[0].np.size < n:
+        if not self._staging or self._staging[0].np.size < n:
             cap = max(n, 4096)
-            self._staging = [_Staging(torch, self.device, cap), _Staging(torch, self.device, cap)]
+            self._staging = [_Staging(torch, self.device, cap) for _ in range(self.STAGING_RING)]
         st = self._staging[self._turn]
-        self._turn ^= 1
-        if st.event is not None:
-            st.event.synchronize()          # the copy that last used this buffer is done
+        self._turn = (self._turn + 1) % self.STAGING_RING
+        if st.used and not st.copied.query():
+            st.copied.synchronize()         # the DMA that last read this host buffer is done
         return st
 
     def _refresh_tables(self):
@@ -105,8 +115,10 @@ class PagedKVEngine:
         self.d_block_tables.copy_(self.torch.from_numpy(self.h_block_tables))
         self._tables_dirty = False
 
-    def lower(self, entries) -> StepMeta:
+    def _lower_host(self, entries):
+        """Lower the step into the next pinned staging buffer (host only)."""
         torch = self.torch
+        stream = torch.cuda.current_stream(self.device)
         nseg = len(entries)
         t = int(sum(e[1] for e in entries))
         # packed metadata: slot_mapping | query_start | query_len | row_to_slot | context_lens
@@ -120,28 +132,58 @@ class PagedKVEngine:
         self.alloc.lower_step(entries, out=host)
         if self.alloc.free_blocks() != free_before:
             self._tables_dirty = True
-        st.dev[:offs[-1]].copy_(st.host[:offs[-1]], non_blocking=True)
         if self._tables_dirty:
             self._refresh_tables()
-        st.event = torch.cuda.Event()
-        st.event.record()
         d = st.dev
         ql = host["query_len"]
         ctx = host["context_lens"][host["row_to_slot"]] if nseg else np.zeros(0, np.int32)
         snapshot = {k: np.array(v) for k, v in host.items()}
         snapshot["block_tables"] = self.h_block_tables
-        return StepMeta(host=snapshot, slot_mapping=d[offs[0]:offs[1]], query_start=d[offs[1]:offs[2]],
+        meta = StepMeta(host=snapshot, slot_mapping=d[offs[0]:offs[1]], query_start=d[offs[1]:offs[2]],
                         query_len=d[offs[2]:offs[3]], row_to_slot=d[offs[3]:offs[4]],
-                        context_lens=d[offs[4]:offs[5]], total_q=t,
-                        max_query_len=int(ql.max()) if nseg else 0,
+                        context_lens=d[offs[4]:offs[5]], stream=B.ctypes.c_void_p(stream.cuda_stream),
+                        total_q=t, max_query_len=int(ql.max()) if nseg else 0,
                         max_context_len=int(ctx.max()) if nseg else 0)
+        return meta, st, offs, stream
+
+    def lower(self, entries) -> StepMeta:
+        """Lower the step and copy its metadata to the device (stream order)."""
+        meta, st, offs, stream = self._lower_host(entries)
+        st.dev[:offs[-1]].copy_(st.host[:offs[-1]], non_blocking=True)
+        st.copied.record(stream)
+        st.used = True
+        return meta
+
+    def fused_step(self, entries, k_new, v_new, q, scale, out=None, out_dtype=None):
+        """Lower on the host, then one library call (pkv_mixed_step): the append
+        kernel stages the metadata to the device and appends; attention follows."""
+        torch = self.torch
+        meta, st, offs, stream = self._lower_host(entries)
+        if out is None:
+            out = torch.empty((meta.total_q, self.num_q_heads, self.pool.head_dim),
+                              dtype=out_dtype or torch.float32, device=self.device)
+        ws = self.workspace_for(meta)
+        nseg = len(entries)
+        desc = B.StepDesc(st.host.data_ptr(), st.dev.data_ptr(), offs[-1], offs[0], offs[1], offs[2], offs[3], offs[4],
+                          meta.total_q, nseg, self.max_slots, meta.total_q, self.num_q_heads, self.max_blocks_per_seq,
+                          meta.max_query_len, meta.max_context_len, k_new.data_ptr(), v_new.data_ptr(),
+                          q.data_ptr(), self.d_block_tables.data_ptr(), float(scale), out.data_ptr(),
+                          B.pkv_dtype_of(out.dtype), ws.data_ptr() if ws is not None else None,
+                          ws.numel() if ws is not None else 0)
+        B.mixed_step(desc, self.pool, meta.stream)
+        st.copied.record(stream)          # the step's kernels have read the host buffer after this
+        st.used = True
+        return out, meta
 
     def append(self, meta: StepMeta, k_new, v_new):
-        B.kv_append(meta.slot_mapping, k_new, v_new, self.pool)
+        B.kv_append(meta.slot_mapping, k_new, v_new, self.pool, stream=meta.stream)
 
     def workspace_for(self, meta: StepMeta):
-        n = B.workspace_bytes(len(meta.host["row_to_slot"]), meta.total_q, self.num_q_heads, meta.max_query_len,
-                              meta.max_context_len, self.pool)
+        key = (len(meta.host["row_to_slot"]), meta.total_q, meta.max_query_len, meta.max_context_len)
+        if key != self._ws_key:
+            self._ws_bytes = B.workspace_bytes(key[0], key[1], self.num_q_heads, key[2], key[3], self.pool)
+            self._ws_key = key
+        n = self._ws_bytes
         if n == 0:
             return None
         if self._workspace is None or self._workspace.numel() < n:
@@ -153,9 +195,11 @@ class PagedKVEngine:
         if out is None:
             out = torch.empty((meta.total_q, self.num_q_heads, self.pool.head_dim),
                               dtype=out_dtype or torch.float32, device=self.device)
-        return B.paged_attend(q, meta.row_to_slot, meta.query_start, meta.query_len, meta.context_lens,
-                              self.d_block_tables, self.pool, scale, max_query_len=meta.max_query_len,
-                              max_context_len=meta.max_context_len, out=out, workspace=self.workspace_for(meta))
+        res = B.paged_attend(q, meta.row_to_slot, meta.query_start, meta.query_len, meta.context_lens,
+                             self.d_block_tables, self.pool, scale, max_query_len=meta.max_query_len,
+                             max_context_len=meta.max_context_len, out=out, workspace=self.workspace_for(meta),
+                             stream=meta.stream)
+        return res
 
     def step(self, entries, k_new, v_new, q, scale, out=None, out_dtype=None):
         meta = self.lower(entries)

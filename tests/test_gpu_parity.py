@@ -49,7 +49,7 @@ def _oracle_bits(a):
     return a.view(np.int16) if a.dtype == np.uint16 else a.view(np.int32)
 
 
-def _run_gpu(w, steps=None, out_dtype=None, free_order=None):
+def _run_gpu(w, steps=None, out_dtype=None, free_order=None, fused=False):
     import torch
     eng = make_engine(pk.PagedKVEngine, w, free_order=free_order)
     place_history(eng, w)
@@ -57,7 +57,7 @@ def _run_gpu(w, steps=None, out_dtype=None, free_order=None):
     for i in range(len(w.steps)):
         if steps is not None and i not in steps:
             break
-        out, meta = run_step(eng, w, i, out_dtype=out_dtype)
+        out, meta = run_step(eng, w, i, out_dtype=out_dtype, fused=fused)
         torch.cuda.synchronize()
         outs.append((out, meta))
     return eng, outs
@@ -73,11 +73,12 @@ def _check_close(name, got, want, tol):
 
 
 # ------------------------------------------------------------------ append
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
 @pytest.mark.parametrize("name", ["1", "2", "4b", "5"])
-def test_kv_append_bit_exact_whole_pool(name, gpu_available):
-    _log(f"append config {name}")
+def test_kv_append_bit_exact_whole_pool(name, fused, gpu_available):
+    _log(f"append config {name} fused={fused}")
     w = _workload(name)
-    eng, _ = _run_gpu(w)
+    eng, _ = _run_gpu(w, fused=fused)
     _, (ok, ov) = _oracle(name)
     assert np.array_equal(_pool_bits(eng.pool.k), _oracle_bits(ok))
     assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
@@ -99,11 +100,12 @@ def test_kv_append_skips_out_of_pool_entries_and_empty(gpu_available):
 
 
 # ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
 @pytest.mark.parametrize("name", ["1", "1+1", "3", "2", "4a", "4b", "5"])
-def test_attention_matches_oracle(name, gpu_available):
-    _log(f"attention config {name}")
+def test_attention_matches_oracle(name, fused, gpu_available):
+    _log(f"attention config {name} fused={fused}")
     w = _workload(name)
-    _, outs = _run_gpu(w)
+    _, outs = _run_gpu(w, fused=fused)
     res, _ = _oracle(name)
     for i, ((out, _), r) in enumerate(zip(outs, res)):
         _check_close(f"config {name} step {i}", out, r["out"], TOL[w.dtype])
@@ -181,12 +183,13 @@ def test_block_permutation_invariance_bitwise(gpu_available):
     assert torch.equal(o1[0][0].cpu(), o2[0][0].cpu())
 
 
-def test_slot_reuse_leaves_other_slots_bitwise_unchanged(gpu_available):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+def test_slot_reuse_leaves_other_slots_bitwise_unchanged(fused, gpu_available):
     """Config 5: after slot 3 is released and its blocks reused by a new
     prompt, the replayed rows of slots 0, 1, 2, 4 are bitwise unchanged."""
     import torch
     w = _workload("5")
-    _, outs = _run_gpu(w)
+    _, outs = _run_gpu(w, fused=fused)
     s1, s2 = outs[0][0].cpu(), outs[1][0].cpu()
     for i in (0, 1, 2):
         assert torch.equal(s2[16 * i:16 * i + 16], s1[16 * i:16 * i + 16])

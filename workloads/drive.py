@@ -60,10 +60,13 @@ def step_tensors(w, step_index, device="cuda"):
             to_device(st.q, w.dtype, device))
 
 
-def run_step(engine, w, step_index, device="cuda", out_dtype=None):
-    """Apply the step's slot ops, then lower + append + attend.  Returns
-    (out tensor, StepMeta)."""
+def run_step(engine, w, step_index, device="cuda", out_dtype=None, fused=False):
+    """Apply the step's slot ops, then lower + append + attend (separate
+    calls, or the one-call fused step).  Returns (out tensor, StepMeta)."""
     st = w.steps[step_index]
     apply_ops(engine, st.ops)
     k, v, q = step_tensors(w, step_index, device)
-    return engine.step([(s.slot, s.n) for s in st.segments], k, v, q, w.scale, out_dtype=out_dtype)
+    entries = [(s.slot, s.n) for s in st.segments]
+    if fused:
+        return engine.fused_step(entries, k, v, q, w.scale, out_dtype=out_dtype)
+    return engine.step(entries, k, v, q, w.scale, out_dtype=out_dtype)

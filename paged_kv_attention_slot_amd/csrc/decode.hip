@@ -442,7 +442,9 @@ int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t 
   const int64_t rows = a.multirow ? static_cast<int64_t>(a.total_q) : a.num_segments;
   const int64_t items_bound = rows * (parts > 0 ? parts : 1) * a.num_kv_heads;
   int st;
-  if (dtype == PKV_BF16) {
+  if (dtype == PKV_BF16 && !a.multirow && PKV_DECODE_MFMA) {
+    st = launch_decode_mfma(a, head_dim, max_context_len, stream);
+  } else if (dtype == PKV_BF16) {
     st = head_dim == 128 ? dispatch_g<uint16_t, 128>(a, G, items_bound, stream)
                          : dispatch_g<uint16_t, 64>(a, G, items_bound, stream);
   } else {

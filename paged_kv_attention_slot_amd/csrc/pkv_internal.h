@@ -25,8 +25,24 @@ constexpr int32_t kDecodePartitionTokens = PKV_DECODE_PARTITION_TOKENS;
 #ifndef PKV_DECODE_WAVES_PER_CU
 #define PKV_DECODE_WAVES_PER_CU 16
 #endif
+// bf16 decode rows on MFMA tiles (decode_mfma.hip) instead of the vector-ALU
+// decode kernel (decode.hip, always used for fp32 pools).
+#ifndef PKV_DECODE_MFMA
+#define PKV_DECODE_MFMA 1
+#endif
+// Minimum wavefronts per SIMD the MFMA decode kernel is compiled for (caps
+// its registers so that many waves stay resident to hide memory latency).
+#ifndef PKV_DECODE_MFMA_MIN_WAVES
+#define PKV_DECODE_MFMA_MIN_WAVES 3
+#endif
+constexpr int kDecodeMfmaMinWaves = PKV_DECODE_MFMA_MIN_WAVES;
 #ifndef PKV_STREAM_LOADS
 #define PKV_STREAM_LOADS 1
+#endif
+#if PKV_STREAM_LOADS
+#define PKV_LDS_DMA_HINT "nt"
+#else
+#define PKV_LDS_DMA_HINT ""
 #endif
 constexpr int kDecodeStages = PKV_DECODE_STAGES;
 constexpr int kDecodeWavesPerCU = PKV_DECODE_WAVES_PER_CU;
@@ -67,6 +83,8 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
 // partition reduce.  `max_query_len`/`max_context_len` size the grid only.
 int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len,
                   int32_t max_query_len, hipStream_t stream);
+
+int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, hipStream_t stream);
 
 // Multi-row segments (query_len > 1) on bf16 MFMA tiles.  chunk_supported()
 // tells whether this shape is built; otherwise multi-row segments take the

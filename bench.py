@@ -36,6 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+# Sources of the measured attention launch: a counter summary in
+# profiles/traffic.json counts only while these files are unchanged.
+TRAFFIC_SOURCES = ("decode_mfma.hip", "decode.hip", "pkv_device.h", "pkv_internal.h")
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 
 
@@ -246,7 +249,7 @@ def main():
     torch.cuda.synchronize()
     attend_avg_s = sum(a_.elapsed_time(b_) for a_, b_ in ev) / reps / 1e3
     achieved = alg_attend / attend_avg_s / 1e9
-    src = source_hash("decode.hip")
+    src = source_hash(*TRAFFIC_SOURCES)
     traffic = measured_traffic("decode_config3", src)
     line = {
         "metric": "paged-attn decode KV GB/s (% HBM peak); mixed-step latency at 64 seqs",

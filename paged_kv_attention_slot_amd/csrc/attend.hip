@@ -32,23 +32,31 @@ bool multirow_on_decode_path(int32_t dtype, int32_t head_dim, int32_t group, int
 
 struct WorkspaceLayout {
   int64_t rows = 0, part_max = 0;
-  size_t acc_bytes = 0, ml_bytes = 0;
-  size_t total() const { return acc_bytes + ml_bytes; }
+  size_t acc_bytes = 0, ml_bytes = 0, chunk_bytes = 0;
+  size_t decode_bytes() const { return acc_bytes + ml_bytes; }
+  size_t total() const { return acc_bytes + ml_bytes + chunk_bytes; }
 };
 
 WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_query_len, int32_t max_context_len, int32_t dtype, int32_t group) {
   WorkspaceLayout w;
+  const bool multirow = multirow_on_decode_path(dtype, head_dim, group, max_query_len);
   w.part_max = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
   if (w.part_max <= 1) {
     w.part_max = 1;
-    return w;
+  } else {
+    w.rows = multirow ? total_q : num_segments;
+    const int64_t n = w.rows * num_q_heads * w.part_max;
+    w.acc_bytes = static_cast<size_t>(n) * head_dim * sizeof(float);
+    w.acc_bytes = (w.acc_bytes + 255) & ~static_cast<size_t>(255);
+    w.ml_bytes = static_cast<size_t>(n) * 2 * sizeof(float);
+    w.ml_bytes = (w.ml_bytes + 255) & ~static_cast<size_t>(255);
   }
-  w.rows = multirow_on_decode_path(dtype, head_dim, group, max_query_len) ? total_q : num_segments;
-  const int64_t n = w.rows * num_q_heads * w.part_max;
-  w.acc_bytes = static_cast<size_t>(n) * head_dim * sizeof(float);
-  w.acc_bytes = (w.acc_bytes + 255) & ~static_cast<size_t>(255);
-  w.ml_bytes = static_cast<size_t>(n) * 2 * sizeof(float);
+  if (max_query_len > 1 && !multirow && group > 0) {
+    // key-range partials of split multi-row segments (see chunk.hip)
+    const int64_t kv_heads = num_q_heads / group;
+    w.chunk_bytes = static_cast<size_t>(num_segments) * kv_heads * kChunkSplitSlots * (head_dim + 4) * sizeof(float);
+  }
   return w;
 }
 
@@ -114,8 +122,10 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
   a.query_len = query_len;
   a.context_lens = context_lens;
   a.block_tables = block_tables;
-  a.part_acc = ws.total() ? static_cast<float *>(workspace) : nullptr;
-  a.part_ml = ws.total() ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.acc_bytes) : nullptr;
+  a.part_acc = ws.decode_bytes() ? static_cast<float *>(workspace) : nullptr;
+  a.part_ml = ws.decode_bytes() ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.acc_bytes) : nullptr;
+  a.chunk_part =
+      ws.chunk_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.decode_bytes()) : nullptr;
   a.num_segments = num_segments;
   a.num_slots = num_slots;
   a.max_blocks = max_blocks_per_seq;

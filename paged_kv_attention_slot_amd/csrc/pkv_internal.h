@@ -45,6 +45,30 @@ constexpr int kDecodeMfmaMinWaves = PKV_DECODE_MFMA_MIN_WAVES;
 #define PKV_LDS_DMA_HINT ""
 #endif
 constexpr int kDecodeStages = PKV_DECODE_STAGES;
+
+// Multi-row segments with fewer than this many 128-row tiles split their
+// key range so that (row tiles x splits) reaches it; partial slots per
+// (segment, KV head) = kChunkSplitRowTiles * 128.
+constexpr int kChunkSplitRowTiles = 32;
+constexpr int kChunkSplitSlots = kChunkSplitRowTiles * 128;
+
+// Chunk kernel LDS ring: tokens per stage and stages, per head_dim.
+#ifndef PKV_CHUNK_RING_TOK_D64
+#define PKV_CHUNK_RING_TOK_D64 64
+#endif
+#ifndef PKV_CHUNK_RING_STAGES_D64
+#define PKV_CHUNK_RING_STAGES_D64 3
+#endif
+#ifndef PKV_CHUNK_RING_TOK_D128
+#define PKV_CHUNK_RING_TOK_D128 32
+#endif
+#ifndef PKV_CHUNK_RING_STAGES_D128
+#define PKV_CHUNK_RING_STAGES_D128 4
+#endif
+// floats per partial slot: D accumulators, running max, running sum, padding
+// to a 16-byte multiple
+template <int D>
+constexpr int kChunkSlotFloats = D + 4;
 constexpr int kDecodeWavesPerCU = PKV_DECODE_WAVES_PER_CU;
 
 struct AttendArgs {
@@ -59,6 +83,7 @@ struct AttendArgs {
   const int32_t *block_tables;
   float *part_acc;   // [part_rows][Hq][part_max][D]
   float *part_ml;    // [part_rows][Hq][part_max][2]  (running max in log2 units, sum)
+  float *chunk_part; // [num_segments][Hkv][kChunkSplitSlots][D + 4]: key-range partials of split chunks
   int32_t num_segments;
   int32_t num_slots;
   int32_t max_blocks;

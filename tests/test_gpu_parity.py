@@ -117,6 +117,7 @@ EDGE_SEQS = [
     [(0, 511, 1), (1, 512, 1), (2, 1023, 1), (3, 1024, 1)],   # partition edges
     [(5, 3000, 1), (2, 7, 1)],                    # slots out of order
     [(0, 0, 5), (1, 40, 1), (2, 3, 2)],           # tiny prompt, decode, 2 drafts
+    [(0, 700, 16), (1, 3000, 3), (2, 200, 40), (3, 1300, 1)],   # key-range splits of short segments
 ]
 
 
@@ -172,6 +173,26 @@ def test_decode_batch_composition_invariance_bitwise(gpu_available):
     _, o2 = _run_gpu(w2)
     a, b = o1[0][0].cpu(), o2[0][0].cpu()
     assert torch.equal(a[3], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_chunk_batch_composition_invariance_bitwise(gpu_available):
+    """Multi-row segments (split and unsplit) give the same bits whatever
+    else shares the step."""
+    import torch
+    base = [(0, 900, 16), (1, 50, 1), (2, 100, 300), (3, 2000, 1)]
+    w1 = make_custom(base, dtype="bf16", hq=32, hkv=8, d=128, seed=81)
+    _, o1 = _run_gpu(w1)
+    w2 = make_custom(base, dtype="bf16", hq=32, hkv=8, d=128, seed=81)
+    st = w2.steps[0]
+    keep = [2, 0]
+    rows = {0: slice(0, 16), 2: slice(17, 317)}
+    st.segments = [st.segments[i] for i in keep]
+    st.q = np.concatenate([st.q[rows[i]] for i in keep])
+    st.k_new = np.concatenate([st.k_new[rows[i]] for i in keep])
+    st.v_new = np.concatenate([st.v_new[rows[i]] for i in keep])
+    _, o2 = _run_gpu(w2)
+    a, b = o1[0][0].cpu(), o2[0][0].cpu()
+    assert torch.equal(a[17:317], b[0:300]) and torch.equal(a[0:16], b[300:316])
 
 
 def test_block_permutation_invariance_bitwise(gpu_available):

@@ -113,7 +113,8 @@ int pkv_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_
  *   max_query_len, max_context_len   host upper bounds over the segments
  *                 (used for grid and workspace sizing only; a value smaller
  *                 than the truth gives unspecified results).
- *   scale         softmax scale (1/sqrt(head_dim) for standard attention).
+ *   scale         softmax scale (1/sqrt(head_dim) for standard attention);
+ *                 finite and > 0, else PKV_ERR_INVALID_ARG.
  *   out           device [total_q][num_q_heads][head_dim]; out_dtype PKV_F32,
  *                 or PKV_BF16 when the pool is bf16 (rounded to nearest even).
  *   workspace     device scratch of at least pkv_paged_attend_workspace_bytes
@@ -148,7 +149,9 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
  *                 row_to_slot [num_segments], context_lens [num_slots].
  *   block_tables  device, as for pkv_paged_attend (kept on the device across
  *                 steps; only changed tables need re-sending).
- * Other arguments as for pkv_kv_append and pkv_paged_attend; same status codes. */
+ * Other arguments as for pkv_kv_append and pkv_paged_attend; same status codes.
+ * Argument errors (a bad scale included) are returned before anything is
+ * appended. */
 typedef struct {
   const int32_t *host_meta;
   int32_t *dev_meta;

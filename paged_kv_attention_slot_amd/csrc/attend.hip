@@ -1,5 +1,7 @@
 // C-ABI entry points for the device side: argument checks, workspace sizing
 // and kernel dispatch on the caller's stream.
+#include <cmath>
+
 #include "pagedkv.h"
 #include "pkv_internal.h"
 
@@ -87,6 +89,9 @@ size_t pkv_paged_attend_workspace_bytes(int32_t num_segments, int32_t total_q, i
       .total();
 }
 
+// The causal mask and the running max assume a positive, finite scale.
+static bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
 int32_t pkv_decode_partition_tokens(void) { return kDecodePartitionTokens; }
 
 int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int32_t *row_to_slot,
@@ -98,7 +103,7 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
   if (!pool_ok(pool) || total_q < 0 || num_segments < 0 || num_q_heads <= 0 || num_slots <= 0 ||
       max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0)
     return PKV_ERR_INVALID_ARG;
-  if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads != 0 || !scale_ok(scale)) return PKV_ERR_INVALID_ARG;
   if (out_dtype != PKV_F32 && !(out_dtype == PKV_BF16 && pool->dtype == PKV_BF16)) return PKV_ERR_INVALID_ARG;
   if (!pool_supported(pool) || num_q_heads / pool->num_kv_heads > 8) return PKV_ERR_UNSUPPORTED;
   if (num_segments == 0 || total_q == 0) return PKV_OK;
@@ -149,7 +154,7 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
 
 int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
   if (!d || !pool_ok(pool) || !d->host_meta || !d->dev_meta || d->meta_len < 0 || d->num_tokens < 0 ||
-      d->num_segments < 0 || d->num_slots <= 0)
+      d->num_segments < 0 || d->num_slots <= 0 || !scale_ok(d->scale))
     return PKV_ERR_INVALID_ARG;
   auto in_meta = [&](int32_t off, int64_t n) { return off >= 0 && off + n <= d->meta_len; };
   if (!in_meta(d->slot_mapping_off, d->num_tokens) || !in_meta(d->query_start_off, d->num_segments) ||

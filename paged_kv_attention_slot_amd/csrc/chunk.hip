@@ -24,6 +24,7 @@
 //   * the causal mask is applied per element only on tiles that reach past a
 //     wavefront's first row; rows of a segment never see past their position.
 #include <cfloat>
+#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -42,12 +43,37 @@ __device__ __forceinline__ shortx4_t lds_read_tr16(const unsigned char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_t *)(p));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// IEEE-754 maximum (NaN-propagating): lowers to v_maximum3_f32 / v_maximum_f32
+// with no canonicalisation of matrix-core results, unlike fmaxf.
+__device__ __forceinline__ float vmaxf(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+template <int N>
+__device__ __forceinline__ float max_of(const float (&v)[N]) {
+  float m = vmaxf(v[0], v[1]);
+#pragma unroll
+  for (int i = 2; i + 1 < N; i += 2) m = vmaxf(m, vmaxf(v[i], v[i + 1]));
+  if constexpr (N % 2 == 1) m = vmaxf(m, v[N - 1]);
+  return m;
+}
+
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups) with the
+// lane-swap instructions: each swap leaves x[l] and x[l ^ 32] (then
+// x[l ^ 16]) in the two returned registers of every lane.
+__device__ __forceinline__ float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;                 // two 16-row MFMA column tiles
 constexpr int kMTile = kWaves * kRowsPerWave;    // M-rows per workgroup
 constexpr int kKV = 64;                          // tokens per K/V tile
 constexpr int kPad = 32;                         // LDS row padding (bytes)
-constexpr int kTableWindow = 2048;               // block-table entries staged per pass
+constexpr int kTableWindow = PKV_CHUNK_TABLE_WINDOW;   // block-table entries staged per pass
 
 template <int D>
 struct ChunkGeo {
@@ -96,10 +122,12 @@ struct Ring;
 template <>
 struct Ring<64> {
   static constexpr int kTok = PKV_CHUNK_RING_TOK_D64, kStages = PKV_CHUNK_RING_STAGES_D64;
+  static constexpr int kMinBlocks = PKV_CHUNK_MIN_BLOCKS_D64;
 };
 template <>
 struct Ring<128> {
   static constexpr int kTok = PKV_CHUNK_RING_TOK_D128, kStages = PKV_CHUNK_RING_STAGES_D128;
+  static constexpr int kMinBlocks = PKV_CHUNK_MIN_BLOCKS_D128;
 };
 
 // Position of 16-byte chunk c of token row t within the row, so that both the
@@ -116,7 +144,7 @@ __device__ __forceinline__ unsigned lds_addr32(const unsigned char *p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void chunk_kernel(AttendArgs a, int G) {
+__global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendArgs a, int G) {
   using C = ChunkGeo<D>;
   constexpr int T = Ring<D>::kTok;            // tokens per ring stage
   constexpr int S = Ring<D>::kStages;
@@ -136,13 +164,14 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(AttendArgs a, int G) {
 
   auto units_fn = [&](int b) { return chunk_units(a, b, G); };
   const int hkv = a.num_kv_heads;
-  const int total = count_units(a.num_segments, units_fn);
+  const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
   if (static_cast<int64_t>(blockIdx.x) >= static_cast<int64_t>(total) * hkv) return;
   const int unit = blockIdx.x / hkv;
   const int g = blockIdx.x - unit * hkv;
   int u;
-  const int b = find_unit(a.num_segments, unit, units_fn, &u);
-  const SegInfo si = seg_info(a, b);
+  const int b = __builtin_amdgcn_readfirstlane(find_unit(a.num_segments, unit, units_fn, &u));
+  u = __builtin_amdgcn_readfirstlane(u);
+  const SegInfo si = seg_info_uniform(a, b);
   if (!si.ok) return;
   const int n = si.n, L = si.L;
   const int mtot = n * G;
@@ -192,19 +221,29 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(AttendArgs a, int G) {
 
   // Direct-to-LDS staging.  Thread tid fills 16-byte chunks q = x * 256 + tid
   // of each K and V stage: token row t = q / kCPR, position p = q % kCPR,
-  // taking chunk ring_swz(t, p) of that row.  Tokens past the sequence read
-  // the last token (finite data; their scores are masked and their weights
-  // are exactly zero).
+  // taking chunk ring_swz(t, p) of that row.  One wavefront's 64 chunks of a
+  // step x are kRowsW consecutive token rows (8 for D = 64, 4 for D = 128)
+  // inside a single pool block, so the block lookup and the 64-bit base are
+  // wave-uniform (scalar registers) and each lane adds a fixed 32-bit offset.
+  // Tokens past the sequence read the last token (finite data; their scores
+  // are masked and their weights are exactly zero).
+  constexpr int kRowsX = kWaves * kWave / kCPR;     // token rows per step x
+  constexpr int kRowsW = kWave / kCPR;              // of which one wavefront's
+  constexpr int kBlockBytes = kBlockTokens * kRowBytes;
+  static_assert(kBlockTokens % kRowsW == 0 && T % kBlockTokens == 0, "a wavefront's rows stay inside one block");
   const int32_t *bt = a.block_tables + static_cast<int64_t>(si.slot) * a.max_blocks;
   const char *kbase = static_cast<const char *>(a.k);
   const char *vbase = static_cast<const char *>(a.v);
-  int row_of[kPer], col_off[kPer];
+  const int lane_row = lane / kCPR;
+  unsigned voff[kPer], col_off[kPer];
 #pragma unroll
   for (int x = 0; x < kPer; ++x) {
-    const int q = x * (kWaves * kWave) + tid;
-    row_of[x] = q / kCPR;
-    col_off[x] = ring_swz<D>(row_of[x], q - row_of[x] * kCPR) * 16;
+    const int t = x * kRowsX + wave * kRowsW + lane_row;          // row within the stage
+    col_off[x] = static_cast<unsigned>(ring_swz<D>(t, lane - lane_row * kCPR) * 16);
+    voff[x] = static_cast<unsigned>((t % kBlockTokens) * kRowBytes) + col_off[x];
   }
+  const int64_t head_off = static_cast<int64_t>(g) * kBlockBytes;
+  const int64_t blk_stride = static_cast<int64_t>(hkv) * kBlockBytes;
   // The tile loads are inline assembly (M0 takes the LDS destination; nothing
   // else here uses M0): the compiler does not wait on them, the explicit
   // vmcnt waits below do.  The block-table entries they need come from a
@@ -214,90 +253,81 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(AttendArgs a, int G) {
   auto issue = [&](int stage, int rt) {
     unsigned char *kd = lds + stage * 2 * kStageBytes;
     unsigned char *vd = kd + kStageBytes;
+    const bool tail = rt * T + T > L;                // uniform
 #pragma unroll
     for (int x = 0; x < kPer; ++x) {
-      const int tok = min(rt * T + row_of[x], L - 1);
-      const int phys = bt_lds[tok / kBlockTokens - blk0];
-      const int64_t off = ((static_cast<int64_t>(phys) * hkv + g) * kBlockTokens + (tok % kBlockTokens)) * kRowBytes +
-                          col_off[x];
+      const int tok0 = rt * T + x * kRowsX + wave * kRowsW;       // wavefront's first row
+      const int tcl = min(tok0, L - 1);
+      const int blk = tcl / kBlockTokens;
+      const int phys = __builtin_amdgcn_readfirstlane(bt_lds[blk - blk0]);
+      const int64_t boff = phys * blk_stride + head_off;
+      unsigned off = voff[x];
+      if (tail)
+        off = static_cast<unsigned>((min(tok0 + lane_row, L - 1) - blk * kBlockTokens) * kRowBytes) + col_off[x];
       const unsigned dst = lds_addr32(kd) + (x * (kWaves * kWave) + wave * kWave) * 16;
       const unsigned dstv = lds_addr32(vd) + (x * (kWaves * kWave) + wave * kWave) * 16;
-      const void *gk = kbase + off;
-      const void *gv = vbase + off;
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off " PKV_LDS_DMA_HINT ::"s"(dst), "v"(gk)
+      const char *gk = kbase + boff;
+      const char *gv = vbase + boff;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 " PKV_CHUNK_DMA_HINT ::"s"(dst), "v"(off),
+                   "s"(gk)
                    : "memory");
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off " PKV_LDS_DMA_HINT ::"s"(dstv), "v"(gv)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 " PKV_CHUNK_DMA_HINT ::"s"(dstv), "v"(off),
+                   "s"(gv)
                    : "memory");
     }
   };
   const int last_blk = (L - 1) / kBlockTokens;
   constexpr int kPassTiles = kTableWindow * kBlockTokens / T;
+  static_assert(S >= 3, "V of tile t and K of tile t + 1 are resident together");
 
-  for (int pass0 = rt_begin; pass0 < rt_end; pass0 += kPassTiles) {
-  const int pass1 = min(rt_end, pass0 + kPassTiles);
-  blk0 = pass0 * T / kBlockTokens;
-  const int nblk = min((pass1 * T - 1) / kBlockTokens, last_blk) - blk0 + 1;
-  __syncthreads();             // the previous pass is done with bt_lds
-  for (int i = tid; i < nblk; i += kWaves * kWave) bt_lds[i] = min(max(bt[blk0 + i], 0), a.num_blocks - 1);
-  __syncthreads();
-  // Q, the metadata and the table slice have landed before any tile load
-  // (vmcnt(0); expcnt and lgkmcnt left at their maxima).
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-
-#pragma unroll
-  for (int i = 0; i < S - 1; ++i) issue(i, min(pass0 + i, pass1 - 1));
-  for (int rt = pass0; rt < pass1; ++rt) {
-    const int stage = (rt - pass0) % S;
-    // this wave's loads of tile rt have landed once at most S - 2 newer
-    // tiles' loads are outstanding; the barrier makes everyone's visible and
-    // retires every read of the stage refilled below
-    if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer) : "memory");
-    if constexpr (S == 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kPer) : "memory");
-    __syncthreads();
-    issue((rt - pass0 + S - 1) % S, min(rt + S - 1, pass1 - 1));
-    const unsigned char *kl = lds + stage * 2 * kStageBytes;
-    const unsigned char *vl = kl + kStageBytes;
-
-    // S^T tiles: kTT token tiles x 2 row tiles.
-    floatx4_t s[kTT][2];
+  // S^T = K Q^T for the tile in stage st: kTT token tiles x 2 row tiles.
+  // Lane holds keys tt*16 + 4*lg + e of the tile for its M-rows (qt, l16).
+  auto qk = [&](int st, floatx4_t(&sc)[kTT][2]) {
+    const unsigned char *kl = lds + st * 2 * kStageBytes;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      s[tt][0] = s[tt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      sc[tt][0] = sc[tt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
       const int kr = tt * 16 + l16;
 #pragma unroll
       for (int kk = 0; kk < C::kKSteps; ++kk) {
         const bf16x8_t ka =
             *reinterpret_cast<const bf16x8_t *>(kl + kr * kRowBytes + ring_swz<D>(kr, kk * 4 + lg) * 16);
-        s[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[0][kk], s[tt][0], 0, 0, 0);
-        s[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[1][kk], s[tt][1], 0, 0, 0);
+        sc[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[0][kk], sc[tt][0], 0, 0, 0);
+        sc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[1][kk], sc[tt][1], 0, 0, 0);
       }
     }
-    // Lane holds keys rt*T + tt*16 + 4*lg + e of its M-rows (qt, l16).
-    const bool need_mask = rt * T + T - 1 > wave_pos0;
-    if (need_mask) {
+  };
+  // Causal mask of tile rt; only tiles reaching past the wave's first row.
+  auto mask = [&](int rt, floatx4_t(&sc)[kTT][2]) {
+    if (rt * T + T - 1 > wave_pos0) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (rt * T + tt * 16 + lg * 4 + e > pos[qt]) s[tt][qt][e] = -INFINITY;
+            if (rt * T + tt * 16 + lg * 4 + e > pos[qt]) sc[tt][qt][e] = -INFINITY;
     }
-    float mnew[2];
+  };
+  // Row max of a tile (log2 units): the candidate new running max, and
+  // whether it exceeds the current one by more than the allowed slack.
+  auto rowmax = [&](const floatx4_t(&sc)[kTT][2], float(&mnew)[2]) {
     bool raise = false;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float mx = s[0][qt][0];
+      float v[4 * kTT];
 #pragma unroll
       for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[tt][qt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mnew[qt] = fmaxf(m_run[qt], mx * c_log2);
-      raise |= mnew[qt] > m_run[qt];
+        for (int e = 0; e < 4; ++e) v[tt * 4 + e] = sc[tt][qt][e];
+      const float mx = group4_max(max_of<4 * kTT>(v)) * c_log2;
+      mnew[qt] = vmaxf(m_run[qt], mx);
+      raise |= mx > m_run[qt] + PKV_CHUNK_RESCALE_SLACK;
     }
+    return raise;
+  };
+  // Move O and l to the new running max when any row of the wave asked.
+  auto rescale = [&](const float(&mnew)[2], bool raise) {
     if (__ballot(raise) != 0) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
@@ -308,27 +338,62 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(AttendArgs a, int G) {
         for (int dt = 0; dt < C::kDTiles; ++dt) o[dt][qt] *= alpha;
       }
     }
-    // P^T as the B operand of O^T += V^T P^T, one per 32-key step.
-    bf16x8_t pb[kKS][2];
+  };
+  // Phase A of an iteration: the matrix cores form the scores of the next
+  // tile (S^T = K Q^T from stage st_next) while the vector ALU turns the
+  // current tile's scores into bf16 weights and row sums.  The two streams
+  // are interleaved by hand, one matrix-core pair per step, each step fenced
+  // so that the scheduler keeps them side by side.
+  auto phase_a = [&](const floatx4_t(&cur)[kTT][2], int st_next, floatx4_t(&nxt)[kTT][2], bf16x8_t(&pb)[kKS][2]) {
+    const unsigned char *kl = lds + st_next * 2 * kStageBytes;
+    bf16x8_t ka[kTT][C::kKSteps];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(fmaf(s[2 * ks][qt][e], c_log2, -m_run[qt]));
-          p[4 + e] = fast_exp2(fmaf(s[2 * ks + 1][qt][e], c_log2, -m_run[qt]));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) l_run[qt] += p[e];
-        pb[ks][qt] = bf16x8_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
-                              static_cast<__bf16>(p[3]), static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
-                              static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
+      for (int kk = 0; kk < C::kKSteps; ++kk) {
+        const int kr = tt * 16 + l16;
+        ka[tt][kk] = *reinterpret_cast<const bf16x8_t *>(kl + kr * kRowBytes + ring_swz<D>(kr, kk * 4 + lg) * 16);
       }
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) nxt[tt][0] = nxt[tt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    constexpr int kPairs = kTT * C::kKSteps;
+    constexpr int kScores = 2 * kKS * 8;
+    float p[2][kKS][8];
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int tt = i / C::kKSteps, kk = i % C::kKSteps;
+      nxt[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][kk], qv[0][kk], nxt[tt][0], 0, 0, 0);
+      nxt[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][kk], qv[1][kk], nxt[tt][1], 0, 0, 0);
+#pragma unroll
+      for (int w = i * kScores / kPairs; w < (i + 1) * kScores / kPairs; ++w) {
+        const int qt = w / (kKS * 8), ks = (w / 8) % kKS, e8 = w % 8;
+        p[qt][ks][e8] = fast_exp2(fmaf(cur[2 * ks + e8 / 4][qt][e8 % 4], c_log2, -m_run[qt]));
+        if (e8 == 7) {
+          const float *q8 = p[qt][ks];
+          pb[ks][qt] = bf16x8_t{static_cast<__bf16>(q8[0]), static_cast<__bf16>(q8[1]), static_cast<__bf16>(q8[2]),
+                                static_cast<__bf16>(q8[3]), static_cast<__bf16>(q8[4]), static_cast<__bf16>(q8[5]),
+                                static_cast<__bf16>(q8[6]), static_cast<__bf16>(q8[7])};
+          float l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 0, 1), ones,
+                                                     l_run[qt], false);
+          float l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 2, 3), ones,
+                                                     0.f, false);
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 4, 5), ones, l0,
+                                               false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 6, 7), ones, l1,
+                                               false);
+          l_run[qt] = l0 + l1;
+        }
+      }
+      if constexpr (PKV_CHUNK_INTERLEAVE) __builtin_amdgcn_sched_barrier(0);
     }
-    // V^T operand: keys 4*lg .. 4*lg+3 and 16 + 4*lg .. of each 32-key step,
-    // dimension dt*16 + l16, read transposed from the swizzled tile.
+  };
+  // Phase B: O^T += V^T P^T of the current tile (stage st) on the matrix
+  // cores while the vector ALU takes the row max of the next tile.  Returns
+  // the rescale vote, as rowmax.
+  auto phase_b = [&](int st, const bf16x8_t(&pb)[kKS][2], const floatx4_t(&nxt)[kTT][2], float(&mnew)[2]) {
+    const unsigned char *vl = lds + st * 2 * kStageBytes + kStageBytes;
+    bf16x8_t va[C::kDTiles][kKS];
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) {
       const int dd = dt * 16 + 4 * (l16 & 3);
@@ -338,14 +403,109 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(AttendArgs a, int G) {
         const int r2 = r1 + 16;
         const shortx4_t v1 = lds_read_tr16(vl + r1 * kRowBytes + ring_swz<D>(r1, dd >> 3) * 16 + (dd & 7) * 2);
         const shortx4_t v2 = lds_read_tr16(vl + r2 * kRowBytes + ring_swz<D>(r2, dd >> 3) * 16 + (dd & 7) * 2);
-        const shortx8_t rr = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, rr);
-        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ks][0], o[dt][0], 0, 0, 0);
-        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ks][1], o[dt][1], 0, 0, 0);
+        va[dt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain before the ring is reused
+    constexpr int kPairs = C::kDTiles * kKS;
+    constexpr int kItems = 2 * kTT;
+    float acc[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int dt = i / kKS, ks = i % kKS;
+      o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][0], o[dt][0], 0, 0, 0);
+      o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][1], o[dt][1], 0, 0, 0);
+#pragma unroll
+      for (int w = i * kItems / kPairs; w < (i + 1) * kItems / kPairs; ++w) {
+        const int qt = w / kTT, tt = w % kTT;
+        const floatx4_t &x = nxt[tt][qt];
+        acc[qt] = vmaxf(acc[qt], vmaxf(vmaxf(x[0], x[1]), vmaxf(x[2], x[3])));
+      }
+      if constexpr (PKV_CHUNK_INTERLEAVE) __builtin_amdgcn_sched_barrier(0);
+    }
+    bool raise = false;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float mx = group4_max(acc[qt]) * c_log2;
+      mnew[qt] = vmaxf(m_run[qt], mx);
+      raise |= mx > m_run[qt] + PKV_CHUNK_RESCALE_SLACK;
+    }
+    return raise;
+  };
+
+  for (int pass0 = rt_begin; pass0 < rt_end; pass0 += kPassTiles) {
+    const int pass1 = min(rt_end, pass0 + kPassTiles);
+    blk0 = pass0 * T / kBlockTokens;
+    const int nblk = min((pass1 * T - 1) / kBlockTokens, last_blk) - blk0 + 1;
+    __syncthreads();             // the previous pass is done with bt_lds
+    for (int i = tid; i < nblk; i += kWaves * kWave) bt_lds[i] = min(max(bt[blk0 + i], 0), a.num_blocks - 1);
+    __syncthreads();
+    // Q, the metadata and the table slice have landed before any tile load
+    // (vmcnt(0); expcnt and lgkmcnt left at their maxima).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // Tile t of the pass sits in stage (t - pass0) % S.  Every iteration
+    // issues exactly one tile's loads (the last ones repeat the final tile),
+    // so "tile t has landed" is "at most k newer tiles are outstanding".
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) issue(i, min(pass0 + i, pass1 - 1));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 2)) : "memory");
+    __syncthreads();
+    floatx4_t s0[kTT][2], s1[kTT][2];
+    float mnew[2];
+    qk(0, s0);
+    mask(pass0, s0);
+    bool raise = rowmax(s0, mnew);
+
+    // One iteration: tile rt's scores are in `cur`, tile rt + 1's go to `nxt`.
+    auto iter = [&](int rt, floatx4_t(&cur)[kTT][2], floatx4_t(&nxt)[kTT][2], auto masked_next) {
+      const int st = (rt - pass0) % S;
+      const int st_next = (rt + 1 - pass0) % S;
+      // Tile rt + 1 has landed (at most S - 3 newer tiles outstanding); past
+      // the barrier every wave is done with tile rt - 1, whose stage refills.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 3)) : "memory");
+      __syncthreads();
+      issue((rt - pass0 + S - 1) % S, min(rt + S - 1, pass1 - 1));
+      rescale(mnew, raise);
+      // Phase A: the weights of tile rt on the vector ALU while the matrix
+      // cores form the scores of tile rt + 1 (of a repeat of tile rt on the
+      // last iteration: computed, never used).
+      bf16x8_t pb[kKS][2];
+      phase_a(cur, st_next, nxt, pb);
+      if constexpr (decltype(masked_next)::value) mask(rt + 1, nxt);
+      // Phase B: O += V P of tile rt on the matrix cores while the vector
+      // ALU takes the row max of tile rt + 1.
+      raise = phase_b(st, pb, nxt, mnew) && rt + 1 < pass1;
+    };
+    // Tiles before `unmasked_end` need no causal mask for any row of this
+    // wave.  Iterations whose next tile is among them run branch-free, two at
+    // a time so the score buffers swap roles; the rest mask the next tile.
+    // Trip counts differ between waves, but every iteration has one barrier
+    // and every wave runs pass1 - pass0 of them.
+    const int unmasked_end = wave_pos0 >= 0 ? (wave_pos0 + 1) / T : 0;
+    const int split_at = max(pass0, min(pass1, unmasked_end - 1));
+    int rt = pass0;
+    for (; rt + 1 < split_at; rt += 2) {
+      iter(rt, s0, s1, std::false_type{});
+      iter(rt + 1, s1, s0, std::false_type{});
+    }
+    if (rt < split_at) {
+      iter(rt, s0, s1, std::false_type{});
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) {
+        s0[tt][0] = s1[tt][0];
+        s0[tt][1] = s1[tt][1];
+      }
+      ++rt;
+    }
+    for (; rt < pass1; ++rt) {
+      iter(rt, s0, s1, std::true_type{});
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) {
+        s0[tt][0] = s1[tt][0];
+        s0[tt][1] = s1[tt][1];
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain before the ring is reused
   }
 
   // Row sums live spread over the 4 lane groups; combine, normalise, store
@@ -385,54 +545,84 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(AttendArgs a, int G) {
 
 // Merge the key-range partials of split segments: for M-row m (query row
 // i = m / G, head g * G + m % G), ranges 0 .. min(splits - 1, pos / (tps*64))
-// hold keys it sees; combine them in range order.  One wavefront per row.
+// hold keys it sees; combine them in range order.  A unit is 4 consecutive
+// M-rows of one split segment and is one wavefront: a 16-lane group per
+// M-row, each lane owning D / 16 output dimensions.
+constexpr int kMergeRowsPerWave = 4;
+constexpr int kMergeWaves = 4;
+
+__device__ __forceinline__ int merge_units(const AttendArgs &a, int b, int G) {
+  const SegInfo s = seg_info(a, b);
+  if (!s.ok || s.n < 2) return 0;
+  const ChunkShape c = chunk_shape(s.n, s.L, G);
+  return c.splits > 1 ? (s.n * G + kMergeRowsPerWave - 1) / kMergeRowsPerWave : 0;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void chunk_merge_kernel(AttendArgs a, int G, int rows_per_block) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kMergeWaves * kWave) void chunk_merge_kernel(AttendArgs a, int G) {
+  constexpr int DPL = D / 16;                         // dimensions per lane
+  constexpr int SF = kChunkSlotFloats<D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15;
   const int hkv = a.num_kv_heads;
-  (void)rows_per_block;
-  // blockIdx.x = (b * hkv + g) * row_blocks + rb
-  const int row_blocks = gridDim.x / (a.num_segments * hkv);
-  const int bg = blockIdx.x / row_blocks;
-  const int rb = blockIdx.x - bg * row_blocks;
-  const int b = bg / hkv;
-  const int g = bg - b * hkv;
-  const SegInfo si = seg_info(a, b);
-  if (!si.ok || si.n < 2) return;
+  const int wg = blockIdx.x / hkv;
+  const int g = blockIdx.x - wg * hkv;                // same head-to-workgroup order as the chunk kernel
+  auto units_fn = [&](int b) { return merge_units(a, b, G); };
+  const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
+  const int unit = wg * kMergeWaves + wave;
+  if (unit >= total) return;
+  int u;
+  const int b = __builtin_amdgcn_readfirstlane(find_unit(a.num_segments, unit, units_fn, &u));
+  u = __builtin_amdgcn_readfirstlane(u);
+  const SegInfo si = seg_info_uniform(a, b);
+  if (!si.ok) return;
   const ChunkShape cs = chunk_shape(si.n, si.L, G);
-  if (cs.splits <= 1 || a.chunk_part == nullptr) return;
-  const int mtot = si.n * G;
-  constexpr int DPL = D / kWave;
-  for (int m = rb * 4 + wave; m < mtot; m += row_blocks * 4) {
-    const int i = m / G;
-    const int h = m - i * G;
-    const int pos = si.L - si.n + i;
-    const int last = min(cs.splits - 1, pos / (cs.tps * kKV));
-    const int64_t base = ((static_cast<int64_t>(b) * hkv + g) * kChunkSplitSlots + static_cast<int64_t>(m) * cs.splits);
-    float mx = -FLT_MAX;
-    for (int sp = 0; sp <= last; ++sp) mx = fmaxf(mx, a.chunk_part[(base + sp) * kChunkSlotFloats<D> + D]);
-    float lsum = 0.f;
-    float o[DPL];
+  const int m = u * kMergeRowsPerWave + (lane >> 4);
+  if (m >= si.n * G) return;                          // no cross-group exchange below
+  const int i = m / G;
+  const int h = m - i * G;
+  const int pos = si.L - si.n + i;
+  const int last = min(cs.splits - 1, pos / (cs.tps * kKV));
+  const float *pp = a.chunk_part + ((static_cast<int64_t>(b) * hkv + g) * kChunkSplitSlots +
+                                    static_cast<int64_t>(m) * cs.splits) * SF;
+  // Row max over the ranges: lane li reads ranges li, li + 16, ...
+  float mx = -FLT_MAX;
+  for (int sp = li; sp <= last; sp += 16) mx = fmaxf(mx, pp[sp * SF + D]);
+  mx = group16_max(mx);
+  float o[DPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] = 0.f;
-    for (int sp = 0; sp <= last; ++sp) {
-      const float *pp = a.chunk_part + (base + sp) * kChunkSlotFloats<D>;
-      const float w = fast_exp2(pp[D] - mx);
-      lsum += w * pp[D + 1];
+  for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+  float lsum = 0.f;
+#pragma unroll 4
+  for (int sp = 0; sp <= last; ++sp) {
+    const float *q = pp + sp * SF;
+    const float2 ml = *reinterpret_cast<const float2 *>(q + D);
+    const float w = fast_exp2(ml.x - mx);
+    lsum = fmaf(w, ml.y, lsum);
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] = fmaf(w, pp[lane + k * kWave], o[k]);
+    for (int k = 0; k < DPL; k += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(q + li * DPL + k);
+      o[k] = fmaf(w, v.x, o[k]);
+      o[k + 1] = fmaf(w, v.y, o[k + 1]);
+      o[k + 2] = fmaf(w, v.z, o[k + 2]);
+      o[k + 3] = fmaf(w, v.w, o[k + 3]);
     }
-    const float inv = 1.f / lsum;
-    const int64_t ob = (static_cast<int64_t>(si.row0 + i) * a.num_q_heads + g * G + h) * D;
+  }
+  const float inv = 1.f / lsum;
+  const int64_t ob = (static_cast<int64_t>(si.row0 + i) * a.num_q_heads + g * G + h) * D + li * DPL;
+  if (a.out_bf16) {
+    uint32_t w[DPL / 2];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      const float val = o[k] * inv;
-      if (a.out_bf16)
-        static_cast<uint16_t *>(a.out)[ob + lane + k * kWave] = static_cast<uint16_t>(f32_to_bf16_rne(val));
-      else
-        static_cast<float *>(a.out)[ob + lane + k * kWave] = val;
-    }
+    for (int k = 0; k < DPL; k += 2) w[k / 2] = f32_to_bf16_rne(o[k] * inv) | (f32_to_bf16_rne(o[k + 1] * inv) << 16);
+    uint16_t *op = static_cast<uint16_t *>(a.out) + ob;
+    if constexpr (DPL == 8) *reinterpret_cast<uint4 *>(op) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint2 *>(op) = make_uint2(w[0], w[1]);
+  } else {
+    float *op = static_cast<float *>(a.out) + ob;
+#pragma unroll
+    for (int k = 0; k < DPL; k += 4)
+      *reinterpret_cast<float4 *>(op + k) = make_float4(o[k] * inv, o[k + 1] * inv, o[k + 2] * inv, o[k + 3] * inv);
   }
 }
 
@@ -461,16 +651,16 @@ int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, i
     chunk_kernel<64><<<grid, block, 0, stream>>>(a, G);
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   if (a.chunk_part == nullptr) return PKV_OK;
-  // Merge: split segments have at most kChunkSplitRowTiles * 128 / G rows x G heads.
-  const int rows_cap = max_query_len * G;
-  const int row_blocks = static_cast<int>((static_cast<int64_t>(min(rows_cap, kChunkSplitRowTiles * kMTile)) + 3) / 4);
-  const int64_t mgrid = static_cast<int64_t>(a.num_segments) * a.num_kv_heads * row_blocks;
+  // Merge: at most total_q * G M-rows in split segments, padded to whole
+  // units per segment.
+  const int64_t units = (static_cast<int64_t>(a.total_q) * G) / kMergeRowsPerWave + a.num_segments;
+  const int64_t mgrid = (units + kMergeWaves - 1) / kMergeWaves * a.num_kv_heads;
   if (mgrid <= 0) return PKV_OK;
   if (mgrid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   if (head_dim == 128)
-    chunk_merge_kernel<128><<<dim3(static_cast<unsigned>(mgrid)), dim3(256), 0, stream>>>(a, G, 4);
+    chunk_merge_kernel<128><<<dim3(static_cast<unsigned>(mgrid)), dim3(kMergeWaves * kWave), 0, stream>>>(a, G);
   else
-    chunk_merge_kernel<64><<<dim3(static_cast<unsigned>(mgrid)), dim3(256), 0, stream>>>(a, G, 4);
+    chunk_merge_kernel<64><<<dim3(static_cast<unsigned>(mgrid)), dim3(kMergeWaves * kWave), 0, stream>>>(a, G);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

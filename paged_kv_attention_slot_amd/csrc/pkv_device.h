@@ -57,6 +57,14 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Max over aligned groups of 16 consecutive lanes; every lane gets its group's.
+__device__ __forceinline__ float group16_max(float v) {
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_mov<kDppMirror>(v));
+}
+
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);  // works for any wave of a multi-wave block
 #pragma unroll
@@ -101,6 +109,19 @@ __device__ __forceinline__ SegInfo seg_info(const AttendArgs &a, int b) {
   s.n = n;
   s.row0 = r0;
   s.ok = true;
+  return s;
+}
+
+// The same for a wave-uniform b, with the fields moved to scalar registers so
+// that loop bounds and block lookups derived from them stay scalar.
+__device__ __forceinline__ SegInfo seg_info_uniform(const AttendArgs &a, int b) {
+  const SegInfo v = seg_info(a, __builtin_amdgcn_readfirstlane(b));
+  SegInfo s;
+  s.slot = __builtin_amdgcn_readfirstlane(v.slot);
+  s.L = __builtin_amdgcn_readfirstlane(v.L);
+  s.n = __builtin_amdgcn_readfirstlane(v.n);
+  s.row0 = __builtin_amdgcn_readfirstlane(v.row0);
+  s.ok = __builtin_amdgcn_readfirstlane(static_cast<int>(v.ok)) != 0;
   return s;
 }
 

@@ -44,12 +44,35 @@ constexpr int kDecodeMfmaMinWaves = PKV_DECODE_MFMA_MIN_WAVES;
 #else
 #define PKV_LDS_DMA_HINT ""
 #endif
+// Chunk K/V tiles are read again by every row tile of their segment (hits
+// in L2), so by default they are loaded without the streaming hint.
+#ifndef PKV_CHUNK_STREAM_LOADS
+#define PKV_CHUNK_STREAM_LOADS 0
+#endif
+#if PKV_CHUNK_STREAM_LOADS
+#define PKV_CHUNK_DMA_HINT "nt"
+#else
+#define PKV_CHUNK_DMA_HINT ""
+#endif
+// Fence the chunk kernel's hand-interleaved matrix-core / vector-ALU steps
+// so that the scheduler keeps them side by side.
+#ifndef PKV_CHUNK_INTERLEAVE
+#define PKV_CHUNK_INTERLEAVE 1
+#endif
+// The chunk kernel's running row max may lag the true max by up to this much
+// (log2 units) before O and l are rescaled: weights stay below 2^slack.
+#ifndef PKV_CHUNK_RESCALE_SLACK
+#define PKV_CHUNK_RESCALE_SLACK 8.0f
+#endif
 constexpr int kDecodeStages = PKV_DECODE_STAGES;
 
 // Multi-row segments with fewer than this many 128-row tiles split their
 // key range so that (row tiles x splits) reaches it; partial slots per
 // (segment, KV head) = kChunkSplitRowTiles * 128.
-constexpr int kChunkSplitRowTiles = 32;
+#ifndef PKV_CHUNK_SPLIT_ROW_TILES
+#define PKV_CHUNK_SPLIT_ROW_TILES 32
+#endif
+constexpr int kChunkSplitRowTiles = PKV_CHUNK_SPLIT_ROW_TILES;
 constexpr int kChunkSplitSlots = kChunkSplitRowTiles * 128;
 
 // Chunk kernel LDS ring: tokens per stage and stages, per head_dim.
@@ -57,7 +80,16 @@ constexpr int kChunkSplitSlots = kChunkSplitRowTiles * 128;
 #define PKV_CHUNK_RING_TOK_D64 64
 #endif
 #ifndef PKV_CHUNK_RING_STAGES_D64
-#define PKV_CHUNK_RING_STAGES_D64 3
+#define PKV_CHUNK_RING_STAGES_D64 4
+#endif
+#ifndef PKV_CHUNK_MIN_BLOCKS_D64
+#define PKV_CHUNK_MIN_BLOCKS_D64 2
+#endif
+#ifndef PKV_CHUNK_MIN_BLOCKS_D128
+#define PKV_CHUNK_MIN_BLOCKS_D128 2
+#endif
+#ifndef PKV_CHUNK_TABLE_WINDOW
+#define PKV_CHUNK_TABLE_WINDOW 512
 #endif
 #ifndef PKV_CHUNK_RING_TOK_D128
 #define PKV_CHUNK_RING_TOK_D128 32

@@ -48,6 +48,18 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
     d5 = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, 0)
     assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1, 1, 1, ctypes.byref(d5), 1.0, 16, 1,
                                 None, 0, None) == pk.binding.PKV_ERR_INVALID_ARG
+    # the softmax scale must be finite and positive
+    for bad in (0.0, -0.125, float("inf"), float("nan")):
+        assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1, 1, 1, ctypes.byref(d4), bad, 16, 0,
+                                    None, 0, None) == pk.binding.PKV_ERR_INVALID_ARG
+        step = pk.binding.StepDesc()
+        meta = (ctypes.c_int32 * 8)()
+        step.host_meta = ctypes.cast(meta, ctypes.c_void_p)
+        step.dev_meta = 16
+        step.meta_len = 8
+        step.num_slots = 1
+        step.scale = bad
+        assert lib.pkv_mixed_step(ctypes.byref(step), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
     # decode rows with a long context need workspace; none given
     assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1000, 1, 5000, ctypes.byref(d4), 1.0, 16, 0,
                                 None, 0, None) == pk.binding.PKV_ERR_WORKSPACE

@@ -57,7 +57,7 @@ WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t 
   if (max_query_len > 1 && !multirow && group > 0) {
     // key-range partials of split multi-row segments (see chunk.hip)
     const int64_t kv_heads = num_q_heads / group;
-    w.chunk_bytes = static_cast<size_t>(num_segments) * kv_heads * kChunkSplitSlots * (head_dim + 4) * sizeof(float);
+    w.chunk_bytes = static_cast<size_t>(num_segments) * kv_heads * chunk_split_slots(head_dim) * (head_dim + 4) * sizeof(float);
   }
   return w;
 }

@@ -97,21 +97,24 @@ struct ChunkShape {
   int tps;         // 64-token K/V tiles per range
 };
 
+template <int D>
 __device__ __forceinline__ ChunkShape chunk_shape(int n, int L, int G) {
   ChunkShape c;
   c.mtiles = (n * G + kMTile - 1) / kMTile;
   const int kv_tiles = (L + kKV - 1) / kKV;
-  int splits = c.mtiles >= kChunkSplitRowTiles ? 1 : kChunkSplitRowTiles / c.mtiles;
+  constexpr int kRT = chunk_split_row_tiles(D);
+  int splits = c.mtiles >= kRT ? 1 : kRT / c.mtiles;
   splits = max(1, min(splits, (kv_tiles + 1) / 2));   // at least two K/V tiles per range
   c.tps = (kv_tiles + splits - 1) / splits;
   c.splits = (kv_tiles + c.tps - 1) / c.tps;
   return c;
 }
 
+template <int D>
 __device__ __forceinline__ int chunk_units(const AttendArgs &a, int b, int G) {
   const SegInfo s = seg_info(a, b);
   if (!s.ok || s.n < 2) return 0;
-  const ChunkShape c = chunk_shape(s.n, s.L, G);
+  const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.mtiles * c.splits;
 }
 
@@ -123,11 +126,13 @@ template <>
 struct Ring<64> {
   static constexpr int kTok = PKV_CHUNK_RING_TOK_D64, kStages = PKV_CHUNK_RING_STAGES_D64;
   static constexpr int kMinBlocks = PKV_CHUNK_MIN_BLOCKS_D64;
+  static constexpr bool kEarlyV = PKV_CHUNK_EARLY_V_D64;
 };
 template <>
 struct Ring<128> {
   static constexpr int kTok = PKV_CHUNK_RING_TOK_D128, kStages = PKV_CHUNK_RING_STAGES_D128;
   static constexpr int kMinBlocks = PKV_CHUNK_MIN_BLOCKS_D128;
+  static constexpr bool kEarlyV = PKV_CHUNK_EARLY_V_D128;
 };
 
 // Position of 16-byte chunk c of token row t within the row, so that both the
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
-  auto units_fn = [&](int b) { return chunk_units(a, b, G); };
+  auto units_fn = [&](int b) { return chunk_units<D>(a, b, G); };
   const int hkv = a.num_kv_heads;
   const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
   if (static_cast<int64_t>(blockIdx.x) >= static_cast<int64_t>(total) * hkv) return;
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
   if (!si.ok) return;
   const int n = si.n, L = si.L;
   const int mtot = n * G;
-  const ChunkShape cs = chunk_shape(n, L, G);
+  const ChunkShape cs = chunk_shape<D>(n, L, G);
   const int mt = cs.mtiles - 1 - u / cs.splits;      // heaviest (latest) rows first
   const int split = u - (cs.mtiles - 1 - mt) * cs.splits;
   const int m0 = mt * kMTile;
@@ -190,7 +195,10 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
   // first position among this wave's rows (rows past the segment see nothing)
   const int wave_pos0 = mw < mtot ? L - n + mw / G : -1;
 
-  // Q operands (B of S^T = K Q^T): lane holds 8 dims of its M-row per k-step.
+  // Q operands (B of S^T = K Q^T): lane holds 8 dims of its M-row per k-step,
+  // pre-multiplied by scale * log2(e) (rounded to bf16) so that the matrix
+  // cores produce scores in log2 units.
+  const float c_log2 = a.scale_log2;
   int pos[2], row[2], hq[2];
   bool valid[2];
   bf16x8_t qv[2][C::kKSteps];
@@ -208,16 +216,24 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk) {
       const uint4 w = valid[qt] ? qp[kk * 4 + lg] : make_uint4(0, 0, 0, 0);
-      qv[qt][kk] = __builtin_bit_cast(bf16x8_t, w);
+      const bf16x8_t raw = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[qt][kk][j] = static_cast<__bf16>(static_cast<float>(raw[j]) * c_log2);
     }
   }
 
+  // Online softmax state per M-row (log2 units): running max m_run, row sum
+  // l_run, and the reference r_ref that the score accumulators start from
+  // (-r_ref), so that a tile's accumulators hold score - r_ref and its
+  // weights are exp2 of them directly.  r_ref follows m_run once the row has
+  // seen an unmasked key (0 before).
   float m_run[2] = {-FLT_MAX, -FLT_MAX};
   float l_run[2] = {0.f, 0.f};
+  float r_ref[2] = {0.f, 0.f};
+  floatx4_t negr[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
   floatx4_t o[C::kDTiles][2];
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt) o[dt][0] = o[dt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  const float c_log2 = a.scale_log2;
 
   // Direct-to-LDS staging.  Thread tid fills 16-byte chunks q = x * 256 + tid
   // of each K and V stage: token row t = q / kCPR, position p = q % kCPR,
@@ -250,16 +266,22 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
   // slice staged in LDS per pass, so no other vector load sits in the loop.
   __shared__ int bt_lds[kTableWindow];
   int blk0 = 0;
-  auto issue = [&](int stage, int rt) {
+  // Block-table entries (from the staged slice) of tile rt's rows that this
+  // wavefront loads; read one iteration before the loads that use them.
+  auto lookup = [&](int rt, int(&ph)[kPer]) {
+#pragma unroll
+    for (int x = 0; x < kPer; ++x)
+      ph[x] = __builtin_amdgcn_readfirstlane(bt_lds[min(rt * T + x * kRowsX + wave * kRowsW, L - 1) / kBlockTokens - blk0]);
+  };
+  auto issue_ph = [&](int stage, int rt, const int(&ph)[kPer]) {
     unsigned char *kd = lds + stage * 2 * kStageBytes;
     unsigned char *vd = kd + kStageBytes;
     const bool tail = rt * T + T > L;                // uniform
 #pragma unroll
     for (int x = 0; x < kPer; ++x) {
       const int tok0 = rt * T + x * kRowsX + wave * kRowsW;       // wavefront's first row
-      const int tcl = min(tok0, L - 1);
-      const int blk = tcl / kBlockTokens;
-      const int phys = __builtin_amdgcn_readfirstlane(bt_lds[blk - blk0]);
+      const int blk = min(tok0, L - 1) / kBlockTokens;
+      const int phys = ph[x];
       const int64_t boff = phys * blk_stride + head_off;
       unsigned off = voff[x];
       if (tail)
@@ -276,6 +298,11 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
                    : "memory");
     }
   };
+  auto issue = [&](int stage, int rt) {
+    int ph[kPer];
+    lookup(rt, ph);
+    issue_ph(stage, rt, ph);
+  };
   const int last_blk = (L - 1) / kBlockTokens;
   constexpr int kPassTiles = kTableWindow * kBlockTokens / T;
   static_assert(S >= 3, "V of tile t and K of tile t + 1 are resident together");
@@ -286,7 +313,8 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
     const unsigned char *kl = lds + st * 2 * kStageBytes;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      sc[tt][0] = sc[tt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      sc[tt][0] = negr[0];
+      sc[tt][1] = negr[1];
       const int kr = tt * 16 + l16;
 #pragma unroll
       for (int kk = 0; kk < C::kKSteps; ++kk) {
@@ -320,14 +348,16 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
       for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[tt * 4 + e] = sc[tt][qt][e];
-      const float mx = group4_max(max_of<4 * kTT>(v)) * c_log2;
+      const float mx = r_ref[qt] + group4_max(max_of<4 * kTT>(v));
       mnew[qt] = vmaxf(m_run[qt], mx);
       raise |= mx > m_run[qt] + PKV_CHUNK_RESCALE_SLACK;
     }
     return raise;
   };
   // Move O and l to the new running max when any row of the wave asked.
-  auto rescale = [&](const float(&mnew)[2], bool raise) {
+  // Move O and l to the new running max when any row of the wave asked, and
+  // re-base the pending tile's accumulators `cur` to the new reference.
+  auto rescale = [&](const float(&mnew)[2], bool raise, floatx4_t(&cur)[kTT][2]) {
     if (__ballot(raise) != 0) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
@@ -336,6 +366,30 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
         l_run[qt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt) o[dt][qt] *= alpha;
+        const float nr = mnew[qt] > -FLT_MAX ? mnew[qt] : r_ref[qt];
+        const float d = nr - r_ref[qt];
+        r_ref[qt] = nr;
+        negr[qt] = floatx4_t{-nr, -nr, -nr, -nr};
+#pragma unroll
+        for (int tt = 0; tt < kTT; ++tt) cur[tt][qt] -= d;
+      }
+    }
+  };
+  // V^T operands of tile stage st for phase B: keys 4*lg .. 4*lg+3 and
+  // 16 + 4*lg .. of each 32-key step, dimension dt*16 + l16, read transposed
+  // from the swizzled tile.
+  auto load_v = [&](int st, bf16x8_t(&va)[C::kDTiles][kKS]) {
+    const unsigned char *vl = lds + st * 2 * kStageBytes + kStageBytes;
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt) {
+      const int dd = dt * 16 + 4 * (l16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const int r1 = ks * 32 + lg * 4 + (l16 >> 2);
+        const int r2 = r1 + 16;
+        const shortx4_t v1 = lds_read_tr16(vl + r1 * kRowBytes + ring_swz<D>(r1, dd >> 3) * 16 + (dd & 7) * 2);
+        const shortx4_t v2 = lds_read_tr16(vl + r2 * kRowBytes + ring_swz<D>(r2, dd >> 3) * 16 + (dd & 7) * 2);
+        va[dt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
@@ -344,31 +398,41 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
   // current tile's scores into bf16 weights and row sums.  The two streams
   // are interleaved by hand, one matrix-core pair per step, each step fenced
   // so that the scheduler keeps them side by side.
-  auto phase_a = [&](const floatx4_t(&cur)[kTT][2], int st_next, floatx4_t(&nxt)[kTT][2], bf16x8_t(&pb)[kKS][2]) {
+  auto phase_a = [&](const floatx4_t(&cur)[kTT][2], int st, int st_next, floatx4_t(&nxt)[kTT][2],
+                     bf16x8_t(&pb)[kKS][2], bf16x8_t(&va)[C::kDTiles][kKS]) {
     const unsigned char *kl = lds + st_next * 2 * kStageBytes;
-    bf16x8_t ka[kTT][C::kKSteps];
+    // K operand of matrix-core pair j (token tile j / kKSteps, k-step
+    // j % kKSteps): read at step j, used kLead steps later.
+    bf16x8_t ka[kTT * C::kKSteps];
+    auto load_k = [&](int j) {
+      const int kr = (j / C::kKSteps) * 16 + l16;
+      ka[j] = *reinterpret_cast<const bf16x8_t *>(kl + kr * kRowBytes + ring_swz<D>(kr, (j % C::kKSteps) * 4 + lg) * 16);
+    };
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
-#pragma unroll
-      for (int kk = 0; kk < C::kKSteps; ++kk) {
-        const int kr = tt * 16 + l16;
-        ka[tt][kk] = *reinterpret_cast<const bf16x8_t *>(kl + kr * kRowBytes + ring_swz<D>(kr, kk * 4 + lg) * 16);
-      }
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) nxt[tt][0] = nxt[tt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < kTT; ++tt) {
+      nxt[tt][0] = negr[0];
+      nxt[tt][1] = negr[1];
+    }
     const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    // The first kLead steps are weights only, covering the operand reads.
+    constexpr int kLead = 2;
     constexpr int kPairs = kTT * C::kKSteps;
+    constexpr int kSteps = kPairs + kLead;
     constexpr int kScores = 2 * kKS * 8;
     float p[2][kKS][8];
 #pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int tt = i / C::kKSteps, kk = i % C::kKSteps;
-      nxt[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][kk], qv[0][kk], nxt[tt][0], 0, 0, 0);
-      nxt[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][kk], qv[1][kk], nxt[tt][1], 0, 0, 0);
+    for (int i = 0; i < kSteps; ++i) {
+      if (Ring<D>::kEarlyV && i == kSteps / 2) load_v(st, va);   // V reads of the current tile, midway
+      if (i < kPairs) load_k(i);
+      if (i >= kLead) {
+        const int j = i - kLead, tt = j / C::kKSteps, kk = j % C::kKSteps;
+        nxt[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qv[0][kk], nxt[tt][0], 0, 0, 0);
+        nxt[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qv[1][kk], nxt[tt][1], 0, 0, 0);
+      }
 #pragma unroll
-      for (int w = i * kScores / kPairs; w < (i + 1) * kScores / kPairs; ++w) {
+      for (int w = i * kScores / kSteps; w < (i + 1) * kScores / kSteps; ++w) {
         const int qt = w / (kKS * 8), ks = (w / 8) % kKS, e8 = w % 8;
-        p[qt][ks][e8] = fast_exp2(fmaf(cur[2 * ks + e8 / 4][qt][e8 % 4], c_log2, -m_run[qt]));
+        p[qt][ks][e8] = fast_exp2(cur[2 * ks + e8 / 4][qt][e8 % 4]);
         if (e8 == 7) {
           const float *q8 = p[qt][ks];
           pb[ks][qt] = bf16x8_t{static_cast<__bf16>(q8[0]), static_cast<__bf16>(q8[1]), static_cast<__bf16>(q8[2]),
@@ -391,21 +455,9 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
   // Phase B: O^T += V^T P^T of the current tile (stage st) on the matrix
   // cores while the vector ALU takes the row max of the next tile.  Returns
   // the rescale vote, as rowmax.
-  auto phase_b = [&](int st, const bf16x8_t(&pb)[kKS][2], const floatx4_t(&nxt)[kTT][2], float(&mnew)[2]) {
-    const unsigned char *vl = lds + st * 2 * kStageBytes + kStageBytes;
-    bf16x8_t va[C::kDTiles][kKS];
-#pragma unroll
-    for (int dt = 0; dt < C::kDTiles; ++dt) {
-      const int dd = dt * 16 + 4 * (l16 & 3);
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const int r1 = ks * 32 + lg * 4 + (l16 >> 2);
-        const int r2 = r1 + 16;
-        const shortx4_t v1 = lds_read_tr16(vl + r1 * kRowBytes + ring_swz<D>(r1, dd >> 3) * 16 + (dd & 7) * 2);
-        const shortx4_t v2 = lds_read_tr16(vl + r2 * kRowBytes + ring_swz<D>(r2, dd >> 3) * 16 + (dd & 7) * 2);
-        va[dt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    }
+  auto phase_b = [&](const bf16x8_t(&pb)[kKS][2], bf16x8_t(&va)[C::kDTiles][kKS], int st,
+                     const floatx4_t(&nxt)[kTT][2], float(&mnew)[2]) {
+    if constexpr (!Ring<D>::kEarlyV) load_v(st, va);
     constexpr int kPairs = C::kDTiles * kKS;
     constexpr int kItems = 2 * kTT;
     float acc[2] = {-INFINITY, -INFINITY};
@@ -425,7 +477,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
     bool raise = false;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const float mx = group4_max(acc[qt]) * c_log2;
+      const float mx = r_ref[qt] + group4_max(acc[qt]);
       mnew[qt] = vmaxf(m_run[qt], mx);
       raise |= mx > m_run[qt] + PKV_CHUNK_RESCALE_SLACK;
     }
@@ -455,6 +507,8 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
     qk(0, s0);
     mask(pass0, s0);
     bool raise = rowmax(s0, mnew);
+    int ph_next[kPer];
+    lookup(min(pass0 + S - 1, pass1 - 1), ph_next);
 
     // One iteration: tile rt's scores are in `cur`, tile rt + 1's go to `nxt`.
     auto iter = [&](int rt, floatx4_t(&cur)[kTT][2], floatx4_t(&nxt)[kTT][2], auto masked_next) {
@@ -464,17 +518,19 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
       // the barrier every wave is done with tile rt - 1, whose stage refills.
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 3)) : "memory");
       __syncthreads();
-      issue((rt - pass0 + S - 1) % S, min(rt + S - 1, pass1 - 1));
-      rescale(mnew, raise);
+      issue_ph((rt - pass0 + S - 1) % S, min(rt + S - 1, pass1 - 1), ph_next);
+      rescale(mnew, raise, cur);
       // Phase A: the weights of tile rt on the vector ALU while the matrix
       // cores form the scores of tile rt + 1 (of a repeat of tile rt on the
       // last iteration: computed, never used).
       bf16x8_t pb[kKS][2];
-      phase_a(cur, st_next, nxt, pb);
+      bf16x8_t va[C::kDTiles][kKS];
+      phase_a(cur, st, st_next, nxt, pb, va);
       if constexpr (decltype(masked_next)::value) mask(rt + 1, nxt);
       // Phase B: O += V P of tile rt on the matrix cores while the vector
       // ALU takes the row max of tile rt + 1.
-      raise = phase_b(st, pb, nxt, mnew) && rt + 1 < pass1;
+      raise = phase_b(pb, va, st, nxt, mnew) && rt + 1 < pass1;
+      lookup(min(rt + S, pass1 - 1), ph_next);
     };
     // Tiles before `unmasked_end` need no causal mask for any row of this
     // wave.  Iterations whose next tile is among them run branch-free, two at
@@ -518,7 +574,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
     if (!valid[qt]) continue;
     if (partial_out) {
       const int m = mw + qt * 16 + l16;
-      const int64_t pidx = (static_cast<int64_t>(b) * hkv + g) * kChunkSplitSlots + m * cs.splits + split;
+      const int64_t pidx = (static_cast<int64_t>(b) * hkv + g) * chunk_split_slots(D) + m * cs.splits + split;
       float *pa = a.chunk_part + pidx * kChunkSlotFloats<D>;
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt)
@@ -551,10 +607,11 @@ __global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendA
 constexpr int kMergeRowsPerWave = 4;
 constexpr int kMergeWaves = 4;
 
+template <int D>
 __device__ __forceinline__ int merge_units(const AttendArgs &a, int b, int G) {
   const SegInfo s = seg_info(a, b);
   if (!s.ok || s.n < 2) return 0;
-  const ChunkShape c = chunk_shape(s.n, s.L, G);
+  const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.splits > 1 ? (s.n * G + kMergeRowsPerWave - 1) / kMergeRowsPerWave : 0;
 }
 
@@ -568,7 +625,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void chunk_merge_kernel(Attend
   const int hkv = a.num_kv_heads;
   const int wg = blockIdx.x / hkv;
   const int g = blockIdx.x - wg * hkv;                // same head-to-workgroup order as the chunk kernel
-  auto units_fn = [&](int b) { return merge_units(a, b, G); };
+  auto units_fn = [&](int b) { return merge_units<D>(a, b, G); };
   const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
   const int unit = wg * kMergeWaves + wave;
   if (unit >= total) return;
@@ -577,14 +634,14 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void chunk_merge_kernel(Attend
   u = __builtin_amdgcn_readfirstlane(u);
   const SegInfo si = seg_info_uniform(a, b);
   if (!si.ok) return;
-  const ChunkShape cs = chunk_shape(si.n, si.L, G);
+  const ChunkShape cs = chunk_shape<D>(si.n, si.L, G);
   const int m = u * kMergeRowsPerWave + (lane >> 4);
   if (m >= si.n * G) return;                          // no cross-group exchange below
   const int i = m / G;
   const int h = m - i * G;
   const int pos = si.L - si.n + i;
   const int last = min(cs.splits - 1, pos / (cs.tps * kKV));
-  const float *pp = a.chunk_part + ((static_cast<int64_t>(b) * hkv + g) * kChunkSplitSlots +
+  const float *pp = a.chunk_part + ((static_cast<int64_t>(b) * hkv + g) * chunk_split_slots(D) +
                                     static_cast<int64_t>(m) * cs.splits) * SF;
   // Row max over the ranges: lane li reads ranges li, li + 16, ...
   float mx = -FLT_MAX;
@@ -637,10 +694,10 @@ int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, i
   (void)max_context_len;
   const int G = a.num_q_heads / a.num_kv_heads;
   // Upper bound on workgroups: per segment, row tiles x splits is at most
-  // max(row tiles, kChunkSplitRowTiles) and row tiles <= n G / 128 + 1;
+  // max(row tiles, the split target) and row tiles <= n G / 128 + 1;
   // surplus workgroups exit at once.
   const int64_t bound =
-      (static_cast<int64_t>(a.total_q) * G / kMTile + static_cast<int64_t>(a.num_segments) * (kChunkSplitRowTiles + 1)) *
+      (static_cast<int64_t>(a.total_q) * G / kMTile + static_cast<int64_t>(a.num_segments) * (chunk_split_row_tiles(head_dim) + 1)) *
       a.num_kv_heads;
   if (bound <= 0) return PKV_OK;
   if (bound > 0x7fffffff) return PKV_ERR_UNSUPPORTED;

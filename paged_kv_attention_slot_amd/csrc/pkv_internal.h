@@ -68,12 +68,17 @@ constexpr int kDecodeStages = PKV_DECODE_STAGES;
 
 // Multi-row segments with fewer than this many 128-row tiles split their
 // key range so that (row tiles x splits) reaches it; partial slots per
-// (segment, KV head) = kChunkSplitRowTiles * 128.
-#ifndef PKV_CHUNK_SPLIT_ROW_TILES
-#define PKV_CHUNK_SPLIT_ROW_TILES 32
+// (segment, KV head) = that target * 128 (chunk_split_slots).
+#ifndef PKV_CHUNK_SPLIT_ROW_TILES_D64
+#define PKV_CHUNK_SPLIT_ROW_TILES_D64 64
 #endif
-constexpr int kChunkSplitRowTiles = PKV_CHUNK_SPLIT_ROW_TILES;
-constexpr int kChunkSplitSlots = kChunkSplitRowTiles * 128;
+#ifndef PKV_CHUNK_SPLIT_ROW_TILES_D128
+#define PKV_CHUNK_SPLIT_ROW_TILES_D128 32
+#endif
+__host__ __device__ constexpr int chunk_split_row_tiles(int head_dim) {
+  return head_dim == 64 ? PKV_CHUNK_SPLIT_ROW_TILES_D64 : PKV_CHUNK_SPLIT_ROW_TILES_D128;
+}
+__host__ __device__ constexpr int chunk_split_slots(int head_dim) { return chunk_split_row_tiles(head_dim) * 128; }
 
 // Chunk kernel LDS ring: tokens per stage and stages, per head_dim.
 #ifndef PKV_CHUNK_RING_TOK_D64
@@ -87,6 +92,13 @@ constexpr int kChunkSplitSlots = kChunkSplitRowTiles * 128;
 #endif
 #ifndef PKV_CHUNK_MIN_BLOCKS_D128
 #define PKV_CHUNK_MIN_BLOCKS_D128 2
+#endif
+// Read the V operands midway through phase A (1) or at the start of phase B.
+#ifndef PKV_CHUNK_EARLY_V_D64
+#define PKV_CHUNK_EARLY_V_D64 1
+#endif
+#ifndef PKV_CHUNK_EARLY_V_D128
+#define PKV_CHUNK_EARLY_V_D128 1
 #endif
 #ifndef PKV_CHUNK_TABLE_WINDOW
 #define PKV_CHUNK_TABLE_WINDOW 512
@@ -115,7 +127,7 @@ struct AttendArgs {
   const int32_t *block_tables;
   float *part_acc;   // [part_rows][Hq][part_max][D]
   float *part_ml;    // [part_rows][Hq][part_max][2]  (running max in log2 units, sum)
-  float *chunk_part; // [num_segments][Hkv][kChunkSplitSlots][D + 4]: key-range partials of split chunks
+  float *chunk_part; // [num_segments][Hkv][chunk_split_slots(D)][D + 4]: key-range partials of split chunks
   int32_t num_segments;
   int32_t num_slots;
   int32_t max_blocks;

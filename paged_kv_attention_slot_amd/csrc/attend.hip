@@ -1,6 +1,7 @@
 // C-ABI entry points for the device side: argument checks, workspace sizing
 // and kernel dispatch on the caller's stream.
 #include <cmath>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "pkv_internal.h"
@@ -62,6 +63,49 @@ WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t 
   return w;
 }
 
+// What the host knows about a step's segments: pkv_mixed_step reads it from
+// the pinned host copy of the metadata; pkv_paged_attend (metadata on the
+// device only) leaves `known` false and every kernel is launched.
+struct StepFacts {
+  bool known = false;
+  int32_t decode_rows = 0;         // segments with query_len == 1
+  int32_t chunk_segments = 0;      // segments with query_len > 1
+  int32_t max_decode_context = 0;  // longest context among the decode rows
+};
+
+// Per-device auxiliary stream (default priority) and fork/join events that
+// let a step's decode rows run beside its chunk kernels.  Created on first
+// use and kept for the life of the process; the mutex makes each fork/join
+// sequence atomic for callers on several host threads.
+struct AuxStream {
+  bool tried = false, ok = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mutex;
+AuxStream g_aux[kMaxDevices];
+
+// Call with g_aux_mutex held.
+AuxStream *aux_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  AuxStream &x = g_aux[dev];
+  if (!x.tried) {
+    x.tried = true;
+    x.ok = hipStreamCreateWithFlags(&x.stream, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return x.ok ? &x : nullptr;
+}
+
+int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int32_t *row_to_slot,
+           const int32_t *query_start, const int32_t *query_len, int32_t num_segments, const int32_t *context_lens,
+           const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq, int32_t max_query_len,
+           int32_t max_context_len, const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
+           size_t workspace_bytes, hipStream_t s, const StepFacts &facts);
+
 }  // namespace
 }  // namespace pkv
 
@@ -100,6 +144,57 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
                      int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_context_len,
                      const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
                      size_t workspace_bytes, void *stream) {
+  return attend(q_packed, total_q, num_q_heads, row_to_slot, query_start, query_len, num_segments, context_lens,
+                block_tables, num_slots, max_blocks_per_seq, max_query_len, max_context_len, pool, scale, out,
+                out_dtype, workspace, workspace_bytes, static_cast<hipStream_t>(stream), StepFacts{});
+}
+
+int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
+  if (!d || !pool_ok(pool) || !d->host_meta || !d->dev_meta || d->meta_len < 0 || d->num_tokens < 0 ||
+      d->num_segments < 0 || d->num_slots <= 0 || !scale_ok(d->scale))
+    return PKV_ERR_INVALID_ARG;
+  auto in_meta = [&](int32_t off, int64_t n) { return off >= 0 && off + n <= d->meta_len; };
+  if (!in_meta(d->slot_mapping_off, d->num_tokens) || !in_meta(d->query_start_off, d->num_segments) ||
+      !in_meta(d->query_len_off, d->num_segments) || !in_meta(d->row_to_slot_off, d->num_segments) ||
+      !in_meta(d->context_lens_off, d->num_slots))
+    return PKV_ERR_INVALID_ARG;
+  if (!pool_supported(pool)) return PKV_ERR_UNSUPPORTED;
+  if (d->num_tokens > 0 && (!d->k_new || !d->v_new)) return PKV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int st = launch_kv_append(d->host_meta + d->slot_mapping_off, d->k_new, d->v_new, d->num_tokens, *pool, s,
+                                  d->host_meta, d->dev_meta, d->meta_len);
+  if (st != PKV_OK) return st;
+  StepFacts f;
+  f.known = true;
+  const int32_t *hq = d->host_meta + d->query_len_off;
+  const int32_t *hs = d->host_meta + d->row_to_slot_off;
+  const int32_t *hl = d->host_meta + d->context_lens_off;
+  for (int32_t b = 0; b < d->num_segments; ++b) {
+    if (hq[b] == 1) {
+      ++f.decode_rows;
+      if (hs[b] >= 0 && hs[b] < d->num_slots && hl[hs[b]] > f.max_decode_context) f.max_decode_context = hl[hs[b]];
+    } else if (hq[b] > 1) {
+      ++f.chunk_segments;
+    }
+  }
+  if (f.max_decode_context > d->max_context_len) f.max_decode_context = d->max_context_len;
+  const int32_t *m = d->dev_meta;
+  return attend(d->q_packed, d->total_q, d->num_q_heads, m + d->row_to_slot_off, m + d->query_start_off,
+                m + d->query_len_off, d->num_segments, m + d->context_lens_off, d->block_tables, d->num_slots,
+                d->max_blocks_per_seq, d->max_query_len, d->max_context_len, pool, d->scale, d->out, d->out_dtype,
+                d->workspace, d->workspace_bytes, s, f);
+}
+
+}  // extern "C"
+
+namespace pkv {
+namespace {
+
+int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int32_t *row_to_slot,
+           const int32_t *query_start, const int32_t *query_len, int32_t num_segments, const int32_t *context_lens,
+           const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq, int32_t max_query_len,
+           int32_t max_context_len, const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
+           size_t workspace_bytes, hipStream_t s, const StepFacts &facts) {
   if (!pool_ok(pool) || total_q < 0 || num_segments < 0 || num_q_heads <= 0 || num_slots <= 0 ||
       max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0)
     return PKV_ERR_INVALID_ARG;
@@ -144,34 +239,35 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (max_query_len > 1 && !multirow) {
+  // Multi-row segments on the chunk kernels (unless they go row by row on
+  // the decode path); decode rows on the decode kernels, whose grid and
+  // partition reduce follow the decode rows' own longest context when the
+  // host knows it.
+  const bool run_chunk = max_query_len > 1 && !multirow && (!facts.known || facts.chunk_segments > 0);
+  const bool run_decode = !facts.known || multirow || facts.decode_rows > 0;
+  const int32_t decode_ctx = facts.known && !multirow ? facts.max_decode_context : max_context_len;
+  const bool need_reduce = decode_ctx > kDecodePartitionTokens;
+  if (run_chunk && run_decode && facts.known && PKV_CONCURRENT_DECODE) {
+    std::lock_guard<std::mutex> lock(g_aux_mutex);
+    AuxStream *ax = aux_for_current_device();
+    if (ax) {
+      if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
+        return PKV_ERR_HIP;
+      const int sd = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, ax->stream);
+      // the join is recorded even after a failed launch, so `s` never waits
+      // on a stale event
+      if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PKV_ERR_HIP;
+      const int sc = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, s);
+      if (hipStreamWaitEvent(s, ax->join, 0) != hipSuccess) return PKV_ERR_HIP;
+      return sd != PKV_OK ? sd : sc;
+    }
+  }
+  if (run_chunk) {
     const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, s);
     if (st != PKV_OK) return st;
   }
-  return launch_decode(a, pool->dtype, pool->head_dim, max_context_len, max_query_len, s);
+  return run_decode ? launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, s) : PKV_OK;
 }
 
-int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
-  if (!d || !pool_ok(pool) || !d->host_meta || !d->dev_meta || d->meta_len < 0 || d->num_tokens < 0 ||
-      d->num_segments < 0 || d->num_slots <= 0 || !scale_ok(d->scale))
-    return PKV_ERR_INVALID_ARG;
-  auto in_meta = [&](int32_t off, int64_t n) { return off >= 0 && off + n <= d->meta_len; };
-  if (!in_meta(d->slot_mapping_off, d->num_tokens) || !in_meta(d->query_start_off, d->num_segments) ||
-      !in_meta(d->query_len_off, d->num_segments) || !in_meta(d->row_to_slot_off, d->num_segments) ||
-      !in_meta(d->context_lens_off, d->num_slots))
-    return PKV_ERR_INVALID_ARG;
-  if (!pool_supported(pool)) return PKV_ERR_UNSUPPORTED;
-  if (d->num_tokens > 0 && (!d->k_new || !d->v_new)) return PKV_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int st = launch_kv_append(d->host_meta + d->slot_mapping_off, d->k_new, d->v_new, d->num_tokens, *pool, s,
-                                  d->host_meta, d->dev_meta, d->meta_len);
-  if (st != PKV_OK) return st;
-  const int32_t *m = d->dev_meta;
-  return pkv_paged_attend(d->q_packed, d->total_q, d->num_q_heads, m + d->row_to_slot_off, m + d->query_start_off,
-                          m + d->query_len_off, d->num_segments, m + d->context_lens_off, d->block_tables,
-                          d->num_slots, d->max_blocks_per_seq, d->max_query_len, d->max_context_len, pool, d->scale,
-                          d->out, d->out_dtype, d->workspace, d->workspace_bytes, stream);
-}
-
-}  // extern "C"
+}  // namespace
+}  // namespace pkv

@@ -435,8 +435,8 @@ int dispatch_g(const AttendArgs &a, int G, int64_t items_bound, hipStream_t stre
 
 }  // namespace
 
-int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len,
-                  int32_t max_query_len, hipStream_t stream) {
+int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len, bool need_reduce,
+                  hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
   const int64_t rows = a.multirow ? static_cast<int64_t>(a.total_q) : a.num_segments;
@@ -451,14 +451,13 @@ int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t 
     st = head_dim == 128 ? dispatch_g<float, 128>(a, G, items_bound, stream)
                          : dispatch_g<float, 64>(a, G, items_bound, stream);
   }
-  if (st != PKV_OK || a.part_max <= 1) return st;
+  if (st != PKV_OK || a.part_max <= 1 || !need_reduce) return st;
   const unsigned grid = static_cast<unsigned>(a.num_segments) * static_cast<unsigned>(a.num_q_heads);
   const size_t lds = static_cast<size_t>(a.part_max) * sizeof(float);
   if (head_dim == 128)
     reduce_kernel<128><<<dim3(grid), dim3(kWave), lds, stream>>>(a);
   else
     reduce_kernel<64><<<dim3(grid), dim3(kWave), lds, stream>>>(a);
-  (void)max_query_len;
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

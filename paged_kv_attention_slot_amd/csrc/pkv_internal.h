@@ -100,6 +100,11 @@ __host__ __device__ constexpr int chunk_split_slots(int head_dim) { return chunk
 #ifndef PKV_CHUNK_EARLY_V_D128
 #define PKV_CHUNK_EARLY_V_D128 1
 #endif
+// Run a step's decode rows on an auxiliary stream beside its chunk kernels
+// when the host knows both are present.
+#ifndef PKV_CONCURRENT_DECODE
+#define PKV_CONCURRENT_DECODE 1
+#endif
 #ifndef PKV_CHUNK_TABLE_WINDOW
 #define PKV_CHUNK_TABLE_WINDOW 512
 #endif
@@ -148,10 +153,11 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
                      int32_t num_tokens, const pkv_pool &pool, hipStream_t stream,
                      const int32_t *stage_src = nullptr, int32_t *stage_dst = nullptr, int32_t stage_len = 0);
 
-// Decode path (one query row per work item; split-context partitions) and the
-// partition reduce.  `max_query_len`/`max_context_len` size the grid only.
-int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len,
-                  int32_t max_query_len, hipStream_t stream);
+// Decode path (one query row per work item; split-context partitions) and,
+// when `need_reduce` (some row has more than one partition), the partition
+// reduce.  `max_context_len` sizes the grid only.
+int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len, bool need_reduce,
+                  hipStream_t stream);
 
 int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, hipStream_t stream);
 

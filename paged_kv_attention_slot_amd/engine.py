@@ -42,6 +42,17 @@ class StepMeta:
     max_context_len: int
 
 
+@dataclass
+class PreparedStep:
+    """A lowered step and its pkv_mixed_step descriptor (see prepare_fused)."""
+    desc: object
+    staging: object
+    stream: object
+    meta: StepMeta
+    out: object
+    keep: tuple
+
+
 class _Staging:
     """A pinned host int32 buffer, its device twin, and the event recorded
     after the copy that last read the host buffer."""
@@ -154,9 +165,10 @@ class PagedKVEngine:
         st.used = True
         return meta
 
-    def fused_step(self, entries, k_new, v_new, q, scale, out=None, out_dtype=None):
-        """Lower on the host, then one library call (pkv_mixed_step): the append
-        kernel stages the metadata to the device and appends; attention follows."""
+    def prepare_fused(self, entries, k_new, v_new, q, scale, out=None, out_dtype=None):
+        """Lower on the host and build the one-call step descriptor for
+        pkv_mixed_step (run it with run_prepared; running it again replays the
+        same append and attention)."""
         torch = self.torch
         meta, st, offs, stream = self._lower_host(entries)
         if out is None:
@@ -170,10 +182,22 @@ class PagedKVEngine:
                           q.data_ptr(), self.d_block_tables.data_ptr(), float(scale), out.data_ptr(),
                           B.pkv_dtype_of(out.dtype), ws.data_ptr() if ws is not None else None,
                           ws.numel() if ws is not None else 0)
-        B.mixed_step(desc, self.pool, meta.stream)
-        st.copied.record(stream)          # the step's kernels have read the host buffer after this
-        st.used = True
-        return out, meta
+        # the tensors are held so their memory outlives every replay
+        return PreparedStep(desc=desc, staging=st, stream=stream, meta=meta, out=out,
+                            keep=(k_new, v_new, q, ws))
+
+    def run_prepared(self, prep):
+        """One library call (pkv_mixed_step): the append kernel stages the
+        metadata to the device and appends; attention follows."""
+        B.mixed_step(prep.desc, self.pool, prep.meta.stream)
+        prep.staging.copied.record(prep.stream)   # the step's kernels have read the host buffer after this
+        prep.staging.used = True
+        return prep.out
+
+    def fused_step(self, entries, k_new, v_new, q, scale, out=None, out_dtype=None):
+        """Lower on the host, then one library call (pkv_mixed_step)."""
+        prep = self.prepare_fused(entries, k_new, v_new, q, scale, out=out, out_dtype=out_dtype)
+        return self.run_prepared(prep), prep.meta
 
     def append(self, meta: StepMeta, k_new, v_new):
         B.kv_append(meta.slot_mapping, k_new, v_new, self.pool, stream=meta.stream)

@@ -71,6 +71,7 @@ struct StepFacts {
   int32_t decode_rows = 0;         // segments with query_len == 1
   int32_t chunk_segments = 0;      // segments with query_len > 1
   int32_t max_decode_context = 0;  // longest context among the decode rows
+  int64_t decode_parts = 0;        // split-context partitions over the decode rows
 };
 
 // Per-device auxiliary stream (default priority) and fork/join events that
@@ -172,7 +173,11 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
   for (int32_t b = 0; b < d->num_segments; ++b) {
     if (hq[b] == 1) {
       ++f.decode_rows;
-      if (hs[b] >= 0 && hs[b] < d->num_slots && hl[hs[b]] > f.max_decode_context) f.max_decode_context = hl[hs[b]];
+      if (hs[b] >= 0 && hs[b] < d->num_slots) {
+        const int32_t L = hl[hs[b]];
+        if (L > f.max_decode_context) f.max_decode_context = L;
+        f.decode_parts += L > 0 ? (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens : 1;
+      }
     } else if (hq[b] > 1) {
       ++f.chunk_segments;
     }
@@ -247,13 +252,14 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   const bool run_decode = !facts.known || multirow || facts.decode_rows > 0;
   const int32_t decode_ctx = facts.known && !multirow ? facts.max_decode_context : max_context_len;
   const bool need_reduce = decode_ctx > kDecodePartitionTokens;
+  const int64_t work_waves = facts.known && !multirow ? facts.decode_parts * pool->num_kv_heads : -1;
   if (run_chunk && run_decode && facts.known && PKV_CONCURRENT_DECODE) {
     std::lock_guard<std::mutex> lock(g_aux_mutex);
     AuxStream *ax = aux_for_current_device();
     if (ax) {
       if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
         return PKV_ERR_HIP;
-      const int sd = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, ax->stream);
+      const int sd = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, ax->stream);
       // the join is recorded even after a failed launch, so `s` never waits
       // on a stale event
       if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PKV_ERR_HIP;
@@ -266,7 +272,7 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
     const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, s);
     if (st != PKV_OK) return st;
   }
-  return run_decode ? launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, s) : PKV_OK;
+  return run_decode ? launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, s) : PKV_OK;
 }
 
 }  // namespace

@@ -436,14 +436,16 @@ int dispatch_g(const AttendArgs &a, int G, int64_t items_bound, hipStream_t stre
 }  // namespace
 
 int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len, bool need_reduce,
-                  hipStream_t stream) {
+                  int64_t work_waves, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
   const int64_t rows = a.multirow ? static_cast<int64_t>(a.total_q) : a.num_segments;
   const int64_t items_bound = rows * (parts > 0 ? parts : 1) * a.num_kv_heads;
   int st;
   if (dtype == PKV_BF16 && !a.multirow && PKV_DECODE_MFMA) {
-    st = launch_decode_mfma(a, head_dim, max_context_len, stream);
+    const int stages =
+        work_waves >= 0 && work_waves < PKV_DECODE_FEW_WAVES ? PKV_DECODE_MFMA_STAGES_FEW : kDecodeMfmaStages;
+    st = launch_decode_mfma(a, head_dim, max_context_len, stages, stream);
   } else if (dtype == PKV_BF16) {
     st = head_dim == 128 ? dispatch_g<uint16_t, 128>(a, G, items_bound, stream)
                          : dispatch_g<uint16_t, 64>(a, G, items_bound, stream);

@@ -9,7 +9,7 @@
 // blog, §Paged KV and paged attention: walk the block table in logical order
 // over the shared pool, no gather):
 //   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, 1
-//     KiB per instruction, nontemporal), kDecodeStages tiles in flight; the
+//     KiB per instruction, nontemporal), kDecodeMfmaStages tiles in flight; the
 //     16-byte chunks of each token row are XOR-swizzled so that the reads
 //     below are free of bank conflicts;
 //   * S^T[token][head] = K Q^T on v_mfma_f32_16x16x32_bf16 (heads are the 16
@@ -67,10 +67,10 @@ __device__ __forceinline__ int decode_units(const AttendArgs &a, int b) {
   return s.ok && s.n == 1 ? num_parts_m(s.L) : 0;
 }
 
-template <int D>
+template <int D, int S>
 __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(AttendArgs a, int G) {
   using M = MGeo<D>;
-  constexpr int S = kDecodeStages;
+  static_assert(S >= 1 && S <= 3, "1 to 3 tiles in flight");
   constexpr int PT = kDecodePartitionTokens;
   // One LDS array per stage and per K/V so the compiler can tell the
   // in-flight tile loads apart from the tile being read.
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
         compute(kt, vt, jj, std::false_type{});
     };
 
-    // kDecodeStages tiles in flight.  Past the last tile the prefetch re-reads
+    // kDecodeMfmaStages tiles in flight.  Past the last tile the prefetch re-reads
     // the last tile (a cache hit) so every wait below has a static count.
     issue(0, 0);
     if constexpr (S > 1) issue(1, min(1, nb - 1));
@@ -296,18 +296,25 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
 
 }  // namespace
 
-int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, hipStream_t stream) {
+template <int D>
+int launch_decode_mfma_d(const AttendArgs &a, int G, int64_t grid, int stages, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>(grid)), b(kWave);
+  if (stages >= 3) decode_mfma_kernel<D, 3><<<g, b, 0, stream>>>(a, G);
+  else if (stages == 2) decode_mfma_kernel<D, 2><<<g, b, 0, stream>>>(a, G);
+  else decode_mfma_kernel<D, 1><<<g, b, 0, stream>>>(a, G);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
+                       hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
   const int64_t items_bound = static_cast<int64_t>(a.num_segments) * (parts > 0 ? parts : 1) * a.num_kv_heads;
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * kDecodeWavesPerCU;
   const int64_t grid = items_bound < cap ? items_bound : cap;
   if (grid <= 0) return PKV_OK;
-  if (head_dim == 128)
-    decode_mfma_kernel<128><<<dim3(static_cast<unsigned>(grid)), dim3(kWave), 0, stream>>>(a, G);
-  else
-    decode_mfma_kernel<64><<<dim3(static_cast<unsigned>(grid)), dim3(kWave), 0, stream>>>(a, G);
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return head_dim == 128 ? launch_decode_mfma_d<128>(a, G, grid, stages, stream)
+                         : launch_decode_mfma_d<64>(a, G, grid, stages, stream);
 }
 
 }  // namespace pkv

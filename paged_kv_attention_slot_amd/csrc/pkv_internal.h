@@ -65,6 +65,20 @@ constexpr int kDecodeMfmaMinWaves = PKV_DECODE_MFMA_MIN_WAVES;
 #define PKV_CHUNK_RESCALE_SLACK 8.0f
 #endif
 constexpr int kDecodeStages = PKV_DECODE_STAGES;
+// K/V tiles in flight per wavefront in the MFMA decode kernel (1 to 3): the
+// default, and the depth used when a launch has fewer than
+// PKV_DECODE_FEW_WAVES wavefronts of work (each must then pull more bytes
+// in flight).  Neither changes the arithmetic.
+#ifndef PKV_DECODE_MFMA_STAGES
+#define PKV_DECODE_MFMA_STAGES 1
+#endif
+#ifndef PKV_DECODE_MFMA_STAGES_FEW
+#define PKV_DECODE_MFMA_STAGES_FEW 3
+#endif
+#ifndef PKV_DECODE_FEW_WAVES
+#define PKV_DECODE_FEW_WAVES 400
+#endif
+constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 
 // Multi-row segments with fewer than this many 128-row tiles split their
 // key range so that (row tiles x splits) reaches it; partial slots per
@@ -156,10 +170,13 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
 // Decode path (one query row per work item; split-context partitions) and,
 // when `need_reduce` (some row has more than one partition), the partition
 // reduce.  `max_context_len` sizes the grid only.
+// `work_waves` is the launch's exact count of (row, KV head, partition)
+// items when the host knows it, else -1.
 int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len, bool need_reduce,
-                  hipStream_t stream);
+                  int64_t work_waves, hipStream_t stream);
 
-int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, hipStream_t stream);
+int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
+                       hipStream_t stream);
 
 // Multi-row segments (query_len > 1) on bf16 MFMA tiles.  chunk_supported()
 // tells whether this shape is built; otherwise multi-row segments take the

@@ -114,7 +114,7 @@ def test_attention_matches_oracle(name, fused, gpu_available):
 EDGE_SEQS = [
     [(0, 0, 1)],                                  # L = 1: output is V0
     [(0, 15, 1), (1, 16, 1), (2, 31, 1)],         # L = 16, 17, 32 block edges
-    [(0, 511, 1), (1, 512, 1), (2, 1023, 1), (3, 1024, 1)],   # partition edges
+    [(0, 511, 1), (1, 512, 1), (2, 1023, 1), (3, 1024, 1), (4, 2047, 1), (5, 2048, 1)],   # partition edges
     [(5, 3000, 1), (2, 7, 1)],                    # slots out of order
     [(0, 0, 5), (1, 40, 1), (2, 3, 2)],           # tiny prompt, decode, 2 drafts
     [(0, 700, 16), (1, 3000, 3), (2, 200, 40), (3, 1300, 1)],   # key-range splits of short segments

@@ -125,13 +125,13 @@ struct Ring;
 template <>
 struct Ring<64> {
   static constexpr int kTok = PKV_CHUNK_RING_TOK_D64, kStages = PKV_CHUNK_RING_STAGES_D64;
-  static constexpr int kMinBlocks = PKV_CHUNK_MIN_BLOCKS_D64;
+  static constexpr int kMinWaves = PKV_CHUNK_MIN_WAVES_D64;
   static constexpr bool kEarlyV = PKV_CHUNK_EARLY_V_D64;
 };
 template <>
 struct Ring<128> {
   static constexpr int kTok = PKV_CHUNK_RING_TOK_D128, kStages = PKV_CHUNK_RING_STAGES_D128;
-  static constexpr int kMinBlocks = PKV_CHUNK_MIN_BLOCKS_D128;
+  static constexpr int kMinWaves = PKV_CHUNK_MIN_WAVES_D128;
   static constexpr bool kEarlyV = PKV_CHUNK_EARLY_V_D128;
 };
 
@@ -149,7 +149,7 @@ __device__ __forceinline__ unsigned lds_addr32(const unsigned char *p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, Ring<D>::kMinBlocks) void chunk_kernel(AttendArgs a, int G) {
+__global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendArgs a, int G) {
   using C = ChunkGeo<D>;
   constexpr int T = Ring<D>::kTok;            // tokens per ring stage
   constexpr int S = Ring<D>::kStages;

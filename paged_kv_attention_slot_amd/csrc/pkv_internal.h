@@ -101,11 +101,13 @@ __host__ __device__ constexpr int chunk_split_slots(int head_dim) { return chunk
 #ifndef PKV_CHUNK_RING_STAGES_D64
 #define PKV_CHUNK_RING_STAGES_D64 4
 #endif
-#ifndef PKV_CHUNK_MIN_BLOCKS_D64
-#define PKV_CHUNK_MIN_BLOCKS_D64 2
+// Chunk kernel occupancy hint: wavefronts per SIMD the register budget must
+// allow (the second launch-bounds argument).
+#ifndef PKV_CHUNK_MIN_WAVES_D64
+#define PKV_CHUNK_MIN_WAVES_D64 2
 #endif
-#ifndef PKV_CHUNK_MIN_BLOCKS_D128
-#define PKV_CHUNK_MIN_BLOCKS_D128 2
+#ifndef PKV_CHUNK_MIN_WAVES_D128
+#define PKV_CHUNK_MIN_WAVES_D128 2
 #endif
 // Read the V operands midway through phase A (1) or at the start of phase B.
 #ifndef PKV_CHUNK_EARLY_V_D64

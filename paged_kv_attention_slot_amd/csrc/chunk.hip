@@ -43,7 +43,6 @@ __device__ __forceinline__ shortx4_t lds_read_tr16(const unsigned char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_t *)(p));
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // IEEE-754 maximum (NaN-propagating): lowers to v_maximum3_f32 / v_maximum_f32
 // with no canonicalisation of matrix-core results, unlike fmaxf.
@@ -148,7 +147,9 @@ __device__ __forceinline__ unsigned lds_addr32(const unsigned char *p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)(p)));
 }
 
-template <int D>
+// OFF32: every byte of a pool tensor lies within 4 GiB of its base, so a tile
+// load addresses the tensor base (scalar) plus one 32-bit vector offset.
+template <int D, bool OFF32>
 __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendArgs a, int G) {
   using C = ChunkGeo<D>;
   constexpr int T = Ring<D>::kTok;            // tokens per ring stage
@@ -222,13 +223,15 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     }
   }
 
-  // Online softmax state per M-row (log2 units): running max m_run, row sum
-  // l_run, and the reference r_ref that the score accumulators start from
-  // (-r_ref), so that a tile's accumulators hold score - r_ref and its
-  // weights are exp2 of them directly.  r_ref follows m_run once the row has
-  // seen an unmasked key (0 before).
+  // Online softmax state per M-row (log2 units): running max m_run, and the
+  // reference r_ref that the score accumulators start from (-r_ref), so that
+  // a tile's accumulators hold score - r_ref and its weights are exp2 of them
+  // directly.  r_ref follows m_run once the row has seen an unmasked key (0
+  // before).  The row sums are one more output tile, lsum: the matrix cores
+  // multiply the bf16 weights by an all-ones V^T tile, so every lane holds
+  // its own row's sum of exactly the weights the products used.
   float m_run[2] = {-FLT_MAX, -FLT_MAX};
-  float l_run[2] = {0.f, 0.f};
+  floatx4_t lsum[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
   float r_ref[2] = {0.f, 0.f};
   floatx4_t negr[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
   floatx4_t o[C::kDTiles][2];
@@ -282,14 +285,21 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       const int tok0 = rt * T + x * kRowsX + wave * kRowsW;       // wavefront's first row
       const int blk = min(tok0, L - 1) / kBlockTokens;
       const int phys = ph[x];
-      const int64_t boff = phys * blk_stride + head_off;
       unsigned off = voff[x];
       if (tail)
         off = static_cast<unsigned>((min(tok0 + lane_row, L - 1) - blk * kBlockTokens) * kRowBytes) + col_off[x];
       const unsigned dst = lds_addr32(kd) + (x * (kWaves * kWave) + wave * kWave) * 16;
       const unsigned dstv = lds_addr32(vd) + (x * (kWaves * kWave) + wave * kWave) * 16;
-      const char *gk = kbase + boff;
-      const char *gv = vbase + boff;
+      const char *gk, *gv;
+      if constexpr (OFF32) {
+        off += static_cast<unsigned>(phys) * static_cast<unsigned>(blk_stride) + static_cast<unsigned>(head_off);
+        gk = kbase;
+        gv = vbase;
+      } else {
+        const int64_t boff = phys * blk_stride + head_off;
+        gk = kbase + boff;
+        gv = vbase + boff;
+      }
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 " PKV_CHUNK_DMA_HINT ::"s"(dst), "v"(off),
                    "s"(gk)
                    : "memory");
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       for (int qt = 0; qt < 2; ++qt) {
         const float alpha = fast_exp2(m_run[qt] - mnew[qt]);
         m_run[qt] = mnew[qt];
-        l_run[qt] *= alpha;
+        lsum[qt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt) o[dt][qt] *= alpha;
         const float nr = mnew[qt] > -FLT_MAX ? mnew[qt] : r_ref[qt];
@@ -413,7 +423,6 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       nxt[tt][0] = negr[0];
       nxt[tt][1] = negr[1];
     }
-    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
     // The first kLead steps are weights only, covering the operand reads.
     constexpr int kLead = 2;
     constexpr int kPairs = kTT * C::kKSteps;
@@ -438,15 +447,6 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
           pb[ks][qt] = bf16x8_t{static_cast<__bf16>(q8[0]), static_cast<__bf16>(q8[1]), static_cast<__bf16>(q8[2]),
                                 static_cast<__bf16>(q8[3]), static_cast<__bf16>(q8[4]), static_cast<__bf16>(q8[5]),
                                 static_cast<__bf16>(q8[6]), static_cast<__bf16>(q8[7])};
-          float l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 0, 1), ones,
-                                                     l_run[qt], false);
-          float l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 2, 3), ones,
-                                                     0.f, false);
-          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 4, 5), ones, l0,
-                                               false);
-          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks][qt], pb[ks][qt], 6, 7), ones, l1,
-                                               false);
-          l_run[qt] = l0 + l1;
         }
       }
       if constexpr (PKV_CHUNK_INTERLEAVE) __builtin_amdgcn_sched_barrier(0);
@@ -458,14 +458,23 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   auto phase_b = [&](const bf16x8_t(&pb)[kKS][2], bf16x8_t(&va)[C::kDTiles][kKS], int st,
                      const floatx4_t(&nxt)[kTT][2], float(&mnew)[2]) {
     if constexpr (!Ring<D>::kEarlyV) load_v(st, va);
-    constexpr int kPairs = C::kDTiles * kKS;
+    // the last kKS pairs are the row sums (all-ones V^T operand)
+    constexpr int kPairs = C::kDTiles * kKS + kKS;
     constexpr int kItems = 2 * kTT;
+    const bf16x8_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f), static_cast<__bf16>(1.f),
+                           static_cast<__bf16>(1.f), static_cast<__bf16>(1.f), static_cast<__bf16>(1.f),
+                           static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
     float acc[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
       const int dt = i / kKS, ks = i % kKS;
-      o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][0], o[dt][0], 0, 0, 0);
-      o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][1], o[dt][1], 0, 0, 0);
+      if (dt < C::kDTiles) {
+        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][0], o[dt][0], 0, 0, 0);
+        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][1], o[dt][1], 0, 0, 0);
+      } else {
+        lsum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][0], lsum[0], 0, 0, 0);
+        lsum[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][1], lsum[1], 0, 0, 0);
+      }
 #pragma unroll
       for (int w = i * kItems / kPairs; w < (i + 1) * kItems / kPairs; ++w) {
         const int qt = w / kTT, tt = w % kTT;
@@ -564,13 +573,11 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain before the ring is reused
   }
 
-  // Row sums live spread over the 4 lane groups; combine, normalise, store
-  // (or store the unnormalised partial of this key range for the merge).
+  // Normalise and store (or store the unnormalised partial of this key range
+  // for the merge); every lane already holds its row's sum.
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    float lt = l_run[qt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lsum[qt][0];
     if (!valid[qt]) continue;
     if (partial_out) {
       const int m = mw + qt * 16 + l16;
@@ -702,10 +709,16 @@ int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, i
   if (bound <= 0) return PKV_OK;
   if (bound > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(bound)), block(kWaves * kWave);
-  if (head_dim == 128)
-    chunk_kernel<128><<<grid, block, 0, stream>>>(a, G);
-  else
-    chunk_kernel<64><<<grid, block, 0, stream>>>(a, G);
+  const uint64_t tensor_bytes =
+      static_cast<uint64_t>(a.num_blocks) * a.num_kv_heads * kBlockTokens * head_dim * 2;   // bf16
+  const bool off32 = tensor_bytes <= 0xFFFFFFFFull;
+  if (head_dim == 128) {
+    if (off32) chunk_kernel<128, true><<<grid, block, 0, stream>>>(a, G);
+    else chunk_kernel<128, false><<<grid, block, 0, stream>>>(a, G);
+  } else {
+    if (off32) chunk_kernel<64, true><<<grid, block, 0, stream>>>(a, G);
+    else chunk_kernel<64, false><<<grid, block, 0, stream>>>(a, G);
+  }
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   if (a.chunk_part == nullptr) return PKV_OK;
   // Merge: at most total_q * G M-rows in split segments, padded to whole

@@ -204,6 +204,26 @@ def test_block_permutation_invariance_bitwise(gpu_available):
     assert torch.equal(o1[0][0].cpu(), o2[0][0].cpu())
 
 
+def test_pool_beyond_4gib_bitwise(gpu_available):
+    """Pool tensors over 4 GiB with every block of the step allocated above
+    the 4 GiB mark give bitwise the outputs of a small pool: the chunk
+    kernel's 64-bit tile addressing (used only for such pools) against its
+    32-bit form, and the decode path's addressing at large offsets."""
+    import copy
+    import torch
+    w = make_custom([(0, 500, 200), (1, 3000, 1), (2, 100, 64), (3, 2000, 16)], dtype="bf16", hq=32, hkv=8,
+                    d=64, seed=73)
+    _, small = _run_gpu(w, fused=True)
+    big = copy.copy(w)
+    big.num_blocks = 300_000       # 300K blocks x 8 heads x 16 x 64 x 2 B = 4.9 GB per tensor
+    order = np.arange(big.num_blocks - 1, -1, -1, dtype=np.int32)    # highest blocks first
+    eng, large = _run_gpu(big, free_order=order, fused=True)
+    assert eng.pool.k.numel() * eng.pool.k.element_size() > 2 ** 32
+    assert torch.equal(small[0][0].cpu(), large[0][0].cpu())
+    del eng, large
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
 def test_slot_reuse_leaves_other_slots_bitwise_unchanged(fused, gpu_available):
     """Config 5: after slot 3 is released and its blocks reused by a new

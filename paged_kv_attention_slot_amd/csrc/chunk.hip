@@ -103,7 +103,8 @@ __device__ __forceinline__ ChunkShape chunk_shape(int n, int L, int G) {
   const int kv_tiles = (L + kKV - 1) / kKV;
   constexpr int kRT = chunk_split_row_tiles(D);
   int splits = c.mtiles >= kRT ? 1 : kRT / c.mtiles;
-  splits = max(1, min(splits, (kv_tiles + 1) / 2));   // at least two K/V tiles per range
+  constexpr int kMin = PKV_CHUNK_MIN_TILES_PER_SPLIT;
+  splits = max(1, min(splits, (kv_tiles + kMin - 1) / kMin));   // at least kMin K/V tiles per range
   c.tps = (kv_tiles + splits - 1) / splits;
   c.splits = (kv_tiles + c.tps - 1) / c.tps;
   return c;

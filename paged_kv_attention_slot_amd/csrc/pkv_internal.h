@@ -83,6 +83,10 @@ constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 // Multi-row segments with fewer than this many 128-row tiles split their
 // key range so that (row tiles x splits) reaches it; partial slots per
 // (segment, KV head) = that target * 128 (chunk_split_slots).
+// Fewest 64-token K/V tiles per key range of a split segment.
+#ifndef PKV_CHUNK_MIN_TILES_PER_SPLIT
+#define PKV_CHUNK_MIN_TILES_PER_SPLIT 6
+#endif
 #ifndef PKV_CHUNK_SPLIT_ROW_TILES_D64
 #define PKV_CHUNK_SPLIT_ROW_TILES_D64 64
 #endif

@@ -34,11 +34,13 @@ bool multirow_on_decode_path(int32_t dtype, int32_t head_dim, int32_t group, int
 }
 
 struct WorkspaceLayout {
-  int64_t rows = 0, part_max = 0;
-  size_t acc_bytes = 0, ml_bytes = 0, chunk_bytes = 0;
+  int64_t rows = 0, part_max = 0, verify_rows = 0;
+  size_t acc_bytes = 0, ml_bytes = 0, chunk_bytes = 0, vacc_bytes = 0, vml_bytes = 0;
   size_t decode_bytes() const { return acc_bytes + ml_bytes; }
-  size_t total() const { return acc_bytes + ml_bytes + chunk_bytes; }
+  size_t total() const { return acc_bytes + ml_bytes + chunk_bytes + vacc_bytes + vml_bytes; }
 };
+
+size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_query_len, int32_t max_context_len, int32_t dtype, int32_t group) {
@@ -58,7 +60,15 @@ WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t 
   if (max_query_len > 1 && !multirow && group > 0) {
     // key-range partials of split multi-row segments (see chunk.hip)
     const int64_t kv_heads = num_q_heads / group;
-    w.chunk_bytes = static_cast<size_t>(num_segments) * kv_heads * chunk_split_slots(head_dim) * (head_dim + 4) * sizeof(float);
+    w.chunk_bytes = align256(static_cast<size_t>(num_segments) * kv_heads * chunk_split_slots(head_dim) *
+                             (head_dim + 4) * sizeof(float));
+    // partition partials of the rows of verify segments (see verify.hip)
+    if (w.part_max > 1) {
+      w.verify_rows = verify_rows_cap(group, head_dim);
+      const int64_t n = static_cast<int64_t>(num_segments) * w.verify_rows * num_q_heads * w.part_max;
+      w.vacc_bytes = align256(static_cast<size_t>(n) * head_dim * sizeof(float));
+      w.vml_bytes = align256(static_cast<size_t>(n) * 2 * sizeof(float));
+    }
   }
   return w;
 }
@@ -72,6 +82,8 @@ struct StepFacts {
   int32_t chunk_segments = 0;      // segments with query_len > 1
   int32_t max_decode_context = 0;  // longest context among the decode rows
   int64_t decode_parts = 0;        // split-context partitions over the decode rows
+  int32_t verify_segments = 0;     // multi-row segments on the verify kernel
+  int32_t max_verify_context = 0;  // longest context among them
 };
 
 // Per-device auxiliary stream (default priority) and fork/join events that
@@ -179,10 +191,17 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
         f.decode_parts += L > 0 ? (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens : 1;
       }
     } else if (hq[b] > 1) {
-      ++f.chunk_segments;
+      if (verify_segment(hq[b], d->num_q_heads / pool->num_kv_heads, pool->head_dim)) {
+        ++f.verify_segments;
+        if (hs[b] >= 0 && hs[b] < d->num_slots && hl[hs[b]] > f.max_verify_context)
+          f.max_verify_context = hl[hs[b]];
+      } else {
+        ++f.chunk_segments;
+      }
     }
   }
   if (f.max_decode_context > d->max_context_len) f.max_decode_context = d->max_context_len;
+  if (f.max_verify_context > d->max_context_len) f.max_verify_context = d->max_context_len;
   const int32_t *m = d->dev_meta;
   return attend(d->q_packed, d->total_q, d->num_q_heads, m + d->row_to_slot_off, m + d->query_start_off,
                 m + d->query_len_off, d->num_segments, m + d->context_lens_off, d->block_tables, d->num_slots,
@@ -229,8 +248,13 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   a.block_tables = block_tables;
   a.part_acc = ws.decode_bytes() ? static_cast<float *>(workspace) : nullptr;
   a.part_ml = ws.decode_bytes() ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.acc_bytes) : nullptr;
-  a.chunk_part =
-      ws.chunk_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.decode_bytes()) : nullptr;
+  char *wsb = static_cast<char *>(workspace);
+  a.chunk_part = ws.chunk_bytes ? reinterpret_cast<float *>(wsb + ws.decode_bytes()) : nullptr;
+  a.verify_acc =
+      ws.vacc_bytes ? reinterpret_cast<float *>(wsb + ws.decode_bytes() + ws.chunk_bytes) : nullptr;
+  a.verify_ml =
+      ws.vml_bytes ? reinterpret_cast<float *>(wsb + ws.decode_bytes() + ws.chunk_bytes + ws.vacc_bytes) : nullptr;
+  a.verify_rows = static_cast<int32_t>(ws.verify_rows);
   a.num_segments = num_segments;
   a.num_slots = num_slots;
   a.max_blocks = max_blocks_per_seq;
@@ -244,22 +268,36 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
 
-  // Multi-row segments on the chunk kernels (unless they go row by row on
-  // the decode path); decode rows on the decode kernels, whose grid and
-  // partition reduce follow the decode rows' own longest context when the
-  // host knows it.
-  const bool run_chunk = max_query_len > 1 && !multirow && (!facts.known || facts.chunk_segments > 0);
+  // Multi-row segments on the chunk kernels, or on the verify kernel when
+  // short (unless every multi-row segment goes row by row on the decode
+  // path); decode rows on the decode kernels, whose grid and partition
+  // reduce follow the decode rows' own longest context when the host knows
+  // it.  Chunk work is matrix-bound, decode and verify work HBM-bound: when
+  // the host knows a step has both kinds, the HBM-bound kernels run on the
+  // auxiliary stream beside the chunk kernels.
+  const bool multi = max_query_len > 1 && !multirow;
+  const bool run_chunk = multi && (!facts.known || facts.chunk_segments > 0);
+  const bool run_verify = multi && (!facts.known || facts.verify_segments > 0);
   const bool run_decode = !facts.known || multirow || facts.decode_rows > 0;
   const int32_t decode_ctx = facts.known && !multirow ? facts.max_decode_context : max_context_len;
   const bool need_reduce = decode_ctx > kDecodePartitionTokens;
+  const int32_t verify_ctx = facts.known ? facts.max_verify_context : max_context_len;
+  const bool need_merge = verify_ctx > kVerifyPartitionTokens;
   const int64_t work_waves = facts.known && !multirow ? facts.decode_parts * pool->num_kv_heads : -1;
-  if (run_chunk && run_decode && facts.known && PKV_CONCURRENT_DECODE) {
+  auto launch_streaming = [&](hipStream_t st) {
+    int r = PKV_OK;
+    if (run_verify) r = launch_verify(a, pool->head_dim, verify_ctx, need_merge, st);
+    if (r == PKV_OK && run_decode)
+      r = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, st);
+    return r;
+  };
+  if (run_chunk && (run_decode || run_verify) && facts.known && PKV_CONCURRENT_DECODE) {
     std::lock_guard<std::mutex> lock(g_aux_mutex);
     AuxStream *ax = aux_for_current_device();
     if (ax) {
       if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
         return PKV_ERR_HIP;
-      const int sd = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, ax->stream);
+      const int sd = launch_streaming(ax->stream);
       // the join is recorded even after a failed launch, so `s` never waits
       // on a stale event
       if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PKV_ERR_HIP;
@@ -272,7 +310,7 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
     const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, s);
     if (st != PKV_OK) return st;
   }
-  return run_decode ? launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, s) : PKV_OK;
+  return launch_streaming(s);
 }
 
 }  // namespace

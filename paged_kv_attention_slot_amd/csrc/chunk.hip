@@ -113,7 +113,7 @@ __device__ __forceinline__ ChunkShape chunk_shape(int n, int L, int G) {
 template <int D>
 __device__ __forceinline__ int chunk_units(const AttendArgs &a, int b, int G) {
   const SegInfo s = seg_info(a, b);
-  if (!s.ok || s.n < 2) return 0;
+  if (!s.ok || s.n < 2 || verify_segment(s.n, G, D)) return 0;
   const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.mtiles * c.splits;
 }
@@ -618,7 +618,7 @@ constexpr int kMergeWaves = 4;
 template <int D>
 __device__ __forceinline__ int merge_units(const AttendArgs &a, int b, int G) {
   const SegInfo s = seg_info(a, b);
-  if (!s.ok || s.n < 2) return 0;
+  if (!s.ok || s.n < 2 || verify_segment(s.n, G, D)) return 0;
   const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.splits > 1 ? (s.n * G + kMergeRowsPerWave - 1) / kMergeRowsPerWave : 0;
 }

@@ -83,6 +83,44 @@ constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 // Multi-row segments with fewer than this many 128-row tiles split their
 // key range so that (row tiles x splits) reaches it; partial slots per
 // (segment, KV head) = that target * 128 (chunk_split_slots).
+// Multi-row segments whose (query row, head) pairs fit one verify
+// wavefront (verify_col_tiles 16-wide MFMA column tiles) go to the streaming
+// verify kernel (short speculative drafts); longer ones to the chunk kernel.
+// The choice depends only on the segment's own (n, G) and the head dim.
+// PKV_VERIFY_MAX_PAIRS, when set, lowers the limit (0 turns the path off).
+// The column groups of a verify partition read the same tiles: loaded with
+// default caching (later groups hit in L2) unless PKV_VERIFY_STREAM_LOADS.
+#ifndef PKV_VERIFY_STREAM_LOADS
+#define PKV_VERIFY_STREAM_LOADS 0
+#endif
+#if PKV_VERIFY_STREAM_LOADS
+#define PKV_VERIFY_DMA_HINT "nt"
+#else
+#define PKV_VERIFY_DMA_HINT ""
+#endif
+#ifndef PKV_VERIFY_STAGES
+#define PKV_VERIFY_STAGES 3
+#endif
+#ifndef PKV_VERIFY_RESCALE_SLACK
+#define PKV_VERIFY_RESCALE_SLACK 8.0f
+#endif
+#ifndef PKV_VERIFY_MAX_PAIRS
+#define PKV_VERIFY_MAX_PAIRS 1024
+#endif
+constexpr int kVerifyPartitionTokens = PKV_DECODE_PARTITION_TOKENS;
+// 16-wide (row, head) pair tiles per verify wavefront (register budget).
+__host__ __device__ constexpr int verify_col_tiles(int head_dim) { return head_dim == 64 ? 3 : 2; }
+__host__ __device__ constexpr int verify_max_pairs(int head_dim) {
+  return verify_col_tiles(head_dim) * 16 < PKV_VERIFY_MAX_PAIRS ? verify_col_tiles(head_dim) * 16
+                                                                 : PKV_VERIFY_MAX_PAIRS;
+}
+__host__ __device__ constexpr bool verify_segment(int n, int G, int head_dim) {
+  return n > 1 && n * G <= verify_max_pairs(head_dim);
+}
+__host__ __device__ constexpr int verify_rows_cap(int G, int head_dim) {
+  return G > 0 ? verify_max_pairs(head_dim) / G : 0;
+}
+
 // Fewest 64-token K/V tiles per key range of a split segment.
 #ifndef PKV_CHUNK_MIN_TILES_PER_SPLIT
 #define PKV_CHUNK_MIN_TILES_PER_SPLIT 6
@@ -153,6 +191,9 @@ struct AttendArgs {
   float *part_acc;   // [part_rows][Hq][part_max][D]
   float *part_ml;    // [part_rows][Hq][part_max][2]  (running max in log2 units, sum)
   float *chunk_part; // [num_segments][Hkv][chunk_split_slots(D)][D + 4]: key-range partials of split chunks
+  float *verify_acc; // [num_segments][verify_rows][Hq][part_max][D]: partition partials of verify rows
+  float *verify_ml;  // [num_segments][verify_rows][Hq][part_max][2]
+  int32_t verify_rows;  // row stride per segment of the verify partials (verify_rows_cap)
   int32_t num_segments;
   int32_t num_slots;
   int32_t max_blocks;
@@ -172,6 +213,11 @@ struct AttendArgs {
 int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
                      int32_t num_tokens, const pkv_pool &pool, hipStream_t stream,
                      const int32_t *stage_src = nullptr, int32_t *stage_dst = nullptr, int32_t stage_len = 0);
+
+// Short multi-row segments (verify_segment) on the streaming verify kernel,
+// plus the merge of their partitions when `need_merge`.
+int launch_verify(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, bool need_merge,
+                  hipStream_t stream);
 
 // Decode path (one query row per work item; split-context partitions) and,
 // when `need_reduce` (some row has more than one partition), the partition

@@ -118,6 +118,7 @@ EDGE_SEQS = [
     [(5, 3000, 1), (2, 7, 1)],                    # slots out of order
     [(0, 0, 5), (1, 40, 1), (2, 3, 2)],           # tiny prompt, decode, 2 drafts
     [(0, 700, 16), (1, 3000, 3), (2, 200, 40), (3, 1300, 1)],   # key-range splits of short segments
+    [(0, 2500, 2), (1, 510, 3), (2, 40, 4), (3, 1021, 4)],     # short drafts whose rows straddle partitions
 ]
 
 

@@ -107,13 +107,16 @@ def run_mixed(args, w, pk, torch, dev):
     dec_lens = [L for s, L in zip(st.segments, lens) if s.n == 1]
     kv, alg = decode_bytes(w, dec_lens, w.elem_bytes)
     fl = chunk_flops(w, st.segments, lens)
+    # K and V of every cached token of the multi-row segments, once
+    mr_kv = sum(2 * L * w.num_kv_heads * w.head_dim * w.elem_bytes for seg, L in zip(st.segments, lens) if seg.n > 1)
     return {"metric": f"mixed-step latency, config {w.name}", "value": round(wall / args.steps * 1e3, 4),
             "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(wall / args.steps * 1e3, 4), "step_gpu_ms_avg": round(att * 1e3, 4),
             "dtype": w.dtype, "data": "synthetic",
             "config": {"workload": f"config {w.name}: {w.description}", "decode_rows": len(dec_lens),
                        "chunk_rows": int(sum(s.n for s in st.segments if s.n > 1))},
-            "decode_kv_bytes": kv, "chunk_causal_flops": fl,
+            "decode_kv_bytes": kv, "chunk_causal_flops": fl, "multi_row_kv_bytes": mr_kv,
+            "step_kv_gbs": round((kv + mr_kv) / att / 1e9, 1),
             "step_tflops_if_all_chunk": round(fl / att / 1e12, 2),
             "roofline_step_ms": round((alg / HBM_PEAK_GBS / 1e9 + fl / BF16_PEAK_TFLOPS / 1e12) * 1e3, 4)}
 

@@ -8,11 +8,12 @@
 // is n * G (row, head) pairs sharing every K/V token: few enough pairs that
 // the work is bound by reading the cache, not by the matrix cores.
 //
-// The segment's pairs m = i * G + h (at most verify_max_pairs(D): one column
-// group of verify_col_tiles(D) 16-wide MFMA tiles, which measured faster than
-// splitting more pairs over several wavefronts that stream the same tiles);
-// one wavefront per (segment, KV head, 512-token partition, column group) streams the partition's 16-token K/V tiles through
-// its own direct-to-LDS ring (no workgroup barrier) and, per tile:
+// The segment's pairs m = i * G + h number at most verify_max_pairs(D): one
+// column group of verify_col_tiles(D) 16-wide MFMA tiles (faster, measured,
+// than spreading more pairs over several wavefronts that stream the same
+// tiles).  One wavefront per (segment, KV head, 512-token partition, column
+// group) streams the partition's 16-token K/V tiles through its own
+// direct-to-LDS ring (no workgroup barrier) and, per tile:
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the K operand read once and
 //     used for every column tile of the group;
 //   * the causal mask (row i sits at L - n + i) only on tiles reaching past

@@ -101,7 +101,7 @@ def test_kv_append_skips_out_of_pool_entries_and_empty(gpu_available):
 
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
-@pytest.mark.parametrize("name", ["1", "1+1", "3", "2", "4a", "4b", "5"])
+@pytest.mark.parametrize("name", ["1", "1+1", "3", "3v", "2", "4a", "4b", "5"])
 def test_attention_matches_oracle(name, fused, gpu_available):
     _log(f"attention config {name} fused={fused}")
     w = _workload(name)

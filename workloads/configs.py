@@ -159,6 +159,19 @@ def _config3():
                   description="64 decode rows, lognormal context (median 2048), slots from 0..127")
 
 
+def _config3v():
+    """Config 3's sequences (same seed, lengths and slots), each verifying 2
+    speculative draft rows in this step instead of decoding one token: the
+    short multi-row segments of a multi-token-prediction verify step."""
+    draw = _Draw(1003, "bf16")
+    z = draw.rng.standard_normal(64)
+    lens = np.clip(np.round(np.exp(math.log(2048.0) + 1.0 * z)), 16, 32768).astype(np.int64)
+    slots = draw.rng.choice(128, size=64, replace=False)
+    seqs = [(int(s), max(int(L) - 2, 0), 2) for s, L in zip(slots, lens)]
+    return _build("3v", 1003, "bf16", 32, 8, 128, 16, seqs, max_slots=128, draw=draw,
+                  description="64 sequences x 2 draft rows (verify), lognormal context (median 2048)")
+
+
 def _config4(chunk):
     draw = _Draw(1004, "bf16")
     if chunk == 2048:
@@ -211,6 +224,8 @@ def make_workload(name: str) -> Workload:
         return _config2()
     if name == "3":
         return _config3()
+    if name == "3v":
+        return _config3v()
     if name == "4a":
         return _config4(2048)
     if name == "4b":

@@ -84,6 +84,8 @@ struct StepFacts {
   int64_t decode_parts = 0;        // split-context partitions over the decode rows
   int32_t verify_segments = 0;     // multi-row segments on the verify kernel
   int32_t max_verify_context = 0;  // longest context among them
+  int32_t max_verify_pairs = 0;    // largest n * G among them
+  int64_t verify_parts = 0;        // their partitions
 };
 
 // Per-device auxiliary stream (default priority) and fork/join events that
@@ -191,10 +193,15 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
         f.decode_parts += L > 0 ? (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens : 1;
       }
     } else if (hq[b] > 1) {
-      if (verify_segment(hq[b], d->num_q_heads / pool->num_kv_heads, pool->head_dim)) {
+      const int32_t G = d->num_q_heads / pool->num_kv_heads;
+      if (verify_segment(hq[b], G, pool->head_dim)) {
         ++f.verify_segments;
-        if (hs[b] >= 0 && hs[b] < d->num_slots && hl[hs[b]] > f.max_verify_context)
-          f.max_verify_context = hl[hs[b]];
+        if (hq[b] * G > f.max_verify_pairs) f.max_verify_pairs = hq[b] * G;
+        if (hs[b] >= 0 && hs[b] < d->num_slots) {
+          const int32_t L = hl[hs[b]];
+          if (L > f.max_verify_context) f.max_verify_context = L;
+          f.verify_parts += L > 0 ? (L + kVerifyPartitionTokens - 1) / kVerifyPartitionTokens : 1;
+        }
       } else {
         ++f.chunk_segments;
       }
@@ -286,7 +293,9 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   const int64_t work_waves = facts.known && !multirow ? facts.decode_parts * pool->num_kv_heads : -1;
   auto launch_streaming = [&](hipStream_t st) {
     int r = PKV_OK;
-    if (run_verify) r = launch_verify(a, pool->head_dim, verify_ctx, need_merge, st);
+    if (run_verify)
+      r = launch_verify(a, pool->head_dim, verify_ctx, need_merge, facts.known ? facts.max_verify_pairs : -1,
+                        facts.known ? facts.verify_parts * pool->num_kv_heads : -1, st);
     if (r == PKV_OK && run_decode)
       r = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, st);
     return r;

@@ -98,8 +98,10 @@ constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 #else
 #define PKV_VERIFY_DMA_HINT ""
 #endif
-#ifndef PKV_VERIFY_STAGES
-#define PKV_VERIFY_STAGES 3
+// Verify prefetch depth (tiles in flight per wavefront) for launches with
+// many wavefronts; launches with fewer than PKV_DECODE_FEW_WAVES take 3.
+#ifndef PKV_VERIFY_SHALLOW_STAGES
+#define PKV_VERIFY_SHALLOW_STAGES 2
 #endif
 #ifndef PKV_VERIFY_RESCALE_SLACK
 #define PKV_VERIFY_RESCALE_SLACK 8.0f
@@ -216,8 +218,11 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
 
 // Short multi-row segments (verify_segment) on the streaming verify kernel,
 // plus the merge of their partitions when `need_merge`.
+// `max_pairs` is the launch's largest segment's n * G and `work_waves` its
+// exact count of (segment, KV head, partition) items when the host knows
+// them, else -1: they pick the column tiles and prefetch depth per wavefront.
 int launch_verify(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, bool need_merge,
-                  hipStream_t stream);
+                  int32_t max_pairs, int64_t work_waves, hipStream_t stream);
 
 // Decode path (one query row per work item; split-context partitions) and,
 // when `need_reduce` (some row has more than one partition), the partition

@@ -65,27 +65,27 @@ struct VGeo {
 };
 
 constexpr int kVPT = kVerifyPartitionTokens;
-constexpr int kVStages = PKV_VERIFY_STAGES;
 
 __device__ __forceinline__ int vnum_parts(int L) { return (L + kVPT - 1) / kVPT; }
 
-template <int D>
+template <int NC>
 __device__ __forceinline__ int vgroups(int n, int G) {
-  constexpr int kPairs = verify_col_tiles(D) * 16;
-  return (n * G + kPairs - 1) / kPairs;
+  return (n * G + NC * 16 - 1) / (NC * 16);
 }
 
-template <int D>
+template <int D, int NC>
 __device__ __forceinline__ int verify_units(const AttendArgs &a, int b, int G) {
   const SegInfo s = seg_info(a, b);
-  return s.ok && verify_segment(s.n, G, D) ? vnum_parts(s.L) * vgroups<D>(s.n, G) : 0;
+  return s.ok && verify_segment(s.n, G, D) ? vnum_parts(s.L) * vgroups<NC>(s.n, G) : 0;
 }
 
-template <int D>
+// NC: 16-wide pair tiles per wavefront (the launch takes the fewest that hold
+// its largest segment); S: K/V tiles in flight per wavefront.  Neither
+// changes the arithmetic of any pair.
+template <int D, int NC, int S>
 __global__ __launch_bounds__(64, 2) void verify_kernel(AttendArgs a, int G) {
   using M = VGeo<D>;
-  constexpr int NC = verify_col_tiles(D);
-  constexpr int S = kVStages;
+  static_assert(NC >= 1 && NC <= verify_col_tiles(D) && S >= 1 && S <= 3, "verify geometry");
   __shared__ __align__(16) unsigned char kst[S][M::kTile];
   __shared__ __align__(16) unsigned char vst[S][M::kTile];
   const int lane = threadIdx.x;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64, 2) void verify_kernel(AttendArgs a, int G) {
   const int lg = lane >> 4;
   const float c_log2 = a.scale_log2;
 
-  auto units_fn = [&](int b) { return verify_units<D>(a, b, G); };
+  auto units_fn = [&](int b) { return verify_units<D, NC>(a, b, G); };
   const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
   const int64_t items = static_cast<int64_t>(total) * a.num_kv_heads;
 
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64, 2) void verify_kernel(AttendArgs a, int G) {
     u = __builtin_amdgcn_readfirstlane(u);
     const SegInfo si = seg_info_uniform(a, b);
     if (!si.ok) continue;
-    const int ngr = vgroups<D>(si.n, G);
+    const int ngr = vgroups<NC>(si.n, G);
     const int part = u / ngr;
     const int cg = u - part * ngr;
     const int np = vnum_parts(si.L);
@@ -371,19 +371,34 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(AttendArgs a, int G) {
 
 }  // namespace
 
+template <int D, int NC>
+void launch_verify_nc(const AttendArgs &a, int G, unsigned grid, bool deep, hipStream_t stream) {
+  if (deep) verify_kernel<D, NC, 3><<<dim3(grid), dim3(kWave), 0, stream>>>(a, G);
+  else verify_kernel<D, NC, PKV_VERIFY_SHALLOW_STAGES><<<dim3(grid), dim3(kWave), 0, stream>>>(a, G);
+}
+
 int launch_verify(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, bool need_merge,
-                  hipStream_t stream) {
+                  int32_t max_pairs, int64_t work_waves, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
+  const int nc_max = verify_col_tiles(head_dim);
+  int nc = max_pairs > 0 ? (max_pairs + 15) / 16 : nc_max;
+  nc = nc < 1 ? 1 : (nc > nc_max ? nc_max : nc);
   const int64_t parts = (static_cast<int64_t>(max_context_len) + kVPT - 1) / kVPT;
-  const int64_t groups = (verify_max_pairs(head_dim) + verify_col_tiles(head_dim) * 16 - 1) / (verify_col_tiles(head_dim) * 16);
+  const int64_t groups = (verify_max_pairs(head_dim) + nc * 16 - 1) / (nc * 16);
   const int64_t items_bound = static_cast<int64_t>(a.num_segments) * (parts > 0 ? parts : 1) * groups * a.num_kv_heads;
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * kDecodeWavesPerCU;
   const int64_t grid = items_bound < cap ? items_bound : cap;
   if (grid <= 0) return PKV_OK;
-  if (head_dim == 128)
-    verify_kernel<128><<<dim3(static_cast<unsigned>(grid)), dim3(kWave), 0, stream>>>(a, G);
-  else
-    verify_kernel<64><<<dim3(static_cast<unsigned>(grid)), dim3(kWave), 0, stream>>>(a, G);
+  const bool deep = work_waves >= 0 && work_waves < PKV_DECODE_FEW_WAVES;
+  const unsigned g = static_cast<unsigned>(grid);
+  if (head_dim == 128) {
+    if (nc == 1) launch_verify_nc<128, 1>(a, G, g, deep, stream);
+    else launch_verify_nc<128, 2>(a, G, g, deep, stream);
+  } else {
+    if (nc == 1) launch_verify_nc<64, 1>(a, G, g, deep, stream);
+    else if (nc == 2) launch_verify_nc<64, 2>(a, G, g, deep, stream);
+    else launch_verify_nc<64, 3>(a, G, g, deep, stream);
+  }
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   if (!need_merge || a.verify_acc == nullptr || a.part_max <= 1) return PKV_OK;
   const int64_t mgrid = static_cast<int64_t>(a.num_segments) * a.num_q_heads * a.verify_rows;

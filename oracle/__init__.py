@@ -9,7 +9,10 @@ What it computes, in plain numpy (fp64 for all floating point):
     slots, per-slot block tables, atomic reservation and LIFO reuse, and the
     lowering of one step into slot_mapping / query_start / query_len /
     row_to_slot / context_lens / block_tables;
+  * block_pool.BlockPool.adopt and the copy-on-write pairs of lower_step -
+    shared prompt-prefix blocks with reference counts;
   * attention.append_reference - the KV append scatter (a byte copy);
+  * attention.copy_blocks_reference - the copy-on-write block copy;
   * attention.paged_attention  - walks each block table in logical
     order, materialises that sequence's contiguous K/V, and computes causal
     softmax attention in fp64.
@@ -27,6 +30,7 @@ block-table example).  No function here is "parity unpinned".
 from .block_pool import BlockPool, NoSpace, pool_blocks_for_tokens  # noqa: F401
 from .attention import (  # noqa: F401
     append_reference,
+    copy_blocks_reference,
     decode_values,
     gather_sequence,
     paged_attention,

@@ -57,6 +57,18 @@ def append_reference(pool_k, pool_v, slot_mapping, k_new, v_new, block_size):
     return k, v
 
 
+def copy_blocks_reference(pool_k, pool_v, copy_src, copy_dst):
+    """Copy-on-write (mlxcel user guide "연속 배칭" §Paged KV 캐시와 프리픽스
+    공유): block copy_dst[c] receives all of block copy_src[c], K and V, every
+    head and position.  Returns new arrays; a pure copy of element bits."""
+    k = pool_k.copy()
+    v = pool_v.copy()
+    for src, dst in zip(np.asarray(copy_src).tolist(), np.asarray(copy_dst).tolist()):
+        k[dst] = pool_k[src]
+        v[dst] = pool_v[src]
+    return k, v
+
+
 def gather_sequence(pool, block_table, num_tokens, block_size):
     """Visit the first ceil(L / block_size) entries of the block table in
     logical order and return the sequence's first L tokens as [L][Hkv][D]."""

@@ -3,7 +3,8 @@
 The step order follows "Continuous batching: Qwen3.8-27B at 301 tok/s ..."
 (lucebox blog) §Chunked prefill is a slot phase: the step's tokens are
 appended to each slot's paged KV, then every packed row attends over its
-slot's history.  The pool starts filled with NaN so that any read of an
+slot's history.  Copy-on-write block copies (mlxcel user guide "연속 배칭"
+§Paged KV 캐시와 프리픽스 공유) run before the append.  The pool starts filled with NaN so that any read of an
 unwritten position shows up in the result.
 """
 from __future__ import annotations
@@ -11,7 +12,7 @@ from __future__ import annotations
 import numpy as np
 
 from .block_pool import BlockPool
-from .attention import append_reference, paged_attention
+from .attention import append_reference, copy_blocks_reference, paged_attention
 
 NAN_BITS = {"f32": (np.uint32, 0x7FC00000, np.float32), "bf16": (np.uint16, 0x7FC0, np.uint16)}
 
@@ -30,6 +31,8 @@ def apply_ops(pool: BlockPool, ops):
             pool.release(op[1])
         elif op[0] == "truncate":
             pool.truncate(op[1], op[2])
+        elif op[0] == "adopt":
+            pool.adopt(op[1], op[2], op[3])
         else:
             raise ValueError(op)
 
@@ -58,6 +61,7 @@ def run_workload(w, steps=None):
             break
         apply_ops(alloc, st.ops)
         meta = alloc.lower_step([(s.slot, s.n) for s in st.segments])
+        pk, pv = copy_blocks_reference(pk, pv, meta["copy_src"], meta["copy_dst"])
         pk, pv = append_reference(pk, pv, meta["slot_mapping"], st.k_new, st.v_new, w.block_size)
         out = paged_attention(st.q, pk, pv, w.dtype, w.block_size, meta["block_tables"],
                               meta["context_lens"], meta["row_to_slot"], meta["query_start"],

@@ -425,3 +425,157 @@ def test_planted_mistakes_are_caught():
     orig_attend = pa.attend_rows
     assert _pins_fail(pa, "attend_rows", lambda q, k, v, s, p: orig_attend(q, k, v, 1.0, p))  # scale dropped
     assert _pins_fail(pa, "attend_rows", lambda q, k, v, s, p: orig_attend(q, v, k, s, p))    # K/V swapped
+
+
+# --------------------------------------------------------------- shared prefixes
+def _assert_refcounts(pool: BlockPool):
+    """Brute-force recount: a block's count is the number of tables holding it,
+    and the free list is exactly the blocks no table holds, each once."""
+    counts = [0] * pool.num_blocks
+    for table in pool.tables.values():
+        for b in table:
+            counts[b] += 1
+    assert counts == pool.refs
+    assert sorted(pool.free) == [b for b in range(pool.num_blocks) if counts[b] == 0]
+
+
+def _golden_saving():
+    vals = {}
+    with open(os.path.join(GOLDEN, "prefix_sharing_saving.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = int(v)
+    return vals
+
+
+def test_prefix_sharing_saving_matches_worked_example():
+    """The page's 8 requests over a 1024-token prefix: adopting stores the
+    prefix blocks once; the blocks not stored, at the page's KV bytes per
+    token, give its 784 MiB."""
+    g = _golden_saving()
+    n, p, bs = g["requests"], g["prefix_tokens"], 16
+    used = {}
+    for adopt in (False, True):
+        pool = BlockPool(n * p // bs + 8, bs, n, p // bs + 1)
+        for s in range(n):
+            pool.acquire(s)
+        if adopt:
+            pool.lower_step([(0, p)])
+            for s in range(1, n):
+                pool.adopt(s, 0, p)
+        else:
+            pool.lower_step([(s, p) for s in range(n)])
+        _assert_refcounts(pool)
+        used[adopt] = pool.num_blocks - pool.free_count()
+        # every request then decodes one token; a block-aligned prefix needs no copy
+        meta = pool.lower_step([(s, 1) for s in range(n)])
+        assert len(meta["copy_src"]) == 0
+        _assert_refcounts(pool)
+    saved_tokens = (used[False] - used[True]) * bs
+    assert saved_tokens == (n - 1) * p
+    assert saved_tokens * g["kib_per_token"] / 1024 == g["saved_mib"]
+
+
+def test_prefix_adoption_decodes_like_cold_bitwise():
+    """An adopting request's outputs equal a cold prefill's, bit for bit, over
+    three steps (suffix chunks that diverge inside the shared partial block,
+    decodes, and the donor's release); the prefix is stored once."""
+    wa, wc = make_workload("prefix"), make_workload("prefix-cold")
+    ra, _ = run_workload(wa)
+    rc, _ = run_workload(wc)
+    assert len(ra) == len(rc) == 3
+    for a, c in zip(ra, rc):
+        assert np.isfinite(a["out"]).all()
+        assert np.array_equal(a["out"], c["out"])
+    # slots 0..6 copy the shared partial block; slot 7, last to write, then
+    # holds it alone and writes in place
+    assert len(ra[0]["meta"]["copy_src"]) == 7 and len(rc[0]["meta"]["copy_src"]) == 0
+    assert len(set(ra[0]["meta"]["copy_dst"].tolist())) == 7
+    assert all(len(r["meta"]["copy_src"]) == 0 for r in ra[1:] + rc)
+
+
+def test_shared_blocks_are_never_written():
+    """Random slot lifecycles with adoption: after every lowering, no token
+    of the step lands in a block that two tables hold, and the reference
+    counts match a brute-force recount."""
+    rng = np.random.default_rng(5)
+    nb, bs, slots, maxb = 80, 16, 6, 10
+    pool = BlockPool(nb, bs, slots, maxb, rng.permutation(nb))
+    live = set()
+    copies = 0
+    both = [0]
+    for _ in range(400):
+        kind = int(rng.integers(0, 5))
+        if kind == 0 and len(live) < slots:
+            s = int(rng.choice([x for x in range(slots) if x not in live]))
+            pool.acquire(s)
+            donors = [x for x in live if pool.lengths[x] > 0]
+            live.add(s)
+            if donors and rng.random() < 0.8:
+                src = int(rng.choice(donors))
+                pool.adopt(s, src, int(rng.integers(0, pool.lengths[src] + 1)))
+        elif kind == 1 and live:
+            s = int(rng.choice(sorted(live)))
+            pool.release(s)
+            live.discard(s)
+        elif kind == 2 and live:
+            s = int(rng.choice(sorted(live)))
+            pool.truncate(s, int(rng.integers(0, pool.lengths[s] + 1)))
+        elif live:
+            ent = [(s, int(rng.integers(1, 20))) for s in sorted(live)
+                   if pool.lengths[s] + 20 <= maxb * bs and rng.random() < 0.7]
+            if not ent:
+                continue
+            try:
+                meta = pool.lower_step(ent)
+            except NoSpace:
+                continue
+            copies += len(meta["copy_src"])
+            written = set((meta["slot_mapping"] // bs).tolist())
+            assert all(pool.refs[b] == 1 for b in written)
+            # a copy source may still be written in this step by its last
+            # holder (two writers shared it; the first copied it out), which
+            # is why the copies run before the append
+            both[0] += bool(written & set(meta["copy_src"].tolist()))
+        _assert_refcounts(pool)
+    assert copies > 10
+
+
+def _prefix_pins_fail(patch):
+    """Run the adopting workload with one planted mistake; True when the
+    adopted outputs no longer equal the cold run's."""
+    wa, wc = make_workload("prefix"), make_workload("prefix-cold")
+    rc, _ = run_workload(wc)
+    undo = patch()
+    try:
+        ra, _ = run_workload(wa)
+    except (IndexError, ValueError, KeyError):
+        return True
+    finally:
+        undo()
+    return not all(np.array_equal(a["out"], c["out"]) for a, c in zip(ra, rc))
+
+
+def test_planted_prefix_mistakes_are_caught():
+    import oracle.step as ostep
+
+    def swap(obj, name, bad):
+        def apply():
+            orig = getattr(obj, name)
+            setattr(obj, name, bad)
+            return lambda: setattr(obj, name, orig)
+        return apply
+
+    # the copy-on-write copy skipped: adopters read the fresh block's poison
+    assert _prefix_pins_fail(swap(ostep, "copy_blocks_reference", lambda k, v, s, d: (k, v)))
+    # no copy-on-write at all: adopters write into the shared block
+    assert _prefix_pins_fail(swap(BlockPool, "_shared_write_index", lambda self, slot: None))
+    # adoption sharing one block too few (floor instead of ceil)
+    orig_adopt = BlockPool.adopt
+
+    def short_adopt(self, slot, src, n):
+        orig_adopt(self, slot, src, n)
+        b = self.tables[slot].pop()
+        self.refs[b] -= 1
+    assert _prefix_pins_fail(swap(BlockPool, "adopt", short_adopt))

@@ -11,6 +11,7 @@ from .configs import (  # noqa: F401
     Step,
     Workload,
     bf16_bits_from_f32,
+    make_prefix_share,
     make_workload,
     make_custom,
 )

@@ -47,8 +47,9 @@ class Segment:
 @dataclass
 class Step:
     """One scheduler step.  `ops` are slot lifecycle events applied before the
-    step: ("acquire", slot), ("release", slot) or ("truncate", slot, new_len)
-    (speculative drafts rejected).  Slots named in Workload.history are
+    step: ("acquire", slot), ("release", slot), ("truncate", slot, new_len)
+    (speculative drafts rejected) or ("adopt", slot, src_slot, num_tokens)
+    (an empty slot shares src_slot's first num_tokens tokens).  Slots named in Workload.history are
     acquired when the history is placed, before the first step.  `k_new`/`v_new` are [T][Hkv][D] and `q` is
     [T][Hq][D], packed in segment order."""
     ops: list
@@ -215,6 +216,61 @@ def _config5():
     return w
 
 
+def make_prefix_share(cold=False, *, dtype="bf16", hq=16, hkv=8, d=128, prefix=1000,
+                      suffixes=(1, 5, 24, 1, 50, 16, 2, 9), seed=1010):
+    """Eight requests with one shared prompt prefix (mlxcel user guide "연속
+    배칭" §Paged KV 캐시와 프리픽스 공유: 8 requests over a 1024-token prefix;
+    head counts of a 0.6B Qwen3, 16/8/128).
+
+    Adopting (cold=False): slot 0 holds the prefix; before step 0 slots 1..7
+    are acquired and adopt its `prefix` tokens by reference.  Cold (True): all
+    eight slots prefill the same prefix themselves.  Then, identically:
+    step 0 - slot s appends its own suffixes[s] rows (slot 0 decodes one);
+    step 1 - every slot decodes one token; step 2 - slot 0 finishes
+    (released) and slots 1..7 decode one more.  The prefix is 1000 tokens,
+    not 1024, so that its last block is partial: every adopter's first write
+    lands in a shared block (copy-on-write); at 1024 adopters would only
+    append to fresh blocks.  Both variants draw the same values in the same
+    order, so a slot's data are identical in the two."""
+    n = len(suffixes)
+    bs = 16
+    draw = _Draw(seed, dtype)
+    maxb = _blocks(prefix + max(suffixes) + 2, bs)
+    num_blocks = math.ceil(1.2 * n * maxb)
+    free_order = draw.rng.permutation(num_blocks).astype(np.int32)
+    pk = draw.values((prefix, hkv, d))
+    pv = draw.values((prefix, hkv, d))
+    history = [(s, pk, pv) for s in range(n)] if cold else [(0, pk, pv)]
+    steps = []
+    plan = [list(enumerate(suffixes)), [(s, 1) for s in range(n)], [(s, 1) for s in range(1, n)]]
+    for i, segs in enumerate(plan):
+        t = sum(m for _, m in segs)
+        k_new, v_new, q = draw.values((t, hkv, d)), draw.values((t, hkv, d)), draw.values((t, hq, d))
+        ops = []
+        if i == 0 and not cold:
+            for s in range(1, n):
+                ops += [("acquire", s), ("adopt", s, 0, prefix)]
+        if i == 2:
+            ops = [("release", 0)]
+        steps.append(Step(ops=ops, segments=[Segment(s, m) for s, m in segs], k_new=k_new, v_new=v_new, q=q))
+    name = "prefix-cold" if cold else "prefix"
+    return Workload(name=name, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                    num_blocks=num_blocks, max_slots=n, max_blocks_per_seq=maxb, scale=1.0 / math.sqrt(d),
+                    free_order=free_order, history=history, steps=steps,
+                    description=f"{n} requests sharing a {prefix}-token prefix ({'cold' if cold else 'adopted'})")
+
+
+def make_gather_ablation(prompt: int, batch: int = 4) -> Workload:
+    """Decode step of `batch` sequences after a `prompt`-token prompt (mlxcel
+    user guide "연속 배칭" §Paged KV 캐시와 프리픽스 공유 compares block-table
+    and gather decode at batch 4 with 512- and 4096-token prompts).  The page
+    names no model for that figure; the head layout is that of the 0.6B Qwen3
+    its paragraph uses (16 query / 8 KV heads, head_dim 128), bf16."""
+    seqs = [(i, prompt, 1) for i in range(batch)]
+    return _build(f"gather-{prompt}", 1020 + prompt, "bf16", 16, 8, 128, 16, seqs,
+                  description=f"decode, batch {batch}, {prompt}-token prompts, 16/8/128")
+
+
 def make_workload(name: str) -> Workload:
     if name == "1":
         return _config1()
@@ -232,4 +288,10 @@ def make_workload(name: str) -> Workload:
         return _config4(512)
     if name == "5":
         return _config5()
+    if name.startswith("gather-"):
+        return make_gather_ablation(int(name.split("-", 1)[1]))
+    if name == "prefix":
+        return make_prefix_share(False)
+    if name == "prefix-cold":
+        return make_prefix_share(True)
     raise ValueError(f"unknown config {name!r}")

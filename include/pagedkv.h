@@ -92,6 +92,41 @@ typedef struct {
 int pkv_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
                   int32_t num_tokens, const pkv_pool *pool, void *stream);
 
+/* Whole-block copies for copy-on-write (mlxcel user guide "연속 배칭" §Paged
+ * KV 캐시와 프리픽스 공유: a shared block is copied only when a sequence
+ * diverges in it).  For c < num_copies copies physical block src_blocks[c]
+ * into dst_blocks[c]: K and V, every KV head, all block_size positions; a
+ * bit-exact copy.  dst blocks must be distinct and differ from every src
+ * block; a block id outside [0, num_blocks) skips that pair.
+ *   src_blocks, dst_blocks   int32 [num_copies] in memory the device can read
+ *                 (device memory, or pinned host memory from hipHostMalloc).
+ * num_copies == 0 is a no-op.  Returns PKV_OK, PKV_ERR_INVALID_ARG,
+ * PKV_ERR_UNSUPPORTED or PKV_ERR_HIP. */
+int pkv_copy_blocks(const int32_t *src_blocks, const int32_t *dst_blocks, int32_t num_copies,
+                    const pkv_pool *pool, void *stream);
+
+/* Gather ablation (mlxcel user guide "연속 배칭" §Paged KV 캐시와 프리픽스
+ * 공유: the native block-table decode is compared with a gather path that
+ * rebuilds each sequence's visible window on every step).  Not needed by the
+ * block-table path; it exists to measure what that path avoids.  For every
+ * segment b with slot s = row_to_slot[b] and L = context_lens[s], copies the
+ * slot's logical blocks j = 0 .. ceil(L / block_size) - 1, whole (K and V,
+ * every head), from src block block_tables[s][j] to dst block
+ * dst_block_start[b] + j.  Afterwards the window reads through the identity
+ * table (dst_block_start[b], dst_block_start[b] + 1, ...) of the dst pool.
+ *   row_to_slot, context_lens, block_tables, num_slots, max_blocks_per_seq
+ *                 device, as for pkv_paged_attend.
+ *   max_context_len   host upper bound of L over the segments (grid sizing).
+ *   dst_block_start   device int32 [num_segments]; the ranges
+ *                 [start, start + ceil(L / block_size)) must not overlap.
+ *   src, dst      pools with equal heads, head_dim, dtype and block size;
+ *                 blocks outside either pool are skipped.
+ * Returns PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED or PKV_ERR_HIP. */
+int pkv_gather_kv(const int32_t *row_to_slot, int32_t num_segments, const int32_t *context_lens,
+                  const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq,
+                  int32_t max_context_len, const int32_t *dst_block_start, const pkv_pool *src,
+                  const pkv_pool *dst, void *stream);
+
 /* Mixed-step paged attention (lucebox blog §Paged KV and paged attention and
  * §Packing unequal prompt chunks together).  The packed batch has
  * num_segments segments; segment b owns rows [query_start[b],
@@ -140,13 +175,17 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
  * memory that the device can read (hipHostMalloc), is copied to device memory
  * by the append kernel itself - no separate copy call - and the attention
  * kernels read the device copy.  Equivalent to copying host_meta to dev_meta,
- * then pkv_kv_append, then pkv_paged_attend, on `stream`.
+ * then pkv_copy_blocks (only when num_copies > 0: the copy-on-write pairs from
+ * pkv_lower_step_cow, a third launch), then pkv_kv_append, then
+ * pkv_paged_attend, on `stream`.
  *   host_meta     pinned host int32 [meta_len]; must stay unchanged until the
  *                 step's kernels have run (record an event after the call).
  *   dev_meta      device int32 [meta_len], overwritten.
  *   *_off         offsets (in int32) of each array inside host_meta/dev_meta:
  *                 slot_mapping [num_tokens], query_start / query_len /
- *                 row_to_slot [num_segments], context_lens [num_slots].
+ *                 row_to_slot [num_segments], context_lens [num_slots];
+ *                 copy_off: copy_src [num_copies] then copy_dst [num_copies]
+ *                 (read from host_meta; ignored when num_copies == 0).
  *   block_tables  device, as for pkv_paged_attend (kept on the device across
  *                 steps; only changed tables need re-sending).
  * Other arguments as for pkv_kv_append and pkv_paged_attend; same status codes.
@@ -166,6 +205,7 @@ typedef struct {
   int32_t out_dtype;
   void *workspace;
   size_t workspace_bytes;
+  int32_t copy_off, num_copies;
 } pkv_step_desc;
 
 int pkv_mixed_step(const pkv_step_desc *step, const pkv_pool *pool, void *stream);
@@ -230,6 +270,44 @@ int pkv_lower_step(pkv_alloc *alloc, int32_t num_entries, const int32_t *entry_s
                    const int32_t *entry_new_tokens, int32_t *slot_mapping,
                    int32_t slot_mapping_cap, int32_t *query_start, int32_t *query_len,
                    int32_t *row_to_slot, int32_t *context_lens, int32_t *block_tables);
+
+/* Shared prefixes (mlxcel user guide "연속 배칭" §Paged KV 캐시와 프리픽스
+ * 공유: requests with a common prompt prefix keep one copy of its KV blocks;
+ * a later request adopts them by reference instead of prefilling again, and a
+ * shared block is duplicated only when one sequence writes into it).
+ * Every block held by a table has a reference count (the number of tables
+ * holding it); release and truncate drop references, and a block goes back on
+ * top of the free list when its count reaches 0.
+ *
+ * pkv_slot_adopt: `slot` (acquired, empty) takes the first
+ * ceil(num_tokens / block_size) blocks of src_slot's table by reference and
+ * holds num_tokens tokens (0 <= num_tokens <= src_slot's length).  No device
+ * work: the adopted tokens are read in place.  Returns PKV_OK,
+ * PKV_ERR_INVALID_ARG (bad slots, slot == src_slot, bad num_tokens) or
+ * PKV_ERR_STATE (a slot not acquired, or `slot` not empty).
+ * pkv_block_refs: reference count of a block (0 = free), -1 if out of range. */
+int pkv_slot_adopt(pkv_alloc *alloc, int32_t slot, int32_t src_slot, int32_t num_tokens);
+int32_t pkv_block_refs(const pkv_alloc *alloc, int32_t block);
+
+/* pkv_lower_step with copy-on-write.  A slot's next write lands in the block
+ * holding position `length`; when another table also holds that block, the
+ * slot's table gets a fresh block in its place (taken before the step's
+ * other new blocks) and the pair is listed:
+ *   copy_src, copy_dst   host int32 [copy_cap]: entry c asks for block
+ *                 copy_src[c] to be copied whole into block copy_dst[c]
+ *                 (K and V, every head) BEFORE this step's append - see
+ *                 pkv_copy_blocks and pkv_step_desc.copy_off;
+ *   *num_copies   host, number of pairs written (at most one per entry, so
+ *                 copy_cap = num_entries always suffices).
+ * The fresh blocks count against the free list like any new block (all or
+ * nothing).  pkv_lower_step is this call without copy buffers: it returns
+ * PKV_ERR_STATE, changing nothing, when the step would need a copy. */
+int pkv_lower_step_cow(pkv_alloc *alloc, int32_t num_entries, const int32_t *entry_slots,
+                       const int32_t *entry_new_tokens, int32_t *slot_mapping,
+                       int32_t slot_mapping_cap, int32_t *query_start, int32_t *query_len,
+                       int32_t *row_to_slot, int32_t *context_lens, int32_t *block_tables,
+                       int32_t *copy_src, int32_t *copy_dst, int32_t copy_cap,
+                       int32_t *num_copies);
 
 /* Current state: free block count; a slot's token count and block count
  * (-1 / PKV_ERR_STATE if not in use); copy of a slot's table (host out). */

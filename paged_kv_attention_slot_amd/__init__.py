@@ -12,7 +12,9 @@ from .binding import (  # noqa: F401
     PagedKVError,
     PKV_BF16,
     PKV_F32,
+    copy_blocks,
     decode_partition_tokens,
+    gather_kv,
     header_symbols,
     kv_append,
     lib,

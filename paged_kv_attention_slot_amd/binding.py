@@ -47,7 +47,8 @@ class StepDesc(ctypes.Structure):
                 ("num_q_heads", _i32), ("max_blocks_per_seq", _i32), ("max_query_len", _i32),
                 ("max_context_len", _i32), ("k_new", _p), ("v_new", _p), ("q_packed", _p),
                 ("block_tables", _p), ("scale", ctypes.c_float), ("out", _p), ("out_dtype", _i32),
-                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+                ("copy_off", _i32), ("num_copies", _i32)]
 
 
 class PagedKVError(RuntimeError):
@@ -69,6 +70,9 @@ _SIGNATURES = {
     "pkv_paged_attend_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc)]),
     "pkv_decode_partition_tokens": (_i32, []),
     "pkv_mixed_step": (_i32, [ctypes.POINTER(StepDesc), ctypes.POINTER(PoolDesc), _p]),
+    "pkv_copy_blocks": (_i32, [_p, _p, _i32, ctypes.POINTER(PoolDesc), _p]),
+    "pkv_gather_kv": (_i32, [_p, _i32, _p, _p, _i32, _i32, _i32, _p, ctypes.POINTER(PoolDesc),
+                             ctypes.POINTER(PoolDesc), _p]),
     "pkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_alloc_create": (_i32, [_i32, _i32, _i32, _i32, _pi32, ctypes.POINTER(_p)]),
     "pkv_alloc_destroy": (None, [_p]),
@@ -77,6 +81,10 @@ _SIGNATURES = {
     "pkv_slot_truncate": (_i32, [_p, _i32, _i32]),
     "pkv_reserve": (_i32, [_p, _i32, _i32]),
     "pkv_lower_step": (_i32, [_p, _i32, _pi32, _pi32, _pi32, _i32, _pi32, _pi32, _pi32, _pi32, _pi32]),
+    "pkv_lower_step_cow": (_i32, [_p, _i32, _pi32, _pi32, _pi32, _i32, _pi32, _pi32, _pi32, _pi32, _pi32,
+                                  _pi32, _pi32, _i32, _pi32]),
+    "pkv_slot_adopt": (_i32, [_p, _i32, _i32, _i32]),
+    "pkv_block_refs": (_i32, [_p, _i32]),
     "pkv_free_blocks": (_i32, [_p]),
     "pkv_slot_info": (_i32, [_p, _i32, _pi32, _pi32]),
     "pkv_slot_table": (_i32, [_p, _i32, _pi32, _i32]),
@@ -184,6 +192,25 @@ def kv_append(slot_mapping, k_new, v_new, pool: KVPool, stream=None):
     _check(st, "pkv_kv_append")
 
 
+def copy_blocks(src_blocks, dst_blocks, pool: KVPool, stream=None):
+    """Copy whole blocks src_blocks[c] -> dst_blocks[c] (device int32 tensors)."""
+    n = int(src_blocks.shape[0])
+    st = lib().pkv_copy_blocks(_dptr(src_blocks), _dptr(dst_blocks), n, pool._desc_ref,
+                               stream if stream is not None else current_stream_handle())
+    _check(st, "pkv_copy_blocks")
+
+
+def gather_kv(row_to_slot, context_lens, block_tables, dst_block_start, src: KVPool, dst: KVPool, *,
+              max_context_len, stream=None):
+    """Rebuild each segment's visible window contiguously in `dst` (the
+    gather ablation); device int32 metadata as for paged_attend."""
+    st = lib().pkv_gather_kv(_dptr(row_to_slot), int(row_to_slot.shape[0]), _dptr(context_lens),
+                             _dptr(block_tables), int(block_tables.shape[0]), int(block_tables.shape[1]),
+                             int(max_context_len), _dptr(dst_block_start), src._desc_ref, dst._desc_ref,
+                             stream if stream is not None else current_stream_handle())
+    _check(st, "pkv_gather_kv")
+
+
 def workspace_bytes(num_segments, total_q, num_q_heads, max_query_len, max_context_len, pool: KVPool) -> int:
     n = lib().pkv_paged_attend_workspace_bytes(num_segments, total_q, num_q_heads, max_query_len,
                                                max_context_len, pool._desc_ref)
@@ -269,6 +296,13 @@ class BlockAllocator:
     def reserve(self, slot, total_tokens):
         _check(self._lib.pkv_reserve(self._h, int(slot), int(total_tokens)), "pkv_reserve")
 
+    def adopt(self, slot, src_slot, num_tokens):
+        """`slot` (acquired, empty) takes src_slot's first num_tokens tokens by reference."""
+        _check(self._lib.pkv_slot_adopt(self._h, int(slot), int(src_slot), int(num_tokens)), "pkv_slot_adopt")
+
+    def block_refs(self, block) -> int:
+        return int(self._lib.pkv_block_refs(self._h, int(block)))
+
     def free_blocks(self) -> int:
         return int(self._lib.pkv_free_blocks(self._h))
 
@@ -286,8 +320,10 @@ class BlockAllocator:
         return out[:info[1]].tolist()
 
     def lower_step(self, entries, out=None):
-        """entries: [(slot, n_new)] in packed order -> dict of host int32 arrays.
-        `out` may supply preallocated arrays (same keys) to fill in place."""
+        """entries: [(slot, n_new)] in packed order -> dict of host int32 arrays,
+        copy-on-write pairs included (copy_src / copy_dst, trimmed to the count).
+        `out` may supply preallocated arrays (same keys) to fill in place; its
+        copy_src / copy_dst, when given, need room for len(entries) pairs."""
         slots = np.ascontiguousarray([e[0] for e in entries], dtype=np.int32)
         news = np.ascontiguousarray([e[1] for e in entries], dtype=np.int32)
         t = int(news.sum()) if len(news) else 0
@@ -297,9 +333,17 @@ class BlockAllocator:
                        query_len=np.empty(n, np.int32), row_to_slot=np.empty(n, np.int32),
                        context_lens=np.empty(self.max_slots, np.int32),
                        block_tables=np.empty((self.max_slots, self.max_blocks_per_seq), np.int32))
-        st = self._lib.pkv_lower_step(self._h, n, _ptr_i32(slots), _ptr_i32(news), _ptr_i32(out["slot_mapping"]),
-                                      len(out["slot_mapping"]), _ptr_i32(out["query_start"]),
-                                      _ptr_i32(out["query_len"]), _ptr_i32(out["row_to_slot"]),
-                                      _ptr_i32(out.get("context_lens")), _ptr_i32(out.get("block_tables")))
-        _check(st, "pkv_lower_step")
+        csrc = out.get("copy_src")
+        cdst = out.get("copy_dst")
+        if csrc is None or cdst is None:
+            csrc, cdst = np.empty(max(n, 1), np.int32), np.empty(max(n, 1), np.int32)
+        ncopy = ctypes.c_int32(0)
+        st = self._lib.pkv_lower_step_cow(self._h, n, _ptr_i32(slots), _ptr_i32(news),
+                                          _ptr_i32(out["slot_mapping"]), len(out["slot_mapping"]),
+                                          _ptr_i32(out["query_start"]), _ptr_i32(out["query_len"]),
+                                          _ptr_i32(out["row_to_slot"]), _ptr_i32(out.get("context_lens")),
+                                          _ptr_i32(out.get("block_tables")), _ptr_i32(csrc), _ptr_i32(cdst),
+                                          min(len(csrc), len(cdst)), ctypes.byref(ncopy))
+        _check(st, "pkv_lower_step_cow")
+        out["copy_src"], out["copy_dst"] = csrc[:ncopy.value], cdst[:ncopy.value]
         return out

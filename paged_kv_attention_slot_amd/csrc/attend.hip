@@ -119,7 +119,7 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
            const int32_t *query_start, const int32_t *query_len, int32_t num_segments, const int32_t *context_lens,
            const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq, int32_t max_query_len,
            int32_t max_context_len, const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
-           size_t workspace_bytes, hipStream_t s, const StepFacts &facts);
+           size_t workspace_bytes, hipStream_t s, const StepFacts &facts, bool check_only = false);
 
 }  // namespace
 }  // namespace pkv
@@ -135,6 +135,32 @@ int pkv_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_
   if (num_tokens == 0) return PKV_OK;
   if (!slot_mapping || !k_new || !v_new) return PKV_ERR_INVALID_ARG;
   return launch_kv_append(slot_mapping, k_new, v_new, num_tokens, *pool, static_cast<hipStream_t>(stream));
+}
+
+int pkv_copy_blocks(const int32_t *src_blocks, const int32_t *dst_blocks, int32_t num_copies, const pkv_pool *pool,
+                    void *stream) {
+  if (!pool_ok(pool) || num_copies < 0 || num_copies > 65535) return PKV_ERR_INVALID_ARG;
+  if (!pool_supported(pool)) return PKV_ERR_UNSUPPORTED;
+  if (num_copies == 0) return PKV_OK;
+  if (!src_blocks || !dst_blocks) return PKV_ERR_INVALID_ARG;
+  return launch_copy_blocks(src_blocks, dst_blocks, num_copies, *pool, static_cast<hipStream_t>(stream));
+}
+
+int pkv_gather_kv(const int32_t *row_to_slot, int32_t num_segments, const int32_t *context_lens,
+                  const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq,
+                  int32_t max_context_len, const int32_t *dst_block_start, const pkv_pool *src,
+                  const pkv_pool *dst, void *stream) {
+  if (!pool_ok(src) || !pool_ok(dst) || num_segments < 0 || num_segments > INT32_MAX / 2 || num_slots <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->dtype != dst->dtype ||
+      src->block_size != dst->block_size)
+    return PKV_ERR_INVALID_ARG;
+  if (!pool_supported(src)) return PKV_ERR_UNSUPPORTED;
+  if (num_segments == 0 || max_context_len == 0) return PKV_OK;
+  if (!row_to_slot || !context_lens || !block_tables || !dst_block_start) return PKV_ERR_INVALID_ARG;
+  return launch_gather_window(row_to_slot, num_segments, context_lens, block_tables, num_slots, max_blocks_per_seq,
+                              max_context_len, dst_block_start, *src, *dst, static_cast<hipStream_t>(stream));
 }
 
 size_t pkv_paged_attend_workspace_bytes(int32_t num_segments, int32_t total_q, int32_t num_q_heads,
@@ -173,9 +199,24 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
       !in_meta(d->query_len_off, d->num_segments) || !in_meta(d->row_to_slot_off, d->num_segments) ||
       !in_meta(d->context_lens_off, d->num_slots))
     return PKV_ERR_INVALID_ARG;
+  if (d->num_copies < 0 || d->num_copies > 65535 ||
+      (d->num_copies > 0 && !in_meta(d->copy_off, 2 * static_cast<int64_t>(d->num_copies))))
+    return PKV_ERR_INVALID_ARG;
   if (!pool_supported(pool)) return PKV_ERR_UNSUPPORTED;
   if (d->num_tokens > 0 && (!d->k_new || !d->v_new)) return PKV_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t *m = d->dev_meta;
+  // Every argument error is reported before the first launch.
+  const int chk = attend(d->q_packed, d->total_q, d->num_q_heads, m + d->row_to_slot_off, m + d->query_start_off,
+                         m + d->query_len_off, d->num_segments, m + d->context_lens_off, d->block_tables,
+                         d->num_slots, d->max_blocks_per_seq, d->max_query_len, d->max_context_len, pool, d->scale,
+                         d->out, d->out_dtype, d->workspace, d->workspace_bytes, s, StepFacts{}, true);
+  if (chk != PKV_OK) return chk;
+  if (d->num_copies > 0) {
+    const int32_t *cp = d->host_meta + d->copy_off;
+    const int sc = launch_copy_blocks(cp, cp + d->num_copies, d->num_copies, *pool, s);
+    if (sc != PKV_OK) return sc;
+  }
   const int st = launch_kv_append(d->host_meta + d->slot_mapping_off, d->k_new, d->v_new, d->num_tokens, *pool, s,
                                   d->host_meta, d->dev_meta, d->meta_len);
   if (st != PKV_OK) return st;
@@ -209,7 +250,6 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
   }
   if (f.max_decode_context > d->max_context_len) f.max_decode_context = d->max_context_len;
   if (f.max_verify_context > d->max_context_len) f.max_verify_context = d->max_context_len;
-  const int32_t *m = d->dev_meta;
   return attend(d->q_packed, d->total_q, d->num_q_heads, m + d->row_to_slot_off, m + d->query_start_off,
                 m + d->query_len_off, d->num_segments, m + d->context_lens_off, d->block_tables, d->num_slots,
                 d->max_blocks_per_seq, d->max_query_len, d->max_context_len, pool, d->scale, d->out, d->out_dtype,
@@ -225,14 +265,14 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
            const int32_t *query_start, const int32_t *query_len, int32_t num_segments, const int32_t *context_lens,
            const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq, int32_t max_query_len,
            int32_t max_context_len, const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
-           size_t workspace_bytes, hipStream_t s, const StepFacts &facts) {
+           size_t workspace_bytes, hipStream_t s, const StepFacts &facts, bool check_only) {
   if (!pool_ok(pool) || total_q < 0 || num_segments < 0 || num_q_heads <= 0 || num_slots <= 0 ||
       max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0)
     return PKV_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads != 0 || !scale_ok(scale)) return PKV_ERR_INVALID_ARG;
   if (out_dtype != PKV_F32 && !(out_dtype == PKV_BF16 && pool->dtype == PKV_BF16)) return PKV_ERR_INVALID_ARG;
   if (!pool_supported(pool) || num_q_heads / pool->num_kv_heads > 8) return PKV_ERR_UNSUPPORTED;
-  if (num_segments == 0 || total_q == 0) return PKV_OK;
+  if (num_segments == 0 || total_q == 0) return PKV_OK;  // nothing to attend (nor to check further)
   if (!q_packed || !row_to_slot || !query_start || !query_len || !context_lens || !block_tables || !out)
     return PKV_ERR_INVALID_ARG;
   if (max_query_len > total_q) max_query_len = total_q;
@@ -242,6 +282,7 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   const WorkspaceLayout ws = workspace_layout(num_segments, total_q, num_q_heads, pool->head_dim, max_query_len,
                                               max_context_len, pool->dtype, group);
   if (ws.total() > 0 && (!workspace || workspace_bytes < ws.total())) return PKV_ERR_WORKSPACE;
+  if (check_only) return PKV_OK;
 
   AttendArgs a{};
   a.q = q_packed;

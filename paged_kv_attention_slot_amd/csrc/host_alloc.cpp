@@ -9,7 +9,19 @@
 //   §Admission and step planning are different decisions - atomic
 //     reservation of KV capacity.
 // mlxcel user guide "연속 배칭" §Paged KV 캐시와 프리픽스 공유 - decode
-//   reserves blocks before the forward pass.
+//   reserves blocks before the forward pass; requests that share a prompt
+//   prefix store its blocks once (reference counts), a request adopts
+//   another's blocks instead of prefilling them again, and a shared block is
+//   copied (copy-on-write) only when one sequence's contents diverge in it.
+//
+// Every block in some table carries a reference count = the number of tables
+// that hold it; a block returns to the free list when its count reaches 0.
+// A slot may write only into blocks whose count is 1.  Appends land at
+// positions >= the slot's length, and adoption shares only blocks below the
+// adopted length, so the one block a step can find shared is the one that
+// holds position `length` (the partial last block): lowering replaces it in
+// that slot's table by a fresh block and lists the pair (old, new), whose
+// contents the device copies before the append.
 //
 // The free list is a stack: the next block handed out is at the back of
 // `free_`.  The constructor lays out `free_order` so that its first entry is
@@ -31,6 +43,7 @@ struct pkv_alloc {
   std::vector<std::vector<int32_t>> tables;   // per slot, logical order
   std::vector<int32_t> lengths;               // tokens per slot
   std::vector<char> in_use;
+  std::vector<int32_t> refs;                  // per block: tables holding it
 };
 
 namespace {
@@ -45,16 +58,34 @@ int32_t extra_blocks(const pkv_alloc *a, int32_t slot, int64_t total_tokens) {
   return need > have ? static_cast<int32_t>(need - have) : 0;
 }
 
-void grow(pkv_alloc *a, int32_t slot, int32_t extra) {
-  for (int32_t i = 0; i < extra; ++i) {
-    a->tables[slot].push_back(a->free_.back());
-    a->free_.pop_back();
-  }
+int32_t take_free(pkv_alloc *a) {
+  int32_t b = a->free_.back();
+  a->free_.pop_back();
+  a->refs[b] = 1;
+  return b;
 }
 
+void grow(pkv_alloc *a, int32_t slot, int32_t extra) {
+  for (int32_t i = 0; i < extra; ++i) a->tables[slot].push_back(take_free(a));
+}
+
+// Drop the table's references past `keep`, last block first; blocks no other
+// table holds go back on top of the free list.
 void give_back(pkv_alloc *a, std::vector<int32_t> &table, size_t keep) {
-  for (size_t i = table.size(); i > keep; --i) a->free_.push_back(table[i - 1]);
+  for (size_t i = table.size(); i > keep; --i) {
+    int32_t b = table[i - 1];
+    if (--a->refs[b] == 0) a->free_.push_back(b);
+  }
   table.resize(keep);
+}
+
+// Index in the slot's table of a shared block that its next write would
+// land in, or -1.
+int64_t shared_write_block(const pkv_alloc *a, int32_t slot) {
+  const std::vector<int32_t> &t = a->tables[slot];
+  int64_t idx = a->lengths[slot] / a->block_size;
+  if (idx < static_cast<int64_t>(t.size()) && a->refs[t[idx]] > 1) return idx;
+  return -1;
 }
 
 }  // namespace
@@ -88,6 +119,7 @@ int pkv_alloc_create(int32_t num_blocks, int32_t block_size, int32_t max_slots,
   a->tables.resize(max_slots);
   a->lengths.assign(max_slots, 0);
   a->in_use.assign(max_slots, 0);
+  a->refs.assign(num_blocks, 0);
   *out = a;
   return PKV_OK;
 }
@@ -131,15 +163,38 @@ int pkv_reserve(pkv_alloc *a, int32_t slot, int32_t total_tokens) {
   return PKV_OK;
 }
 
-int pkv_lower_step(pkv_alloc *a, int32_t num_entries, const int32_t *entry_slots,
-                   const int32_t *entry_new_tokens, int32_t *slot_mapping, int32_t slot_mapping_cap,
-                   int32_t *query_start, int32_t *query_len, int32_t *row_to_slot,
-                   int32_t *context_lens, int32_t *block_tables) {
+int pkv_slot_adopt(pkv_alloc *a, int32_t slot, int32_t src_slot, int32_t num_tokens) {
+  if (!slot_ok(a, slot) || !slot_ok(a, src_slot) || slot == src_slot || num_tokens < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!a->in_use[slot] || !a->in_use[src_slot]) return PKV_ERR_STATE;
+  if (a->lengths[slot] != 0 || !a->tables[slot].empty()) return PKV_ERR_STATE;
+  if (num_tokens > a->lengths[src_slot]) return PKV_ERR_INVALID_ARG;
+  const size_t nb = static_cast<size_t>(ceil_div(num_tokens, a->block_size));
+  const std::vector<int32_t> &src = a->tables[src_slot];
+  for (size_t i = 0; i < nb; ++i) {
+    a->tables[slot].push_back(src[i]);
+    ++a->refs[src[i]];
+  }
+  a->lengths[slot] = num_tokens;
+  return PKV_OK;
+}
+
+int32_t pkv_block_refs(const pkv_alloc *a, int32_t block) {
+  if (!a || block < 0 || block >= a->num_blocks) return -1;
+  return a->refs[block];
+}
+
+int pkv_lower_step_cow(pkv_alloc *a, int32_t num_entries, const int32_t *entry_slots,
+                       const int32_t *entry_new_tokens, int32_t *slot_mapping, int32_t slot_mapping_cap,
+                       int32_t *query_start, int32_t *query_len, int32_t *row_to_slot,
+                       int32_t *context_lens, int32_t *block_tables, int32_t *copy_src,
+                       int32_t *copy_dst, int32_t copy_cap, int32_t *num_copies) {
   if (!a || num_entries < 0 || (num_entries > 0 && (!entry_slots || !entry_new_tokens)))
     return PKV_ERR_INVALID_ARG;
+  if (num_copies) *num_copies = 0;
   // Validate the whole step before changing anything.
   std::vector<char> seen(a->max_slots, 0);
-  int64_t total_new = 0, total_extra = 0;
+  int64_t total_new = 0, total_extra = 0, copies = 0;
   for (int32_t e = 0; e < num_entries; ++e) {
     int32_t s = entry_slots[e], n = entry_new_tokens[e];
     if (!slot_ok(a, s) || n < 1 || seen[s]) return PKV_ERR_INVALID_ARG;
@@ -149,14 +204,29 @@ int pkv_lower_step(pkv_alloc *a, int32_t num_entries, const int32_t *entry_slots
     if (total > INT32_MAX || ceil_div(total, a->block_size) > a->max_blocks) return PKV_ERR_INVALID_ARG;
     total_new += n;
     total_extra += extra_blocks(a, s, total);
+    if (shared_write_block(a, s) >= 0) ++copies;
   }
   if (slot_mapping && total_new > slot_mapping_cap) return PKV_ERR_INVALID_ARG;
-  if (total_extra > static_cast<int64_t>(a->free_.size())) return PKV_ERR_NO_SPACE;
+  if (copies > 0 && (!copy_src || !copy_dst)) return PKV_ERR_STATE;
+  if (copies > copy_cap && copies > 0) return PKV_ERR_INVALID_ARG;
+  // An upper bound: a block shared by two writers of this step is copied by
+  // the first only (the second then holds it alone).
+  if (total_extra + copies > static_cast<int64_t>(a->free_.size())) return PKV_ERR_NO_SPACE;
 
-  int32_t row = 0;
+  int32_t row = 0, ncopy = 0;
   for (int32_t e = 0; e < num_entries; ++e) {
     int32_t s = entry_slots[e], n = entry_new_tokens[e];
     int32_t first = a->lengths[s];
+    const int64_t idx = shared_write_block(a, s);
+    if (idx >= 0) {
+      int32_t old = a->tables[s][idx];
+      int32_t fresh = take_free(a);
+      --a->refs[old];
+      a->tables[s][idx] = fresh;
+      copy_src[ncopy] = old;
+      copy_dst[ncopy] = fresh;
+      ++ncopy;
+    }
     grow(a, s, extra_blocks(a, s, static_cast<int64_t>(first) + n));
     const std::vector<int32_t> &t = a->tables[s];
     if (slot_mapping) {
@@ -180,7 +250,17 @@ int pkv_lower_step(pkv_alloc *a, int32_t num_entries, const int32_t *entry_slots
       std::memcpy(block_tables + static_cast<size_t>(s) * a->max_blocks, t.data(), t.size() * sizeof(int32_t));
     }
   }
+  if (num_copies) *num_copies = ncopy;
   return PKV_OK;
+}
+
+int pkv_lower_step(pkv_alloc *a, int32_t num_entries, const int32_t *entry_slots,
+                   const int32_t *entry_new_tokens, int32_t *slot_mapping, int32_t slot_mapping_cap,
+                   int32_t *query_start, int32_t *query_len, int32_t *row_to_slot,
+                   int32_t *context_lens, int32_t *block_tables) {
+  return pkv_lower_step_cow(a, num_entries, entry_slots, entry_new_tokens, slot_mapping, slot_mapping_cap,
+                            query_start, query_len, row_to_slot, context_lens, block_tables, nullptr, nullptr, 0,
+                            nullptr);
 }
 
 int32_t pkv_free_blocks(const pkv_alloc *a) { return a ? static_cast<int32_t>(a->free_.size()) : -1; }

@@ -84,4 +84,39 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+// Copy-on-write block copies (mlxcel user guide "연속 배칭" §Paged KV 캐시와
+// 프리픽스 공유): pair c copies the whole K and V tile set of block src[c]
+// into block dst[c].  Workgroup (x, c) copies 256 16-byte units of pair c's
+// [Hkv][block][row16] span; both sides are contiguous, so every access is
+// coalesced.  The ids may live in pinned host memory (read once per thread).
+template <int ROW16>
+__global__ __launch_bounds__(256) void kv_copy_blocks_kernel(const int32_t *src, const int32_t *dst, uint4 *pool_k,
+                                                             uint4 *pool_v, int32_t num_blocks,
+                                                             int32_t num_kv_heads) {
+  const int64_t per_block = static_cast<int64_t>(num_kv_heads) * kBlockTokens * ROW16;
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (u >= per_block) return;
+  const int64_t s = src[blockIdx.y], d = dst[blockIdx.y];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  pool_k[d * per_block + u] = pool_k[s * per_block + u];
+  pool_v[d * per_block + u] = pool_v[s * per_block + u];
+}
+
+int launch_copy_blocks(const int32_t *src, const int32_t *dst, int32_t num_copies, const pkv_pool &pool,
+                       hipStream_t stream) {
+  if (num_copies <= 0) return PKV_OK;
+  if (num_copies > 65535) return PKV_ERR_INVALID_ARG;
+  const int row16 = pool.head_dim * (pool.dtype == PKV_F32 ? 4 : 2) / 16;
+  const int64_t per_block = static_cast<int64_t>(pool.num_kv_heads) * kBlockTokens * row16;
+  const dim3 grid(static_cast<unsigned>((per_block + 255) / 256), static_cast<unsigned>(num_copies));
+  uint4 *k = static_cast<uint4 *>(pool.k), *v = static_cast<uint4 *>(pool.v);
+  switch (row16) {
+    case 8: kv_copy_blocks_kernel<8><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, pool.num_blocks, pool.num_kv_heads); break;
+    case 16: kv_copy_blocks_kernel<16><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, pool.num_blocks, pool.num_kv_heads); break;
+    case 32: kv_copy_blocks_kernel<32><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, pool.num_blocks, pool.num_kv_heads); break;
+    default: return PKV_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // namespace pkv

@@ -216,6 +216,17 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
                      int32_t num_tokens, const pkv_pool &pool, hipStream_t stream,
                      const int32_t *stage_src = nullptr, int32_t *stage_dst = nullptr, int32_t stage_len = 0);
 
+// Contiguous rebuild of each segment's visible window (the gather ablation).
+int launch_gather_window(const int32_t *row_to_slot, int32_t num_segments, const int32_t *context_lens,
+                         const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, const int32_t *dst_block_start, const pkv_pool &src,
+                         const pkv_pool &dst, hipStream_t stream);
+
+// Whole-block copies src[c] -> dst[c] (K and V, every head); the ids may sit
+// in device-readable pinned host memory.
+int launch_copy_blocks(const int32_t *src, const int32_t *dst, int32_t num_copies, const pkv_pool &pool,
+                       hipStream_t stream);
+
 // Short multi-row segments (verify_segment) on the streaming verify kernel,
 // plus the merge of their partitions when `need_merge`.
 // `max_pairs` is the launch's largest segment's n * G and `work_waves` its

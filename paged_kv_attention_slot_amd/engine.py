@@ -2,7 +2,8 @@
 allocator, device copies of the slot metadata, and the per-step sequence
 
     lower the step plan (host C++)  ->  one async copy of the metadata
-    ->  kv_append (HIP)  ->  paged_attend (HIP)
+    ->  [copy-on-write block copies (HIP)]  ->  kv_append (HIP)
+    ->  paged_attend (HIP)
 
 all on the caller's current stream.  It plays the role the lucebox blog
 (§One scheduler, model-specific execution) gives the engine below the
@@ -18,6 +19,12 @@ block tables are re-sent only when a table changed (a block was reserved,
 released or truncated); slots that reserved decode headroom ahead of time
 (§Admission and step planning: capacity for the prompt and rolling decode
 headroom) send no table bytes on their decode steps.
+
+Shared prompt prefixes (mlxcel user guide "연속 배칭" §Paged KV 캐시와
+프리픽스 공유): `adopt` lets an empty slot take another slot's first tokens
+by reference; when a step writes into a block that another table still
+holds, the lowering hands the writer a fresh block and lists the pair, and
+the block is copied on the device before the append.
 """
 from __future__ import annotations
 
@@ -36,10 +43,14 @@ class StepMeta:
     query_len: object
     row_to_slot: object
     context_lens: object      # device int32 [max_slots]
+    copy_src: object          # device int32 [num_copies]: copy-on-write pairs
+    copy_dst: object
     stream: object            # handle of the stream the step was lowered on
     total_q: int
     max_query_len: int
     max_context_len: int
+    num_copies: int = 0
+    copy_off: int = 0         # offset of copy_src in the staged metadata
 
 
 @dataclass
@@ -104,6 +115,11 @@ class PagedKVEngine:
         self.alloc.reserve(slot, total_tokens)
         self._tables_dirty = True
 
+    def adopt(self, slot, src_slot, num_tokens):
+        """`slot` (acquired, empty) shares src_slot's first num_tokens tokens."""
+        self.alloc.adopt(slot, src_slot, num_tokens)
+        self._tables_dirty = True
+
     # -- one step ---------------------------------------------------------
     def _stage(self, n):
         torch = self.torch
@@ -133,7 +149,8 @@ class PagedKVEngine:
         nseg = len(entries)
         t = int(sum(e[1] for e in entries))
         # packed metadata: slot_mapping | query_start | query_len | row_to_slot | context_lens
-        offs = [int(x) for x in np.cumsum([0, t, nseg, nseg, nseg, self.max_slots])]
+        #                  | copy-on-write room (up to one pair per entry)
+        offs = [int(x) for x in np.cumsum([0, t, nseg, nseg, nseg, self.max_slots, 2 * nseg])]
         st = self._stage(offs[-1])
         h = st.np
         host = dict(slot_mapping=h[offs[0]:offs[1]], query_start=h[offs[1]:offs[2]],
@@ -142,7 +159,12 @@ class PagedKVEngine:
         free_before = self.alloc.free_blocks()
         self.alloc.lower_step(entries, out=host)
         if self.alloc.free_blocks() != free_before:
-            self._tables_dirty = True
+            self._tables_dirty = True     # new blocks, copy-on-write blocks included
+        nc = len(host["copy_src"])
+        cs, cd = offs[5], offs[5] + nc    # copy_src [nc] then copy_dst [nc]
+        h[cs:cd] = host["copy_src"]
+        h[cd:cd + nc] = host["copy_dst"]
+        offs[6] = offs[5] + 2 * nc
         if self._tables_dirty:
             self._refresh_tables()
         d = st.dev
@@ -152,9 +174,10 @@ class PagedKVEngine:
         snapshot["block_tables"] = self.h_block_tables
         meta = StepMeta(host=snapshot, slot_mapping=d[offs[0]:offs[1]], query_start=d[offs[1]:offs[2]],
                         query_len=d[offs[2]:offs[3]], row_to_slot=d[offs[3]:offs[4]],
-                        context_lens=d[offs[4]:offs[5]], stream=B.ctypes.c_void_p(stream.cuda_stream),
+                        context_lens=d[offs[4]:offs[5]], copy_src=d[cs:cd], copy_dst=d[cd:cd + nc],
+                        stream=B.ctypes.c_void_p(stream.cuda_stream),
                         total_q=t, max_query_len=int(ql.max()) if nseg else 0,
-                        max_context_len=int(ctx.max()) if nseg else 0)
+                        max_context_len=int(ctx.max()) if nseg else 0, num_copies=nc, copy_off=cs)
         return meta, st, offs, stream
 
     def lower(self, entries) -> StepMeta:
@@ -181,7 +204,7 @@ class PagedKVEngine:
                           meta.max_query_len, meta.max_context_len, k_new.data_ptr(), v_new.data_ptr(),
                           q.data_ptr(), self.d_block_tables.data_ptr(), float(scale), out.data_ptr(),
                           B.pkv_dtype_of(out.dtype), ws.data_ptr() if ws is not None else None,
-                          ws.numel() if ws is not None else 0)
+                          ws.numel() if ws is not None else 0, meta.copy_off, meta.num_copies)
         # the tensors are held so their memory outlives every replay
         return PreparedStep(desc=desc, staging=st, stream=stream, meta=meta, out=out,
                             keep=(k_new, v_new, q, ws))
@@ -200,6 +223,9 @@ class PagedKVEngine:
         return self.run_prepared(prep), prep.meta
 
     def append(self, meta: StepMeta, k_new, v_new):
+        """Copy-on-write block copies (if any), then the KV append."""
+        if meta.num_copies:
+            B.copy_blocks(meta.copy_src, meta.copy_dst, self.pool, stream=meta.stream)
         B.kv_append(meta.slot_mapping, k_new, v_new, self.pool, stream=meta.stream)
 
     def workspace_for(self, meta: StepMeta):

@@ -236,3 +236,114 @@ def test_slot_reuse_leaves_other_slots_bitwise_unchanged(fused, gpu_available):
     for i in (0, 1, 2):
         assert torch.equal(s2[16 * i:16 * i + 16], s1[16 * i:16 * i + 16])
     assert torch.equal(s2[3048:3064], s1[64:80])
+
+
+# ------------------------------------------------------------------ shared prefixes
+def test_copy_blocks_bit_exact(gpu_available):
+    """pkv_copy_blocks against the oracle's block copy over the whole pool;
+    pairs with an id outside the pool are skipped."""
+    import torch
+    from oracle.attention import copy_blocks_reference
+    from workloads import bf16_bits_from_f32
+    from workloads.drive import torch_dtype
+    rng = np.random.default_rng(11)
+    for dtype, d, hkv in [("bf16", 128, 8), ("f32", 64, 2), ("bf16", 64, 1)]:
+        _log(f"copy_blocks {dtype} D{d} Hkv{hkv}")
+        nb = 40
+        shape = (nb, hkv, 16, d)
+        raw = [rng.standard_normal(shape, dtype=np.float32) for _ in range(2)]
+        if dtype == "bf16":
+            raw = [bf16_bits_from_f32(x) for x in raw]
+        pool = pk.KVPool(nb, hkv, d, torch_dtype(dtype), poison=False)
+        pool.k.copy_(to_device(raw[0], dtype, "cuda").view(shape))
+        pool.v.copy_(to_device(raw[1], dtype, "cuda").view(shape))
+        src = rng.choice(20, size=7).astype(np.int32)                # repeats allowed
+        dst = rng.choice(np.arange(20, nb), size=7, replace=False).astype(np.int32)
+        spare = [b for b in range(20, nb) if b not in dst][0]          # must stay untouched
+        bad_src = np.array([nb + 3, 5], np.int32)
+        bad_dst = np.array([spare, -1], np.int32)
+        all_src = torch.from_numpy(np.concatenate([src, bad_src])).cuda()
+        all_dst = torch.from_numpy(np.concatenate([dst, bad_dst])).cuda()
+        pk.copy_blocks(all_src, all_dst, pool)
+        pk.copy_blocks(all_src[:0], all_dst[:0], pool)                # no-op
+        torch.cuda.synchronize()
+        wk, wv = copy_blocks_reference(raw[0], raw[1], src, dst)
+        assert np.array_equal(_pool_bits(pool.k), _oracle_bits(wk))
+        assert np.array_equal(_pool_bits(pool.v), _oracle_bits(wv))
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+def test_prefix_adoption_matches_oracle_and_cold_bitwise(fused, gpu_available):
+    """Eight requests over one 1000-token prefix: adopted by reference (seven
+    copy-on-write copies in step 0) versus prefilled cold.  Every step's output
+    is within tolerance of the oracle and bit-identical to the cold run's; the
+    pool after the adopting run equals the oracle's bit for bit."""
+    _log(f"prefix adoption fused={fused}")
+    wa, wc = _workload("prefix"), _workload("prefix-cold")
+    ea, oa = _run_gpu(wa, fused=fused)
+    _, oc = _run_gpu(wc, fused=fused)
+    res, (ok, ov) = _oracle("prefix")
+    assert len(oa) == len(oc) == len(res) == 3
+    for i, ((a, ma), (c, _), r) in enumerate(zip(oa, oc, res)):
+        _check_close(f"prefix step {i}", a, r["out"], TOL[wa.dtype])
+        assert np.array_equal(a.cpu().numpy().view(np.int32), c.cpu().numpy().view(np.int32)), f"step {i}"
+        assert np.array_equal(ma.host["copy_src"], r["meta"]["copy_src"])
+        assert np.array_equal(ma.host["copy_dst"], r["meta"]["copy_dst"])
+    assert np.array_equal(_pool_bits(ea.pool.k), _oracle_bits(ok))
+    assert np.array_equal(_pool_bits(ea.pool.v), _oracle_bits(ov))
+
+
+# ------------------------------------------------------------------ gather ablation
+def _gather_then_attend(w, eng, meta, q):
+    """Rebuild every segment's window contiguously in a second (poisoned)
+    pool with pkv_gather_kv, then attend over it through identity tables.
+    Returns (out, gathered pool, per-segment first block, block counts)."""
+    import torch
+    from workloads.drive import torch_dtype
+    h = meta.host
+    r2s, ctx = h["row_to_slot"], h["context_lens"]
+    nbs = [-(-int(ctx[s]) // 16) for s in r2s]
+    start = np.concatenate([[0], np.cumsum(nbs)[:-1]]).astype(np.int32)
+    dst = pk.KVPool(int(sum(nbs)) + 1, w.num_kv_heads, w.head_dim, torch_dtype(w.dtype))
+    dense = np.zeros((w.max_slots, max(nbs)), np.int32)
+    for b, s in enumerate(r2s):
+        dense[s, :nbs[b]] = start[b] + np.arange(nbs[b])
+    pk.gather_kv(meta.row_to_slot, meta.context_lens, eng.d_block_tables, torch.from_numpy(start).cuda(),
+                 eng.pool, dst, max_context_len=meta.max_context_len)
+    out = torch.empty((meta.total_q, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    pk.paged_attend(q, meta.row_to_slot, meta.query_start, meta.query_len, meta.context_lens,
+                    torch.from_numpy(dense).cuda(), dst, w.scale, max_query_len=meta.max_query_len,
+                    max_context_len=meta.max_context_len, out=out, workspace=eng.workspace_for(meta))
+    torch.cuda.synchronize()
+    return out, dst, start, nbs
+
+
+@pytest.mark.parametrize("name", ["3", "gather-mixed"])
+def test_gather_then_attend_equals_paged_bitwise(name, gpu_available):
+    """The gather path (rebuild each window contiguously, then attend through
+    identity tables) gives the block-table path's output bit for bit, and the
+    rebuilt windows equal the oracle's logical gather of each sequence."""
+    from oracle.attention import gather_sequence
+    from workloads.drive import step_tensors
+    _log(f"gather ablation parity {name}")
+    if name == "gather-mixed":
+        w = make_custom([(0, 700, 16), (1, 3000, 3), (2, 200, 40), (3, 1300, 1), (4, 0, 1)],
+                        dtype="bf16", hq=32, hkv=8, d=128, seed=23)
+        res, (ok, ov) = run_workload(w)
+    else:
+        w = _workload(name)
+        res, (ok, ov) = _oracle(name)
+    eng, outs = _run_gpu(w)
+    out_paged, meta = outs[-1]
+    _, _, q = step_tensors(w, len(w.steps) - 1)
+    out, dst, start, nbs = _gather_then_attend(w, eng, meta, q)
+    assert np.array_equal(out.cpu().numpy().view(np.int32), out_paged.cpu().numpy().view(np.int32))
+    tables = res[-1]["meta"]["block_tables"]
+    gk, gv = _pool_bits(dst.k), _pool_bits(dst.v)
+    for b, s in enumerate(meta.host["row_to_slot"].tolist()):
+        L = int(meta.host["context_lens"][s])
+        for got_pool, want_pool in ((gk, ok), (gv, ov)):
+            got = got_pool[start[b]:start[b] + nbs[b]].transpose(0, 2, 1, 3).reshape(-1, w.num_kv_heads,
+                                                                                    w.head_dim)[:L]
+            want = gather_sequence(want_pool, tables[s], L, 16)
+            assert np.array_equal(got, _oracle_bits(want)), f"segment {b}"

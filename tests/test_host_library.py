@@ -60,6 +60,20 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
         step.num_slots = 1
         step.scale = bad
         assert lib.pkv_mixed_step(ctypes.byref(step), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
+    # block copies: a negative count, or a NULL pool
+    assert lib.pkv_copy_blocks(None, None, -1, ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
+    assert lib.pkv_copy_blocks(None, None, 1, ctypes.byref(d), None) == pk.binding.PKV_ERR_INVALID_ARG
+    assert lib.pkv_copy_blocks(None, None, 0, ctypes.byref(d4), None) == pk.binding.PKV_OK
+    # copy-on-write pairs that do not fit in the staged metadata
+    step = pk.binding.StepDesc()
+    meta = (ctypes.c_int32 * 8)()
+    step.host_meta = ctypes.cast(meta, ctypes.c_void_p)
+    step.dev_meta = 16
+    step.meta_len = 8
+    step.num_slots = 1
+    step.scale = 1.0
+    step.copy_off, step.num_copies = 4, 3
+    assert lib.pkv_mixed_step(ctypes.byref(step), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
     # decode rows with a long context need workspace; none given
     assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1000, 1, 5000, ctypes.byref(d4), 1.0, 16, 0,
                                 None, 0, None) == pk.binding.PKV_ERR_WORKSPACE
@@ -75,7 +89,7 @@ def test_workspace_sizing():
     assert n == ((acc + 255) // 256) * 256 + 64 * 32 * 4 * 2 * 4
 
 
-def _random_ops(seed, n_ops=300):
+def _random_ops(seed, n_ops=300, adopt=False):
     rng = np.random.default_rng(seed)
     nb, bs, slots, maxb = 64, 16, 8, 12
     order = rng.permutation(nb).astype(np.int32)
@@ -88,7 +102,13 @@ def _random_ops(seed, n_ops=300):
             s = int(rng.choice([x for x in range(slots) if x not in live]))
             ours.acquire(s)
             ref.acquire(s)
+            donors = [x for x in sorted(live) if ref.lengths[x] > 0]
             live.add(s)
+            if adopt and donors and rng.random() < 0.7:
+                src = int(rng.choice(donors))
+                n = int(rng.integers(0, ref.lengths[src] + 1))
+                ours.adopt(s, src, n)
+                ref.adopt(s, src, n)
         elif kind == 1 and live:
             s = int(rng.choice(sorted(live)))
             ours.release(s)
@@ -136,6 +156,7 @@ def _random_ops(seed, n_ops=300):
                     ours.lower_step(entries)
         # full state comparison after every op
         assert ours.free_blocks() == ref.free_count()
+        assert [ours.block_refs(b) for b in range(nb)] == ref.refs
         for s in range(slots):
             if s in live:
                 assert ours.slot_table(s) == ref.tables[s]
@@ -147,6 +168,47 @@ def _random_ops(seed, n_ops=300):
 @pytest.mark.parametrize("seed", range(6))
 def test_allocator_and_lowering_match_oracle(seed):
     _random_ops(seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_adoption_and_copy_on_write_match_oracle(seed):
+    """Shared prefixes: adopt, reference counts, and the copy-on-write pairs
+    of each lowering (compared key by key with the oracle's)."""
+    _random_ops(100 + seed, adopt=True)
+
+
+def test_adoption_errors_and_plain_lowering_refuses_copies():
+    al = pk.BlockAllocator(16, 16, 4, 8)
+    al.acquire(0)
+    al.lower_step([(0, 20)])                         # 2 blocks, the second partial
+    al.acquire(1)
+    with pytest.raises(pk.PagedKVError):
+        al.adopt(1, 0, 21)                           # more than the source holds
+    with pytest.raises(pk.PagedKVError):
+        al.adopt(1, 1, 0)                            # itself
+    with pytest.raises(pk.PagedKVError):
+        al.adopt(2, 0, 4)                            # slot 2 not acquired
+    al.adopt(1, 0, 20)
+    t0 = al.slot_table(0)
+    assert al.slot_table(1) == t0 and [al.block_refs(b) for b in t0] == [2, 2]
+    with pytest.raises(pk.PagedKVError):
+        al.adopt(1, 0, 4)                            # slot 1 no longer empty
+    # the C entry point without copy buffers refuses a step that needs a copy
+    lib = pk.lib()
+    slots, news = np.array([1], np.int32), np.array([1], np.int32)
+    st = lib.pkv_lower_step(al._h, 1, slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            news.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, 0, None, None, None,
+                            None, None)
+    assert st == pk.binding.PKV_ERR_STATE
+    assert al.slot_info(1) == (20, 2)                # nothing changed
+    meta = al.lower_step([(1, 1)])
+    assert meta["copy_src"].tolist() == [t0[1]] and al.slot_table(1)[0] == t0[0]
+    assert al.slot_table(1)[1] == meta["copy_dst"][0] != t0[1]
+    assert [al.block_refs(b) for b in t0] == [2, 1]
+    al.release(0)
+    assert al.block_refs(t0[0]) == 1 and al.block_refs(t0[1]) == 0
+    al.release(1)
+    assert al.free_blocks() == 16
 
 
 def test_allocator_matches_oracle_on_config_workloads():

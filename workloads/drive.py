@@ -50,6 +50,8 @@ def apply_ops(engine, ops):
             engine.release(op[1])
         elif op[0] == "truncate":
             engine.truncate(op[1], op[2])
+        elif op[0] == "adopt":
+            engine.adopt(op[1], op[2], op[3])
         else:
             raise ValueError(op)
 

@@ -13,6 +13,9 @@ What it computes, in plain numpy (fp64 for all floating point):
     shared prompt-prefix blocks with reference counts;
   * attention.append_reference - the KV append scatter (a byte copy);
   * attention.copy_blocks_reference - the copy-on-write block copy;
+  * quant.quantize_rows / append_reference_q8 / paged_attention_q8 - the
+    8-bit KV format (one float32 scale per (token, KV head) row), its append
+    and attention over the values the codes stand for;
   * attention.paged_attention  - walks each block table in logical
     order, materialises that sequence's contiguous K/V, and computes causal
     softmax attention in fp64.

@@ -36,6 +36,8 @@ def decode_values(raw: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         bits = np.asarray(raw, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "f64":                  # values already decoded (a dequantized pool)
+        return np.asarray(raw, dtype=np.float64)
     raise ValueError(dtype)
 
 
@@ -109,18 +111,21 @@ def attend_rows(q, k, v, scale, positions):
 
 
 def paged_attention(q_raw, pool_k, pool_v, dtype, block_size, block_tables, context_lens,
-                    row_to_slot, query_start, query_len, scale, num_kv_heads=None):
+                    row_to_slot, query_start, query_len, scale, num_kv_heads=None, kv_dtype=None):
     """Mixed-step paged attention over a packed batch.  Returns fp64
-    [total_q][Hq][D]; rows not covered by any segment stay NaN."""
+    [total_q][Hq][D]; rows not covered by any segment stay NaN.  `kv_dtype`
+    (default `dtype`) is the pools' element type ("f64" for pools already
+    dequantized)."""
     q = decode_values(q_raw, dtype)
+    kv_dtype = kv_dtype or dtype
     out = np.full(q.shape, np.nan, dtype=np.float64)
     for b in range(len(row_to_slot)):
         s = int(row_to_slot[b])
         L = int(context_lens[s])
         n = int(query_len[b])
         r0 = int(query_start[b])
-        k = decode_values(gather_sequence(pool_k, block_tables[s], L, block_size), dtype)
-        v = decode_values(gather_sequence(pool_v, block_tables[s], L, block_size), dtype)
+        k = decode_values(gather_sequence(pool_k, block_tables[s], L, block_size), kv_dtype)
+        v = decode_values(gather_sequence(pool_v, block_tables[s], L, block_size), kv_dtype)
         positions = L - n + np.arange(n)
         out[r0:r0 + n] = attend_rows(q[r0:r0 + n], k, v, float(scale), positions)
     return out

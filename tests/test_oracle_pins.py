@@ -579,3 +579,142 @@ def test_planted_prefix_mistakes_are_caught():
         b = self.tables[slot].pop()
         self.refs[b] -= 1
     assert _prefix_pins_fail(swap(BlockPool, "adopt", short_adopt))
+
+
+# --------------------------------------------------------------- 8-bit KV rows
+from fractions import Fraction  # noqa: E402
+
+from oracle import quant as pq  # noqa: E402
+
+
+def _f32_nearest(r: Fraction) -> np.float32:
+    """The float32 nearest the rational r (ties to even), by exact comparison
+    of the neighbours of a first guess (no double rounding)."""
+    c = np.float32(float(r))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    def key(f):
+        return (abs(Fraction(float(f)) - r), int(np.array(f, np.float32).view(np.uint32)) & 1)
+    return min(cands, key=key)
+
+
+def _round_half_even(r: Fraction) -> int:
+    fl = r.numerator // r.denominator
+    rem = r - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        return fl + 1
+    return fl
+
+
+def _q8_brute(x_bits):
+    """The format's definition evaluated with exact rationals: every float32
+    rounding done by nearest-neighbour search, the integer rounding by hand."""
+    x = [Fraction(float(v)) for v in pa.decode_values(x_bits, "bf16")]
+    amax = max(abs(v) for v in x)
+    if amax == 0:
+        return [0] * len(x), np.float32(0)
+    inv = _f32_nearest(Fraction(127) / amax)
+    scale = _f32_nearest(amax / 127)
+    codes = []
+    for v in x:
+        prod = _f32_nearest(v * Fraction(float(inv)))
+        codes.append(max(-127, min(127, _round_half_even(Fraction(float(prod))))))
+    return codes, scale
+
+
+def test_q8_hand_cases():
+    """Hand-computed rows: ties go to the even code; a zero row is all zeros
+    with scale 0; a row whose largest magnitude is 127 keeps its integers."""
+    row = bf16_bits_from_f32(np.array([[254, 1, 3, 5, -3, -1, 0, 7]], np.float32))
+    codes, scale = pq.quantize_rows(row)            # inv = 1/2, scale = 2
+    assert codes.tolist() == [[127, 0, 2, 2, -2, 0, 0, 4]] and scale.tolist() == [2.0]
+    codes, scale = pq.quantize_rows(np.zeros((1, 8), np.uint16))
+    assert codes.tolist() == [[0] * 8] and scale.tolist() == [0.0]
+    ints = np.array([[-127, -64, -1, 0, 1, 2, 100, 127]], np.float32)
+    codes, scale = pq.quantize_rows(bf16_bits_from_f32(ints))
+    assert codes.tolist() == ints.astype(int).tolist() and scale.tolist() == [1.0]
+
+
+def test_q8_matches_exact_rational_brute_force():
+    rng = np.random.default_rng(17)
+    rows = bf16_bits_from_f32(rng.standard_normal((24, 64), dtype=np.float32) *
+                              np.exp2(rng.integers(-6, 7, size=(24, 1))).astype(np.float32))
+    codes, scales = pq.quantize_rows(rows)
+    for i in range(rows.shape[0]):
+        want_c, want_s = _q8_brute(rows[i])
+        assert codes[i].tolist() == want_c, i
+        assert scales[i].view(np.uint32) == np.float32(want_s).view(np.uint32), i
+
+
+def test_q8_properties():
+    """Codes within [-127, 127], the largest magnitude at +-127, signs kept,
+    dequantization error within half a step, and scaling a row by a power of
+    two scales its scale and keeps its codes."""
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((200, 128), dtype=np.float32)
+    bits = bf16_bits_from_f32(x)
+    xf = pa.decode_values(bits, "bf16")
+    codes, scales = pq.quantize_rows(bits)
+    assert np.abs(codes.astype(int)).max() <= 127
+    assert (np.abs(codes.astype(int)).max(axis=1) == 127).all()
+    assert (codes.astype(float) * xf >= 0).all()
+    err = np.abs(xf - pq.dequantize(codes, scales))
+    assert (err <= scales[:, None].astype(np.float64) * (0.5 + 1e-4)).all()
+    for k in (-5, 3):
+        c2, s2 = pq.quantize_rows(bf16_bits_from_f32(pa.decode_values(bits, "bf16").astype(np.float32) * 2.0 ** k))
+        assert np.array_equal(c2, codes)
+        assert np.array_equal(s2, (scales * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def test_q8_append_and_attention():
+    """The 8-bit append stores each token's codes and scale at its slot and
+    touches nothing else; attention over the codes equals attention over a
+    pool already holding their values, and stays within a few hundredths of
+    the unquantized attention on N(0, 1) data."""
+    w = make_custom([(0, 40, 1), (1, 70, 3), (2, 5, 1)], dtype="bf16", hq=8, hkv=2, d=64, seed=5)
+    w.kv_quant = "q8"
+    res, (pk, pv) = run_workload(w)
+    out = res[0]["out"]
+    meta = res[0]["meta"]
+    # scatter: every written position holds the row's own quantization
+    st = w.steps[0]
+    ck, sk = pk
+    for t, slot in enumerate(meta["slot_mapping"].tolist()):
+        b, o = divmod(slot, w.block_size)
+        c, s = pq.quantize_rows(st.k_new[t])
+        assert np.array_equal(ck[b, :, o, :], c) and np.array_equal(sk[b, :, o], s)
+    hist_rows = sum(len(k) for _, k, _ in w.history)
+    assert np.isnan(sk).sum() == sk.size - (hist_rows + len(meta["slot_mapping"])) * w.num_kv_heads
+    # attention over the dequantized pools through the plain path
+    deq_k = pq.dequantize(pk[0], np.nan_to_num(pk[1]))
+    deq_v = pq.dequantize(pv[0], np.nan_to_num(pv[1]))
+    plain = pa.paged_attention(st.q, deq_k, deq_v, "bf16", w.block_size, meta["block_tables"],
+                               meta["context_lens"], meta["row_to_slot"], meta["query_start"],
+                               meta["query_len"], w.scale, kv_dtype="f64")
+    assert np.array_equal(out, plain)
+    w.kv_quant = ""
+    ref, _ = run_workload(w)
+    err = np.abs(out - ref[0]["out"]).max()
+    assert 0 < err < 0.05, err
+
+
+def test_planted_q8_mistakes_are_caught():
+    row = bf16_bits_from_f32(np.array([[254, 1, 3, 5, -3, -1, 0, 7]], np.float32))
+    orig_rint = np.rint
+    try:
+        pq.np.rint = lambda a: np.floor(a + 0.5)              # ties away from even
+        assert pq.quantize_rows(row)[0].tolist() != [[127, 0, 2, 2, -2, 0, 0, 4]]
+    finally:
+        pq.np.rint = orig_rint
+    orig_q = pq.quantize_rows
+
+    def scale_128(bits):                                     # wrong divisor
+        c, s = orig_q(bits)
+        return c, (s * np.float32(127) / np.float32(128)).astype(np.float32)
+    pq.quantize_rows = scale_128
+    try:
+        rng = np.random.default_rng(3)
+        bits = bf16_bits_from_f32(rng.standard_normal((4, 64), dtype=np.float32))
+        assert any(pq.quantize_rows(bits[i:i + 1])[1][0].view(np.uint32) !=
+                   np.float32(_q8_brute(bits[i])[1]).view(np.uint32) for i in range(4))
+    finally:
+        pq.quantize_rows = orig_q

@@ -76,6 +76,7 @@ class Workload:
     steps: list                # [Step]
     description: str = ""
     notes: dict = field(default_factory=dict)
+    kv_quant: str = ""         # "" (pool holds `dtype` values) or "q8" (8-bit codes + scales; inputs bf16)
 
     @property
     def elem_bytes(self) -> int:
@@ -171,6 +172,17 @@ def _config3v():
     seqs = [(int(s), max(int(L) - 2, 0), 2) for s, L in zip(slots, lens)]
     return _build("3v", 1003, "bf16", 32, 8, 128, 16, seqs, max_slots=128, draw=draw,
                   description="64 sequences x 2 draft rows (verify), lognormal context (median 2048)")
+
+
+def _config3q():
+    """Config 3 (same seed, lengths, slots and values) with the KV pool held
+    as 8-bit codes with one scale per (token, KV head): the bf16 K/V rows are
+    quantized on append."""
+    w = _config3()
+    w.name = "3q"
+    w.kv_quant = "q8"
+    w.description = "64 decode rows, lognormal context (median 2048), 8-bit KV"
+    return w
 
 
 def _config4(chunk):
@@ -282,6 +294,8 @@ def make_workload(name: str) -> Workload:
         return _config3()
     if name == "3v":
         return _config3v()
+    if name == "3q":
+        return _config3q()
     if name == "4a":
         return _config4(2048)
     if name == "4b":

@@ -41,6 +41,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 # Sources of the measured attention launch: a counter summary in
 # profiles/traffic.json counts only while these files are unchanged.
 TRAFFIC_SOURCES = ("decode_mfma.hip", "decode.hip", "pkv_device.h", "pkv_internal.h")
+TRAFFIC_SOURCES_Q8 = ("decode_q8.hip", "decode.hip", "pkv_device.h", "pkv_internal.h")
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 
 
@@ -63,10 +64,12 @@ def parse_args():
 
 def decode_bytes(w, lens, elem):
     """Algorithmic bytes of the decode rows: K and V of every cached token
-    once, plus Q in, fp32 O out and the block-table entries walked."""
+    once (an 8-bit pool: head_dim codes plus one float32 scale per token and
+    KV head), plus Q in, fp32 O out and the block-table entries walked."""
     hkv, hq, d = w.num_kv_heads, w.num_q_heads, w.head_dim
-    kv = sum(2 * L * hkv * d * elem for L in lens)
-    other = sum(hq * d * elem + hq * d * 4 + 4 * (-(-L // 16)) for L in lens)
+    row = d + 4 if getattr(w, "kv_quant", "") == "q8" else d * elem
+    kv = sum(2 * L * hkv * row for L in lens)
+    other = sum(hq * d * 2 + hq * d * 4 + 4 * (-(-L // 16)) for L in lens)
     return kv, kv + other
 
 
@@ -146,7 +149,7 @@ def run_gather_ablation(args, pk, torch, dev):
     first copies each window into contiguous blocks (pkv_gather_kv) and then
     attends through identity tables, so the ratio prices the rebuild alone."""
     from workloads import make_workload
-    from workloads.drive import make_engine, place_history, step_tensors, torch_dtype
+    from workloads.drive import make_engine, place_history, pool_torch_dtype, step_tensors
     rows = []
     stream = torch.cuda.current_stream()
     reps = max(args.steps, 5)
@@ -161,7 +164,7 @@ def run_gather_ablation(args, pk, torch, dev):
         h = meta.host
         nbs = [-(-int(h["context_lens"][s]) // 16) for s in h["row_to_slot"]]
         start = torch.tensor([0] + list(itertools.accumulate(nbs))[:-1], dtype=torch.int32, device=dev)
-        dst = pk.KVPool(sum(nbs), w.num_kv_heads, w.head_dim, torch_dtype(w.dtype), device=dev, poison=False)
+        dst = pk.KVPool(sum(nbs), w.num_kv_heads, w.head_dim, pool_torch_dtype(w), device=dev, poison=False)
         dense = torch.zeros((w.max_slots, max(nbs)), dtype=torch.int32)
         off = 0
         for b, s in enumerate(h["row_to_slot"].tolist()):
@@ -282,11 +285,8 @@ def cpu_baseline(w, sample_rows, repeats):
     """Time the oracle (numpy fp64) on the first `sample_rows` decode rows of
     the step: block-table walk + fp64 attention, best of `repeats`.  Setup is
     not timed."""
-    import numpy as np
-    from oracle.attention import paged_attention
-    from oracle.step import place_history, poisoned_pool
     from oracle.block_pool import BlockPool
-    from oracle.attention import append_reference
+    from oracle.step import append_kv, attend_step, place_history, poisoned_pool
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -296,13 +296,14 @@ def cpu_baseline(w, sample_rows, repeats):
     pk_, pv_ = place_history(w, alloc, poisoned_pool(w), poisoned_pool(w))
     st = w.steps[0]
     meta = alloc.lower_step([(s.slot, s.n) for s in st.segments])
-    pk_, pv_ = append_reference(pk_, pv_, meta["slot_mapping"], st.k_new, st.v_new, w.block_size)
+    pk_, pv_ = append_kv(w, pk_, pv_, meta["slot_mapping"], st.k_new, st.v_new)
     rows = min(sample_rows, len(st.segments))
+    sample = dict(meta, row_to_slot=meta["row_to_slot"][:rows], query_start=meta["query_start"][:rows],
+                  query_len=meta["query_len"][:rows])
     dt = float("inf")
     for _ in range(repeats):
         t0 = time.perf_counter()
-        paged_attention(st.q[:rows], pk_, pv_, w.dtype, w.block_size, meta["block_tables"], meta["context_lens"],
-                        meta["row_to_slot"][:rows], meta["query_start"][:rows], meta["query_len"][:rows], w.scale)
+        attend_step(w, st, pk_, pv_, sample)
         dt = min(dt, time.perf_counter() - t0)
     lens = [int(meta["context_lens"][s]) for s in meta["row_to_slot"][:rows]]
     kv, _ = decode_bytes(w, lens, w.elem_bytes)
@@ -392,8 +393,9 @@ def main():
     torch.cuda.synchronize()
     attend_avg_s = sum(a_.elapsed_time(b_) for a_, b_ in ev) / reps / 1e3
     achieved = alg_attend / attend_avg_s / 1e9
-    src = source_hash(*TRAFFIC_SOURCES)
-    traffic = measured_traffic("decode_config3", src)
+    q8 = getattr(w, "kv_quant", "") == "q8"
+    src = source_hash(*(TRAFFIC_SOURCES_Q8 if q8 else TRAFFIC_SOURCES))
+    traffic = measured_traffic(f"decode_config{w.name}", src)
     line = {
         "metric": "paged-attn decode KV GB/s (% HBM peak); mixed-step latency at 64 seqs",
         "value": round(kv_total / wall / 1e9, 2),
@@ -405,7 +407,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": "i8 KV (bf16 Q, fp32 accumulate)" if q8 else ("bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": f"config {w.name}: {w.description}", "decode_rows": len(entries),
                    "heads_q_kv": [w.num_q_heads, w.num_kv_heads], "head_dim": w.head_dim, "block_size": 16,
@@ -415,7 +417,8 @@ def main():
         "attend_ms_avg": round(attend_avg_s * 1e3, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "pkv decode_kernel + reduce_kernel (one paged_attend launch)"},
+                     "kernel": ("pkv decode_q8_kernel" if q8 else "pkv decode_mfma_kernel")
+                     + " + reduce_kernel (one paged_attend launch)"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows, args.cpu_repeats)

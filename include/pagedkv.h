@@ -63,10 +63,26 @@ typedef enum {
   PKV_ERR_STATE = -6        /* allocator: slot not in the required state          */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 } pkv_dtype;
 
 /* The shared KV pool.  Supported shapes: block_size 16; head_dim 64 or 128;
- * dtype PKV_F32 or PKV_BF16. */
+ * dtype PKV_F32, PKV_BF16 or PKV_I8.
+ *
+ * PKV_I8 is an 8-bit KV cache (the lucebox blog's R9700 DFlash2 section runs
+ * its KV in an 8-bit format; the pages do not define one, so this is the
+ * library's own).  k and v hold int8 codes in the layout above; k_scale and
+ * v_scale hold one float32 per (block, KV head, position):
+ * [num_blocks][num_kv_heads][block_size].  A stored row (the head_dim values
+ * of one token and KV head) stands for code * scale.  Rows are written by
+ * pkv_kv_append from bf16 input:
+ *   amax = max |x| over the row;  amax == 0 gives codes 0 and scale 0;
+ *   otherwise inv = 127 / amax and scale = amax / 127 (float32, correctly
+ *   rounded), code = round-half-to-even(float32(x * inv)) clamped to +-127.
+ * Queries (q_packed) on an 8-bit pool are bf16 and are used as fp16 (exact
+ * for |q| below 65504; magnitudes under 2^-14 keep fp16's subnormal
+ * precision); output is float32 or bf16.
+ * Attention on an 8-bit pool is built for decode rows (query_len 1) only:
+ * max_query_len > 1 gives PKV_ERR_UNSUPPORTED. */
 typedef struct {
   void *k;              /* device [num_blocks][num_kv_heads][block_size][head_dim] */
   void *v;              /* device, same shape and dtype as k                        */
@@ -75,6 +91,8 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t dtype;        /* pkv_dtype */
+  float *k_scale;       /* PKV_I8 only: device [num_blocks][num_kv_heads][block_size] */
+  float *v_scale;       /* PKV_I8 only: same shape; NULL for other dtypes            */
 } pkv_pool;
 
 /* ------------------------------------------------------------------ device */
@@ -82,11 +100,14 @@ typedef struct {
 /* KV append (lucebox blog §Chunked prefill is a slot phase: a chunk appends
  * directly to its slot's paged KV).  For every token t < num_tokens and every
  * KV head h, copies k_new[t][h][:] to K[s / bs][h][s % bs][:] and v_new[t][h][:]
- * to V[...] where s = slot_mapping[t].  A bit-exact copy: no conversion.
+ * to V[...] where s = slot_mapping[t].  A bit-exact copy: no conversion
+ * (an 8-bit pool stores the row's codes and scale instead).
  *   slot_mapping  device int32 [num_tokens]; flat pool token slots.  Entries
  *                 must be distinct (a repeat is a write race); an entry outside
  *                 [0, num_blocks * block_size) is skipped (nothing written).
- *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], pool dtype.
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], pool dtype
+ *                 (bf16 for a PKV_I8 pool: each row is quantized as stated
+ *                 at pkv_pool, codes and scale stored together).
  * num_tokens == 0 is a no-op.  Returns PKV_OK, PKV_ERR_INVALID_ARG,
  * PKV_ERR_UNSUPPORTED or PKV_ERR_HIP. */
 int pkv_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new,
@@ -95,8 +116,8 @@ int pkv_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_
 /* Whole-block copies for copy-on-write (mlxcel user guide "연속 배칭" §Paged
  * KV 캐시와 프리픽스 공유: a shared block is copied only when a sequence
  * diverges in it).  For c < num_copies copies physical block src_blocks[c]
- * into dst_blocks[c]: K and V, every KV head, all block_size positions; a
- * bit-exact copy.  dst blocks must be distinct and differ from every src
+ * into dst_blocks[c]: K and V, every KV head, all block_size positions
+ * (with their scales for an 8-bit pool); a bit-exact copy.  dst blocks must be distinct and differ from every src
  * block; a block id outside [0, num_blocks) skips that pair.
  *   src_blocks, dst_blocks   int32 [num_copies] in memory the device can read
  *                 (device memory, or pinned host memory from hipHostMalloc).
@@ -111,7 +132,8 @@ int pkv_copy_blocks(const int32_t *src_blocks, const int32_t *dst_blocks, int32_
  * block-table path; it exists to measure what that path avoids.  For every
  * segment b with slot s = row_to_slot[b] and L = context_lens[s], copies the
  * slot's logical blocks j = 0 .. ceil(L / block_size) - 1, whole (K and V,
- * every head), from src block block_tables[s][j] to dst block
+ * every head, scales of an 8-bit pool included), from src block
+ * block_tables[s][j] to dst block
  * dst_block_start[b] + j.  Afterwards the window reads through the identity
  * table (dst_block_start[b], dst_block_start[b] + 1, ...) of the dst pool.
  *   row_to_slot, context_lens, block_tables, num_slots, max_blocks_per_seq
@@ -139,7 +161,8 @@ int pkv_gather_kv(const int32_t *row_to_slot, int32_t num_segments, const int32_
  * h reads KV head h / (num_q_heads / num_kv_heads).  For each row and head:
  *     out = sum_j softmax_j(scale * q . K_j) V_j
  * accumulated in fp32.
- *   q_packed      device [total_q][num_q_heads][head_dim], pool dtype.
+ *   q_packed      device [total_q][num_q_heads][head_dim], pool dtype (bf16
+ *                 for a PKV_I8 pool, which attends over code * scale).
  *   row_to_slot, query_start, query_len   device int32 [num_segments].
  *                 query_len >= 1; segments cover disjoint rows; a slot appears
  *                 in at most one segment; query_len <= L.
@@ -151,7 +174,8 @@ int pkv_gather_kv(const int32_t *row_to_slot, int32_t num_segments, const int32_
  *   scale         softmax scale (1/sqrt(head_dim) for standard attention);
  *                 finite and > 0, else PKV_ERR_INVALID_ARG.
  *   out           device [total_q][num_q_heads][head_dim]; out_dtype PKV_F32,
- *                 or PKV_BF16 when the pool is bf16 (rounded to nearest even).
+ *                 or PKV_BF16 when the pool is bf16 or 8-bit (rounded to
+ *                 nearest even).
  *   workspace     device scratch of at least pkv_paged_attend_workspace_bytes
  *                 bytes (may be NULL when that is 0); contents on entry ignored.
  * Rows not covered by any segment are not written.  Returns PKV_OK,

@@ -33,7 +33,7 @@ def poisoned_pool(w):
     return np.full(shape, bits, dtype=utype).view(store)
 
 
-def _append(w, pk, pv, slot_mapping, k_new, v_new):
+def append_kv(w, pk, pv, slot_mapping, k_new, v_new):
     if getattr(w, "kv_quant", "") == "q8":
         ck, sk, cv, sv = append_reference_q8(pk[0], pk[1], pv[0], pv[1], slot_mapping, k_new, v_new,
                                              w.block_size)
@@ -41,7 +41,7 @@ def _append(w, pk, pv, slot_mapping, k_new, v_new):
     return append_reference(pk, pv, slot_mapping, k_new, v_new, w.block_size)
 
 
-def _copy(w, pk, pv, copy_src, copy_dst):
+def copy_kv(w, pk, pv, copy_src, copy_dst):
     if getattr(w, "kv_quant", "") == "q8":
         ck, cv = copy_blocks_reference(pk[0], pv[0], copy_src, copy_dst)
         sk, sv = copy_blocks_reference(pk[1], pv[1], copy_src, copy_dst)
@@ -49,7 +49,7 @@ def _copy(w, pk, pv, copy_src, copy_dst):
     return copy_blocks_reference(pk, pv, copy_src, copy_dst)
 
 
-def _attend(w, st, pk, pv, meta):
+def attend_step(w, st, pk, pv, meta):
     args = (w.block_size, meta["block_tables"], meta["context_lens"], meta["row_to_slot"],
             meta["query_start"], meta["query_len"], w.scale)
     if getattr(w, "kv_quant", "") == "q8":
@@ -80,7 +80,7 @@ def place_history(w, alloc: BlockPool, pk, pv):
         meta = alloc.lower_step(entries)
         hk = np.concatenate([k for _, k, _ in w.history if len(k) > 0])
         hv = np.concatenate([v for _, _, v in w.history if len(v) > 0])
-        pk, pv = _append(w, pk, pv, meta["slot_mapping"], hk, hv)
+        pk, pv = append_kv(w, pk, pv, meta["slot_mapping"], hk, hv)
     return pk, pv
 
 
@@ -95,8 +95,8 @@ def run_workload(w, steps=None):
             break
         apply_ops(alloc, st.ops)
         meta = alloc.lower_step([(s.slot, s.n) for s in st.segments])
-        pk, pv = _copy(w, pk, pv, meta["copy_src"], meta["copy_dst"])
-        pk, pv = _append(w, pk, pv, meta["slot_mapping"], st.k_new, st.v_new)
-        out = _attend(w, st, pk, pv, meta)
+        pk, pv = copy_kv(w, pk, pv, meta["copy_src"], meta["copy_dst"])
+        pk, pv = append_kv(w, pk, pv, meta["slot_mapping"], st.k_new, st.v_new)
+        out = attend_step(w, st, pk, pv, meta)
         results.append(dict(meta=meta, out=out))
     return results, (pk, pv)

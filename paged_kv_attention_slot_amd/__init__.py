@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     PagedKVError,
     PKV_BF16,
     PKV_F32,
+    PKV_I8,
     copy_blocks,
     decode_partition_tokens,
     gather_kv,

@@ -28,6 +28,7 @@ PKV_ERR_HIP = -5
 PKV_ERR_STATE = -6
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_I8 = 2
 
 _i32 = ctypes.c_int32
 _p = ctypes.c_void_p
@@ -36,7 +37,8 @@ _pi32 = ctypes.POINTER(ctypes.c_int32)
 
 class PoolDesc(ctypes.Structure):
     _fields_ = [("k", _p), ("v", _p), ("num_blocks", _i32), ("block_size", _i32),
-                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32)]
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32),
+                ("k_scale", _p), ("v_scale", _p)]
 
 
 class StepDesc(ctypes.Structure):
@@ -151,6 +153,8 @@ def pkv_dtype_of(tdtype) -> int:
         return PKV_BF16
     if tdtype == torch.float32:
         return PKV_F32
+    if tdtype == torch.int8:
+        return PKV_I8
     raise ValueError(f"unsupported dtype {tdtype}")
 
 
@@ -164,20 +168,35 @@ def _dptr(t):
 
 
 class KVPool:
-    """The shared pool: K and V, each [num_blocks][num_kv_heads][16][head_dim]."""
+    """The shared pool: K and V, each [num_blocks][num_kv_heads][16][head_dim].
+    dtype torch.int8 makes an 8-bit pool: int8 codes plus float32 scales
+    k_scale / v_scale [num_blocks][num_kv_heads][16] (see pkv_pool).  Poison
+    fills unwritten positions with NaN (codes: -128, never a valid code)."""
 
     def __init__(self, num_blocks, num_kv_heads, head_dim, dtype, block_size=16, device="cuda", poison=True):
         torch = _torch()
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         self.k = torch.empty(shape, dtype=dtype, device=device)
         self.v = torch.empty(shape, dtype=dtype, device=device)
+        self.k_scale = self.v_scale = None
+        if dtype == torch.int8:
+            self.k_scale = torch.empty(shape[:3], dtype=torch.float32, device=device)
+            self.v_scale = torch.empty(shape[:3], dtype=torch.float32, device=device)
         if poison:
-            self.k.fill_(float("nan"))
-            self.v.fill_(float("nan"))
+            if dtype == torch.int8:
+                self.k.fill_(-128)
+                self.v.fill_(-128)
+                self.k_scale.fill_(float("nan"))
+                self.v_scale.fill_(float("nan"))
+            else:
+                self.k.fill_(float("nan"))
+                self.v.fill_(float("nan"))
         self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size = num_blocks, num_kv_heads, head_dim, block_size
         self.dtype = dtype
         self._desc = PoolDesc(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.block_size,
-                              self.num_kv_heads, self.head_dim, pkv_dtype_of(self.dtype))
+                              self.num_kv_heads, self.head_dim, pkv_dtype_of(self.dtype),
+                              self.k_scale.data_ptr() if self.k_scale is not None else None,
+                              self.v_scale.data_ptr() if self.v_scale is not None else None)
         self._desc_ref = ctypes.byref(self._desc)
 
     def desc(self) -> PoolDesc:

@@ -22,7 +22,7 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kv_append.hip", "decode.hip", "decode_mfma.hip", "chunk.hip", "verify.hip", "gather.hip", "attend.hip"]
+HIP_SOURCES = ["kv_append.hip", "decode.hip", "decode_mfma.hip", "decode_q8.hip", "chunk.hip", "verify.hip", "gather.hip", "attend.hip"]
 HOST_SOURCES = ["host_alloc.cpp"]
 
 # Packed-fp32 instructions are kept out of the generated code on purpose.

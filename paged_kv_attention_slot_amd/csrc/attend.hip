@@ -20,6 +20,7 @@ namespace {
 bool pool_ok(const pkv_pool *p) {
   if (!p || !p->k || !p->v) return false;
   if (p->num_blocks <= 0 || p->num_kv_heads <= 0 || p->block_size <= 0 || p->head_dim <= 0) return false;
+  if (p->dtype == PKV_I8) return p->k_scale && p->v_scale;
   return p->dtype == PKV_F32 || p->dtype == PKV_BF16;
 }
 
@@ -270,8 +271,9 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
       max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0)
     return PKV_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads != 0 || !scale_ok(scale)) return PKV_ERR_INVALID_ARG;
-  if (out_dtype != PKV_F32 && !(out_dtype == PKV_BF16 && pool->dtype == PKV_BF16)) return PKV_ERR_INVALID_ARG;
+  if (out_dtype != PKV_F32 && !(out_dtype == PKV_BF16 && pool->dtype != PKV_F32)) return PKV_ERR_INVALID_ARG;
   if (!pool_supported(pool) || num_q_heads / pool->num_kv_heads > 8) return PKV_ERR_UNSUPPORTED;
+  if (pool->dtype == PKV_I8 && max_query_len > 1) return PKV_ERR_UNSUPPORTED;  // 8-bit pools: decode rows only
   if (num_segments == 0 || total_q == 0) return PKV_OK;  // nothing to attend (nor to check further)
   if (!q_packed || !row_to_slot || !query_start || !query_len || !context_lens || !block_tables || !out)
     return PKV_ERR_INVALID_ARG;
@@ -315,6 +317,8 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.k_scale = pool->dtype == PKV_I8 ? pool->k_scale : nullptr;
+  a.v_scale = pool->dtype == PKV_I8 ? pool->v_scale : nullptr;
 
   // Multi-row segments on the chunk kernels, or on the verify kernel when
   // short (unless every multi-row segment goes row by row on the decode

@@ -34,6 +34,10 @@ struct GatherArgs {
   const uint4 *src_v;
   uint4 *dst_k;
   uint4 *dst_v;
+  const float *src_sk;   // 8-bit pools: per-row scales, [blocks][Hkv][16] (else null)
+  const float *src_sv;
+  float *dst_sk;
+  float *dst_sv;
   int32_t num_slots;
   int32_t max_blocks;
   int32_t src_blocks;
@@ -101,6 +105,13 @@ __device__ inline void gather_one(const GatherArgs &g, int b, int s, int j) {
       }
     }
   }
+  if (g.src_sk) {
+    const int64_t per_scales = static_cast<int64_t>(g.num_kv_heads) * kBlockTokens;
+    for (int64_t u = threadIdx.x; u < per_scales; u += 256) {
+      g.dst_sk[dst * per_scales + u] = g.src_sk[phys * per_scales + u];
+      g.dst_sv[dst * per_scales + u] = g.src_sv[phys * per_scales + u];
+    }
+  }
 }
 
 template <int ROW16>
@@ -153,7 +164,7 @@ int launch_gather_window(const int32_t *row_to_slot, int32_t num_segments, const
                          int32_t max_context_len, const int32_t *dst_block_start, const pkv_pool &src,
                          const pkv_pool &dst, hipStream_t stream) {
   if (num_segments == 0 || max_context_len == 0) return PKV_OK;
-  const int row16 = src.head_dim * (src.dtype == PKV_F32 ? 4 : 2) / 16;
+  const int row16 = pool_row16(src);
   const int64_t max_nb = (static_cast<int64_t>(max_context_len) + kBlockTokens - 1) / kBlockTokens;
   GatherArgs g;
   g.row_to_slot = row_to_slot;
@@ -169,13 +180,19 @@ int launch_gather_window(const int32_t *row_to_slot, int32_t num_segments, const
   g.src_blocks = src.num_blocks;
   g.dst_blocks = dst.num_blocks;
   g.num_kv_heads = src.num_kv_heads;
-  if (row16 != 8 && row16 != 16 && row16 != 32) return PKV_ERR_UNSUPPORTED;
+  const bool q8 = src.dtype == PKV_I8;
+  g.src_sk = q8 ? src.k_scale : nullptr;
+  g.src_sv = q8 ? src.v_scale : nullptr;
+  g.dst_sk = q8 ? dst.k_scale : nullptr;
+  g.dst_sv = q8 ? dst.v_scale : nullptr;
+  if (row16 != 4 && row16 != 8 && row16 != 16 && row16 != 32) return PKV_ERR_UNSUPPORTED;
   if (num_segments <= kGatherLdsSegments) {
     // a persistent grid, never more workgroups than blocks
     int64_t wg = static_cast<int64_t>(num_segments) * max_nb;
     if (wg > PKV_GATHER_WGS) wg = PKV_GATHER_WGS;
     const dim3 grid(static_cast<unsigned>(wg));
     switch (row16) {
+      case 4: gather_flat_kernel<4><<<grid, dim3(256), 0, stream>>>(g, num_segments); break;
       case 8: gather_flat_kernel<8><<<grid, dim3(256), 0, stream>>>(g, num_segments); break;
       case 16: gather_flat_kernel<16><<<grid, dim3(256), 0, stream>>>(g, num_segments); break;
       default: gather_flat_kernel<32><<<grid, dim3(256), 0, stream>>>(g, num_segments); break;
@@ -187,6 +204,7 @@ int launch_gather_window(const int32_t *row_to_slot, int32_t num_segments, const
     if (gy < 1) gy = 1;
     const dim3 grid(static_cast<unsigned>(num_segments), static_cast<unsigned>(gy));
     switch (row16) {
+      case 4: gather_window_kernel<4><<<grid, dim3(256), 0, stream>>>(g); break;
       case 8: gather_window_kernel<8><<<grid, dim3(256), 0, stream>>>(g); break;
       case 16: gather_window_kernel<16><<<grid, dim3(256), 0, stream>>>(g); break;
       default: gather_window_kernel<32><<<grid, dim3(256), 0, stream>>>(g); break;

@@ -54,9 +54,112 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   }
 }
 
+// 8-bit pools: each (token, KV head) row of bf16 input becomes head_dim int8
+// codes plus one float32 scale (the format stated at pkv_pool in pagedkv.h):
+// amax over the row, inv = 127 / amax and scale = amax / 127 as correctly
+// rounded divisions, code = rint(x * inv) (the float32 product, ties to even)
+// clamped to +-127; a zero row gives codes 0 and scale 0.  R = D / 8 lanes
+// share a row, 8 values each: a 16-byte load of bf16, an R-lane max, an
+// 8-byte store of codes; the row's first lane stores the scale.
+struct Q8AppendArgs {
+  const int32_t *slot_mapping;
+  const uint4 *k_new;          // [T][Hkv][D] bf16, as 16-byte units
+  const uint4 *v_new;
+  uint2 *codes_k;              // [blocks][Hkv][16][D] int8, as 8-byte units
+  uint2 *codes_v;
+  float *scale_k;              // [blocks][Hkv][16]
+  float *scale_v;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int64_t pool_slots;
+  const int32_t *stage_src;
+  int32_t *stage_dst;
+  int32_t stage_len;
+};
+
+template <int R>
+__device__ __forceinline__ void quantize_row8(const uint4 in, int li, uint2 *codes, float *scale) {
+  float x[8];
+  const unsigned w[4] = {in.x, in.y, in.z, in.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int m = 1; m < R; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  unsigned lo = 0, hi = 0;
+  float sc = 0.f;
+  if (amax > 0.f) {
+    const float inv = __fdiv_rn(127.f, amax);
+    sc = __fdiv_rn(amax, 127.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float prod = x[i] * inv;
+      const int c = static_cast<int>(fminf(fmaxf(rintf(prod), -127.f), 127.f));
+      const unsigned byte = static_cast<unsigned>(c) & 0xFFu;
+      if (i < 4) lo |= byte << (8 * i);
+      else hi |= byte << (8 * (i - 4));
+    }
+  }
+  *codes = make_uint2(lo, hi);
+  if (li == 0) *scale = sc;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void kv_append_q8_kernel(Q8AppendArgs a) {
+  constexpr int R = D / 8;                    // lanes per row
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = tid; i < a.stage_len; i += nthreads) a.stage_dst[i] = a.stage_src[i];
+  const int li = static_cast<int>(tid % R);
+  const int64_t rows = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads;
+  for (int64_t r = tid / R; r < rows; r += nthreads / R) {
+    const int64_t t = r / a.num_kv_heads;
+    const int64_t h = r - t * a.num_kv_heads;
+    const int64_t s = a.slot_mapping[t];
+    if (s < 0 || s >= a.pool_slots) continue;   // the whole row's lanes skip together
+    const int64_t blk = s / kBlockTokens;
+    const int64_t off = s - blk * kBlockTokens;
+    const int64_t drow = (blk * a.num_kv_heads + h) * kBlockTokens + off;
+    quantize_row8<R>(a.k_new[r * R + li], li, a.codes_k + drow * R + li, a.scale_k + drow);
+    quantize_row8<R>(a.v_new[r * R + li], li, a.codes_v + drow * R + li, a.scale_v + drow);
+  }
+}
+
 int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new, int32_t num_tokens,
                      const pkv_pool &pool, hipStream_t stream, const int32_t *stage_src, int32_t *stage_dst,
                      int32_t stage_len) {
+  if (pool.dtype == PKV_I8) {
+    Q8AppendArgs a;
+    a.slot_mapping = slot_mapping;
+    a.k_new = static_cast<const uint4 *>(k_new);
+    a.v_new = static_cast<const uint4 *>(v_new);
+    a.codes_k = static_cast<uint2 *>(pool.k);
+    a.codes_v = static_cast<uint2 *>(pool.v);
+    a.scale_k = pool.k_scale;
+    a.scale_v = pool.v_scale;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = pool.num_kv_heads;
+    a.pool_slots = static_cast<int64_t>(pool.num_blocks) * pool.block_size;
+    a.stage_src = stage_src;
+    a.stage_dst = stage_dst;
+    a.stage_len = stage_src && stage_dst ? stage_len : 0;
+    const int64_t lanes = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * (pool.head_dim / 8);
+    int64_t blocks = ((lanes > a.stage_len ? lanes : a.stage_len) + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 65536) blocks = 65536;
+    if (pool.head_dim == 128)
+      kv_append_q8_kernel<128><<<dim3(blocks), dim3(256), 0, stream>>>(a);
+    else if (pool.head_dim == 64)
+      kv_append_q8_kernel<64><<<dim3(blocks), dim3(256), 0, stream>>>(a);
+    else
+      return PKV_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  }
   const int row16 = pool.head_dim * (pool.dtype == PKV_F32 ? 4 : 2) / 16;
   const int64_t units = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * row16;
   const int threads = 256;
@@ -89,10 +192,11 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
 // into block dst[c].  Workgroup (x, c) copies 256 16-byte units of pair c's
 // [Hkv][block][row16] span; both sides are contiguous, so every access is
 // coalesced.  The ids may live in pinned host memory (read once per thread).
+// An 8-bit pool's scales ([Hkv][16] floats per block) travel with the codes.
 template <int ROW16>
 __global__ __launch_bounds__(256) void kv_copy_blocks_kernel(const int32_t *src, const int32_t *dst, uint4 *pool_k,
-                                                             uint4 *pool_v, int32_t num_blocks,
-                                                             int32_t num_kv_heads) {
+                                                             uint4 *pool_v, float *scale_k, float *scale_v,
+                                                             int32_t num_blocks, int32_t num_kv_heads) {
   const int64_t per_block = static_cast<int64_t>(num_kv_heads) * kBlockTokens * ROW16;
   const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (u >= per_block) return;
@@ -100,20 +204,34 @@ __global__ __launch_bounds__(256) void kv_copy_blocks_kernel(const int32_t *src,
   if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
   pool_k[d * per_block + u] = pool_k[s * per_block + u];
   pool_v[d * per_block + u] = pool_v[s * per_block + u];
+  const int64_t per_scales = static_cast<int64_t>(num_kv_heads) * kBlockTokens;
+  if (scale_k && u < per_scales) {
+    scale_k[d * per_scales + u] = scale_k[s * per_scales + u];
+    scale_v[d * per_scales + u] = scale_v[s * per_scales + u];
+  }
+}
+
+int pool_row16(const pkv_pool &pool) {
+  const int elem = pool.dtype == PKV_F32 ? 4 : (pool.dtype == PKV_I8 ? 1 : 2);
+  return pool.head_dim * elem / 16;
 }
 
 int launch_copy_blocks(const int32_t *src, const int32_t *dst, int32_t num_copies, const pkv_pool &pool,
                        hipStream_t stream) {
   if (num_copies <= 0) return PKV_OK;
   if (num_copies > 65535) return PKV_ERR_INVALID_ARG;
-  const int row16 = pool.head_dim * (pool.dtype == PKV_F32 ? 4 : 2) / 16;
+  const int row16 = pool_row16(pool);
   const int64_t per_block = static_cast<int64_t>(pool.num_kv_heads) * kBlockTokens * row16;
   const dim3 grid(static_cast<unsigned>((per_block + 255) / 256), static_cast<unsigned>(num_copies));
   uint4 *k = static_cast<uint4 *>(pool.k), *v = static_cast<uint4 *>(pool.v);
+  float *sk = pool.dtype == PKV_I8 ? pool.k_scale : nullptr;
+  float *sv = pool.dtype == PKV_I8 ? pool.v_scale : nullptr;
+  const int nb = pool.num_blocks, hkv = pool.num_kv_heads;
   switch (row16) {
-    case 8: kv_copy_blocks_kernel<8><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, pool.num_blocks, pool.num_kv_heads); break;
-    case 16: kv_copy_blocks_kernel<16><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, pool.num_blocks, pool.num_kv_heads); break;
-    case 32: kv_copy_blocks_kernel<32><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, pool.num_blocks, pool.num_kv_heads); break;
+    case 4: kv_copy_blocks_kernel<4><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
+    case 8: kv_copy_blocks_kernel<8><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
+    case 16: kv_copy_blocks_kernel<16><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
+    case 32: kv_copy_blocks_kernel<32><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
     default: return PKV_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;

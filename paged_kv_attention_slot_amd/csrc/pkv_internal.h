@@ -80,6 +80,18 @@ constexpr int kDecodeStages = PKV_DECODE_STAGES;
 #endif
 constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 
+// 8-bit pools: tiles in flight per decode wavefront (half the bytes of a
+// bf16 tile, so more of them), and when the launch has few waves.
+#ifndef PKV_DECODE_Q8_STAGES
+#define PKV_DECODE_Q8_STAGES 1
+#endif
+#ifndef PKV_DECODE_Q8_MIN_WAVES
+#define PKV_DECODE_Q8_MIN_WAVES 3   // waves per SIMD the register budget must allow
+#endif
+#ifndef PKV_DECODE_Q8_STAGES_FEW
+#define PKV_DECODE_Q8_STAGES_FEW 3
+#endif
+
 // Multi-row segments with fewer than this many 128-row tiles split their
 // key range so that (row tiles x splits) reaches it; partial slots per
 // (segment, KV head) = that target * 128 (chunk_split_slots).
@@ -208,6 +220,8 @@ struct AttendArgs {
   int32_t out_bf16;
   float scale;          // softmax scale
   float scale_log2;     // scale * log2(e)
+  const float *k_scale; // 8-bit pools: [num_blocks][Hkv][16] per-row scales (else null)
+  const float *v_scale;
 };
 
 // KV append; optionally also copies stage_len int32 of step metadata from
@@ -222,8 +236,11 @@ int launch_gather_window(const int32_t *row_to_slot, int32_t num_segments, const
                          int32_t max_context_len, const int32_t *dst_block_start, const pkv_pool &src,
                          const pkv_pool &dst, hipStream_t stream);
 
-// Whole-block copies src[c] -> dst[c] (K and V, every head); the ids may sit
-// in device-readable pinned host memory.
+// 16-byte units per (token, head) row of a pool (head_dim x element bytes / 16).
+int pool_row16(const pkv_pool &pool);
+
+// Whole-block copies src[c] -> dst[c] (K and V, every head, with an 8-bit
+// pool's scales); the ids may sit in device-readable pinned host memory.
 int launch_copy_blocks(const int32_t *src, const int32_t *dst, int32_t num_copies, const pkv_pool &pool,
                        hipStream_t stream);
 
@@ -243,6 +260,9 @@ int launch_verify(const AttendArgs &a, int32_t head_dim, int32_t max_context_len
 int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len, bool need_reduce,
                   int64_t work_waves, hipStream_t stream);
 
+// Decode rows over an 8-bit pool (codes + per-row scales).
+int launch_decode_q8(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
+                     hipStream_t stream);
 int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
                        hipStream_t stream);
 

@@ -299,12 +299,12 @@ def _gather_then_attend(w, eng, meta, q):
     pool with pkv_gather_kv, then attend over it through identity tables.
     Returns (out, gathered pool, per-segment first block, block counts)."""
     import torch
-    from workloads.drive import torch_dtype
+    from workloads.drive import pool_torch_dtype
     h = meta.host
     r2s, ctx = h["row_to_slot"], h["context_lens"]
     nbs = [-(-int(ctx[s]) // 16) for s in r2s]
     start = np.concatenate([[0], np.cumsum(nbs)[:-1]]).astype(np.int32)
-    dst = pk.KVPool(int(sum(nbs)) + 1, w.num_kv_heads, w.head_dim, torch_dtype(w.dtype))
+    dst = pk.KVPool(int(sum(nbs)) + 1, w.num_kv_heads, w.head_dim, pool_torch_dtype(w))
     dense = np.zeros((w.max_slots, max(nbs)), np.int32)
     for b, s in enumerate(r2s):
         dense[s, :nbs[b]] = start[b] + np.arange(nbs[b])
@@ -347,3 +347,90 @@ def test_gather_then_attend_equals_paged_bitwise(name, gpu_available):
                                                                                     w.head_dim)[:L]
             want = gather_sequence(want_pool, tables[s], L, 16)
             assert np.array_equal(got, _oracle_bits(want)), f"segment {b}"
+
+
+# ------------------------------------------------------------------ 8-bit KV
+Q8_EDGE = [
+    [(0, 0, 1)],                                  # L = 1
+    [(0, 15, 1), (1, 16, 1), (2, 31, 1)],         # block edges
+    [(0, 511, 1), (1, 512, 1), (2, 1023, 1), (3, 1024, 1), (4, 2047, 1), (5, 2048, 1)],   # partition edges
+    [(5, 3000, 1), (2, 7, 1)],                    # slots out of order
+]
+
+
+def _q8_workload(seqs, d, hq, hkv, seed=7):
+    w = make_custom(seqs, dtype="bf16", hq=hq, hkv=hkv, d=d, seed=seed)
+    w.kv_quant = "q8"
+    return w
+
+
+def _q8_pool_check(eng, pools):
+    (ck, sk), (cv, sv) = pools
+    assert np.array_equal(eng.pool.k.cpu().numpy(), ck)
+    assert np.array_equal(eng.pool.v.cpu().numpy(), cv)
+    assert np.array_equal(eng.pool.k_scale.cpu().numpy().view(np.uint32), sk.view(np.uint32))
+    assert np.array_equal(eng.pool.v_scale.cpu().numpy().view(np.uint32), sv.view(np.uint32))
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+def test_q8_config3_append_bit_exact_and_attention(fused, gpu_available):
+    """Config 3 with an 8-bit pool: codes and scales bit-exact with the
+    oracle's quantizer over the whole pool (poison included); attention
+    within 1e-2 of the oracle's fp64 attention over code * scale."""
+    _log(f"q8 config 3q fused={fused}")
+    w = _workload("3q")
+    eng, outs = _run_gpu(w, fused=fused)
+    res, pools = _oracle("3q")
+    _q8_pool_check(eng, pools)
+    _check_close("config 3q", outs[0][0], res[0]["out"], TOL["bf16"])
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 8), (128, 40, 8), (64, 8, 1), (128, 32, 4)])
+@pytest.mark.parametrize("case", range(len(Q8_EDGE)))
+def test_q8_edge_cases(d, hq, hkv, case, gpu_available):
+    _log(f"q8 edge case {case} D{d} {hq}/{hkv}")
+    w = _q8_workload(Q8_EDGE[case], d, hq, hkv, seed=40 + case)
+    eng, outs = _run_gpu(w)
+    res, pools = run_workload(w)
+    _q8_pool_check(eng, pools)
+    _check_close(f"q8 edge {case}", outs[0][0], res[0]["out"], TOL["bf16"])
+
+
+def test_q8_zero_rows_and_bf16_output(gpu_available):
+    """Rows of zeros quantize to codes 0 with scale 0 and attend as zeros;
+    bf16 output is the fp32 result rounded to nearest even."""
+    import torch
+    w = _q8_workload([(0, 300, 1), (1, 40, 1)], 128, 16, 8, seed=61)
+    for slot, hk, hv in w.history:
+        hk[::7] = 0                               # every 7th token's K rows all zero
+        hv[::5] = 0
+    _, outs = _run_gpu(w)
+    _, outs_b = _run_gpu(w, out_dtype=torch.bfloat16)
+    res, _ = run_workload(w)
+    _check_close("q8 zero rows", outs[0][0], res[0]["out"], TOL["bf16"])
+    f = outs[0][0].cpu()
+    assert torch.equal(outs_b[0][0].cpu(), f.to(torch.bfloat16))
+
+
+def test_q8_copy_on_write_and_gather(gpu_available):
+    """On an 8-bit pool the copy-on-write copies and the gather carry the
+    scales with the codes: the prefix workload matches the oracle and the
+    cold run bit for bit, and gather-then-attend equals paged attention."""
+    from workloads import make_prefix_share
+    # one-token suffixes: 8-bit pools attend decode rows only
+    wa, wc = make_prefix_share(False, suffixes=(1,) * 8), make_prefix_share(True, suffixes=(1,) * 8)
+    wa.kv_quant = wc.kv_quant = "q8"
+    _log("q8 prefix adoption")
+    ea, oa = _run_gpu(wa, fused=True)
+    _, oc = _run_gpu(wc, fused=True)
+    res, pools = run_workload(wa)
+    _q8_pool_check(ea, pools)
+    assert len(res[0]["meta"]["copy_src"]) == 7
+    for i, ((a, _), (c, _), r) in enumerate(zip(oa, oc, res)):
+        _check_close(f"q8 prefix step {i}", a, r["out"], TOL["bf16"])
+        assert np.array_equal(a.cpu().numpy().view(np.int32), c.cpu().numpy().view(np.int32))
+    from workloads.drive import step_tensors
+    out_paged, meta = oa[-1]
+    _, _, q = step_tensors(wa, len(wa.steps) - 1)
+    out, _, _, _ = _gather_then_attend(wa, ea, meta, q)
+    assert np.array_equal(out.cpu().numpy().view(np.int32), out_paged.cpu().numpy().view(np.int32))

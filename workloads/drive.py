@@ -22,9 +22,16 @@ def torch_dtype(dtype: str):
     return torch.float32 if dtype == "f32" else torch.bfloat16
 
 
+def pool_torch_dtype(w):
+    """The pool's element type: the workload dtype, or int8 codes for an
+    8-bit KV workload (whose inputs stay bf16)."""
+    import torch
+    return torch.int8 if getattr(w, "kv_quant", "") == "q8" else torch_dtype(w.dtype)
+
+
 def make_engine(engine_cls, w, device="cuda", free_order=None, poison=True):
     return engine_cls(num_blocks=w.num_blocks, num_kv_heads=w.num_kv_heads, num_q_heads=w.num_q_heads,
-                      head_dim=w.head_dim, dtype=torch_dtype(w.dtype), max_slots=w.max_slots,
+                      head_dim=w.head_dim, dtype=pool_torch_dtype(w), max_slots=w.max_slots,
                       max_blocks_per_seq=w.max_blocks_per_seq,
                       free_order=w.free_order if free_order is None else free_order, device=device, poison=poison)
 

@@ -116,7 +116,8 @@ def run_mixed(args, w, pk, torch, dev):
     kv, alg = decode_bytes(w, dec_lens, w.elem_bytes)
     fl = chunk_flops(w, st.segments, lens)
     # K and V of every cached token of the multi-row segments, once
-    mr_kv = sum(2 * L * w.num_kv_heads * w.head_dim * w.elem_bytes for seg, L in zip(st.segments, lens) if seg.n > 1)
+    row = w.head_dim + 4 if getattr(w, "kv_quant", "") == "q8" else w.head_dim * w.elem_bytes
+    mr_kv = sum(2 * L * w.num_kv_heads * row for seg, L in zip(st.segments, lens) if seg.n > 1)
     return {"metric": f"mixed-step latency, config {w.name}", "value": round(wall / args.steps * 1e3, 4),
             "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(wall / args.steps * 1e3, 4), "step_gpu_ms_avg": round(att * 1e3, 4),

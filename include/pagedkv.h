@@ -81,8 +81,9 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 } pkv_dtype;
  * Queries (q_packed) on an 8-bit pool are bf16 and are used as fp16 (exact
  * for |q| below 65504; magnitudes under 2^-14 keep fp16's subnormal
  * precision); output is float32 or bf16.
- * Attention on an 8-bit pool is built for decode rows (query_len 1) only:
- * max_query_len > 1 gives PKV_ERR_UNSUPPORTED. */
+ * On an 8-bit pool, multi-row segments (prompt chunks, drafts) run row by
+ * row on the decode path: correct for any segment, but each row reads its
+ * own window, so long chunks cost far more HBM traffic than on bf16. */
 typedef struct {
   void *k;              /* device [num_blocks][num_kv_heads][block_size][head_dim] */
   void *v;              /* device, same shape and dtype as k                        */

@@ -273,7 +273,6 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   if (num_q_heads % pool->num_kv_heads != 0 || !scale_ok(scale)) return PKV_ERR_INVALID_ARG;
   if (out_dtype != PKV_F32 && !(out_dtype == PKV_BF16 && pool->dtype != PKV_F32)) return PKV_ERR_INVALID_ARG;
   if (!pool_supported(pool) || num_q_heads / pool->num_kv_heads > 8) return PKV_ERR_UNSUPPORTED;
-  if (pool->dtype == PKV_I8 && max_query_len > 1) return PKV_ERR_UNSUPPORTED;  // 8-bit pools: decode rows only
   if (num_segments == 0 || total_q == 0) return PKV_OK;  // nothing to attend (nor to check further)
   if (!q_packed || !row_to_slot || !query_start || !query_len || !context_lens || !block_tables || !out)
     return PKV_ERR_INVALID_ARG;

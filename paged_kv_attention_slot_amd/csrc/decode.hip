@@ -443,7 +443,6 @@ int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t 
   const int64_t items_bound = rows * (parts > 0 ? parts : 1) * a.num_kv_heads;
   int st;
   if (dtype == PKV_I8) {
-    if (a.multirow) return PKV_ERR_UNSUPPORTED;
     const int stages =
         work_waves >= 0 && work_waves < PKV_DECODE_FEW_WAVES ? PKV_DECODE_Q8_STAGES_FEW : PKV_DECODE_Q8_STAGES;
     st = launch_decode_q8(a, head_dim, max_context_len, stages, stream);

@@ -6,7 +6,9 @@
 // The work and its split are those of the bf16 MFMA decode kernel - one
 // wavefront per (decode row, KV head g, split-context partition), all G query
 // heads of the group sharing every tile, online softmax, partition partials
-// merged by the reduce kernel - with half the tile bytes:
+// merged by the reduce kernel - with half the tile bytes.  Multi-row
+// segments (on an 8-bit pool every one) go row by row: row i of a segment is
+// a decode row over its first L - n + i + 1 keys.
 //   * the K and V code tiles (16 x head_dim bytes each) and their 2 x 16
 //     scales go from HBM straight into LDS staging (global_load_lds_dwordx4
 //     for codes, one global_load_lds_dword for the scales), S tiles in
@@ -82,9 +84,13 @@ __device__ __forceinline__ int q8_parts(int L) {
   return (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
 }
 
+// Work units of segment b: its partitions; in multi-row mode every row of
+// every segment takes the segment's partition count (a row's partitions past
+// its own causal limit are empty).
 __device__ __forceinline__ int q8_units(const AttendArgs &a, int b) {
   const SegInfo s = seg_info(a, b);
-  return s.ok && s.n == 1 ? q8_parts(s.L) : 0;
+  if (!s.ok || (!a.multirow && s.n != 1)) return 0;
+  return (a.multirow ? s.n : 1) * q8_parts(s.L);
 }
 
 template <int D, int S>
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
   const int lg = lane >> 4;
 
   const SegInfo mine = seg_info(a, lane);
-  const int u0 = mine.ok && mine.n == 1 ? q8_parts(mine.L) : 0;
+  const int u0 = mine.ok && (a.multirow || mine.n == 1) ? (a.multirow ? mine.n : 1) * q8_parts(mine.L) : 0;
   const int incl0 = wave_inclusive_scan(u0);
   int total = __shfl(incl0, kWave - 1);
   if (a.num_segments > kWave) total = count_units(a.num_segments, [&](int b) { return q8_units(a, b); });
@@ -110,28 +116,32 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
   for (int64_t f = blockIdx.x; f < items; f += gridDim.x) {
     const int unit = static_cast<int>(f / a.num_kv_heads);
     const int g = static_cast<int>(f - static_cast<int64_t>(unit) * a.num_kv_heads);
-    int b, part;
+    int b, rest;
     SegInfo si;
     if (unit < __shfl(incl0, kWave - 1)) {
       const unsigned long long mask = __ballot(incl0 > unit);
       b = __ffsll(static_cast<long long>(mask)) - 1;
-      part = unit - (__shfl(incl0, b) - __shfl(u0, b));
+      rest = unit - (__shfl(incl0, b) - __shfl(u0, b));
       si.slot = __builtin_amdgcn_readlane(mine.slot, b);
       si.L = __builtin_amdgcn_readlane(mine.L, b);
-      si.n = 1;
+      si.n = __builtin_amdgcn_readlane(mine.n, b);
       si.row0 = __builtin_amdgcn_readlane(mine.row0, b);
       si.ok = true;
     } else {
-      b = find_unit(a.num_segments, unit, [&](int bb) { return q8_units(a, bb); }, &part);
+      b = find_unit(a.num_segments, unit, [&](int bb) { return q8_units(a, bb); }, &rest);
       si = seg_info(a, b);
       if (!si.ok) continue;
     }
     const int np = q8_parts(si.L);
-    const int row = si.row0;
+    const int ri = a.multirow ? rest / np : 0;         // row of the segment
+    const int part = rest - ri * np;
+    const int row = si.row0 + ri;
+    const int prow = a.multirow ? row : b;             // partials index
+    const int limit = si.L - si.n + ri + 1;            // keys visible to this row
     const int tok0 = part * PT;
-    const int tok1 = min(si.L, tok0 + PT);
+    const int tok1 = min(limit, tok0 + PT);            // tok0 >= tok1: an empty partition
     const int j0 = tok0 / kBlockTokens;
-    const int nb = (tok1 + kBlockTokens - 1) / kBlockTokens - j0;
+    const int nb = tok1 > tok0 ? (tok1 + kBlockTokens - 1) / kBlockTokens - j0 : 0;
     const int head = l16;                    // MFMA column = query head of the group
     const bool hv = head < G;
     const int hq = g * G + (hv ? head : 0);
@@ -287,10 +297,13 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     };
 
     // S tiles in flight.  Past the last tile the prefetch re-reads the last
-    // tile (a cache hit) so every wait below has a static count.
-    issue(0, 0);
-    if constexpr (S > 1) issue(1, min(1, nb - 1));
-    if constexpr (S > 2) issue(2, min(2, nb - 1));
+    // tile (a cache hit) so every wait below has a static count.  An empty
+    // partition loads nothing and leaves m = -FLT_MAX, l = 0, O = 0.
+    if (nb > 0) {
+      issue(0, 0);
+      if constexpr (S > 1) issue(1, min(1, nb - 1));
+      if constexpr (S > 2) issue(2, min(2, nb - 1));
+    }
     for (int jj = 0; jj < nb; jj += S) {
 #pragma unroll
       for (int st = 0; st < S; ++st) {
@@ -343,7 +356,7 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
         }
       }
     } else {
-      const int64_t pidx = (static_cast<int64_t>(b) * a.num_q_heads + hq) * a.part_max + part;
+      const int64_t pidx = (static_cast<int64_t>(prow) * a.num_q_heads + hq) * a.part_max + part;
       float *pa = a.part_acc + pidx * D + lg * 4;
 #pragma unroll
       for (int dt = 0; dt < M::kDTiles; ++dt)
@@ -367,7 +380,8 @@ int launch_q8_d(const AttendArgs &a, int G, int64_t grid, int stages, hipStream_
 int launch_decode_q8(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
-  const int64_t items_bound = static_cast<int64_t>(a.num_segments) * (parts > 0 ? parts : 1) * a.num_kv_heads;
+  const int64_t rows = a.multirow ? static_cast<int64_t>(a.total_q) : a.num_segments;
+  const int64_t items_bound = rows * (parts > 0 ? parts : 1) * a.num_kv_heads;
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * kDecodeWavesPerCU;
   const int64_t grid = items_bound < cap ? items_bound : cap;
   if (grid <= 0) return PKV_OK;

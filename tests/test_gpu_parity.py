@@ -434,3 +434,29 @@ def test_q8_copy_on_write_and_gather(gpu_available):
     _, _, q = step_tensors(wa, len(wa.steps) - 1)
     out, _, _, _ = _gather_then_attend(wa, ea, meta, q)
     assert np.array_equal(out.cpu().numpy().view(np.int32), out_paged.cpu().numpy().view(np.int32))
+
+
+@pytest.mark.parametrize("case", [4, 5, 6])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 40, 8)])
+def test_q8_multirow_edge_cases(case, d, hq, hkv, gpu_available):
+    """Multi-row segments on an 8-bit pool (row by row on the decode path):
+    tiny prompts, drafts, and chunks whose rows span several partitions."""
+    _log(f"q8 multirow case {case} D{d} {hq}/{hkv}")
+    w = _q8_workload(EDGE_SEQS[case], d, hq, hkv, seed=70 + case)
+    eng, outs = _run_gpu(w)
+    res, pools = run_workload(w)
+    _q8_pool_check(eng, pools)
+    _check_close(f"q8 multirow {case}", outs[0][0], res[0]["out"], TOL["bf16"])
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+def test_q8_config5(fused, gpu_available):
+    """Config 5 on an 8-bit pool: 16-row drafts, then rollback, slot reuse
+    and a 3000-row prompt, all row by row."""
+    _log(f"q8 config 5 fused={fused}")
+    w = _workload("5q")
+    eng, outs = _run_gpu(w, fused=fused)
+    res, pools = _oracle("5q")
+    _q8_pool_check(eng, pools)
+    for i, ((out, _), r) in enumerate(zip(outs, res)):
+        _check_close(f"q8 config 5 step {i}", out, r["out"], TOL["bf16"])

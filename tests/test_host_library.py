@@ -60,11 +60,13 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
         step.num_slots = 1
         step.scale = bad
         assert lib.pkv_mixed_step(ctypes.byref(step), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
-    # 8-bit pools: scales required; decode rows only
+    # 8-bit pools: scales required; multi-row segments go row by row, whose
+    # split-context partials need workspace
     d8 = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, pk.PKV_I8, 16, 16)
     d8_noscale = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, pk.PKV_I8)
-    assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1, 2, 16, ctypes.byref(d8), 1.0, 16, 0,
-                                None, 0, None) == pk.binding.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_paged_attend(16, 4, 4, 16, 16, 16, 1, 16, 16, 1, 1000, 4, 5000, ctypes.byref(d8), 1.0, 16, 0,
+                                None, 0, None) == pk.binding.PKV_ERR_WORKSPACE
+    assert lib.pkv_paged_attend_workspace_bytes(1, 4, 4, 4, 5000, ctypes.byref(d8)) > 0
     assert lib.pkv_paged_attend(16, 1, 4, 16, 16, 16, 1, 16, 16, 1, 1, 1, 16, ctypes.byref(d8_noscale), 1.0, 16,
                                 0, None, 0, None) == pk.binding.PKV_ERR_INVALID_ARG
     assert lib.pkv_kv_append(None, None, None, 4, ctypes.byref(d8_noscale), None) == pk.binding.PKV_ERR_INVALID_ARG

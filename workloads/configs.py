@@ -185,6 +185,15 @@ def _config3q():
     return w
 
 
+def _config5q():
+    """Config 5 (same seed and values) with an 8-bit pool."""
+    w = _config5()
+    w.name = "5q"
+    w.kv_quant = "q8"
+    w.description = "speculative verify + slot reuse on an 8-bit KV pool"
+    return w
+
+
 def _config4(chunk):
     draw = _Draw(1004, "bf16")
     if chunk == 2048:
@@ -302,6 +311,8 @@ def make_workload(name: str) -> Workload:
         return _config4(512)
     if name == "5":
         return _config5()
+    if name == "5q":
+        return _config5q()
     if name.startswith("gather-"):
         return make_gather_ablation(int(name.split("-", 1)[1]))
     if name == "prefix":

@@ -6,9 +6,12 @@
 // The work and its split are those of the bf16 MFMA decode kernel - one
 // wavefront per (decode row, KV head g, split-context partition), all G query
 // heads of the group sharing every tile, online softmax, partition partials
-// merged by the reduce kernel - with half the tile bytes.  Multi-row
-// segments (on an 8-bit pool every one) go row by row: row i of a segment is
-// a decode row over its first L - n + i + 1 keys.
+// merged by the reduce kernel - with half the tile bytes.  The 16 MFMA
+// columns are a segment's (row, head) pairs: G heads of one row for a decode
+// row; for a multi-row segment (prompt chunk, drafts) up to 16 pairs of
+// consecutive rows per wavefront, each column with its own causal limit
+// (row i sees keys 0 .. L - n + i), so the codes are read once per column
+// group rather than once per row.
 //   * the K and V code tiles (16 x head_dim bytes each) and their 2 x 16
 //     scales go from HBM straight into LDS staging (global_load_lds_dwordx4
 //     for codes, one global_load_lds_dword for the scales), S tiles in
@@ -84,13 +87,16 @@ __device__ __forceinline__ int q8_parts(int L) {
   return (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
 }
 
-// Work units of segment b: its partitions; in multi-row mode every row of
-// every segment takes the segment's partition count (a row's partitions past
-// its own causal limit are empty).
-__device__ __forceinline__ int q8_units(const AttendArgs &a, int b) {
+// 16-wide MFMA column groups of a segment's (row, head) pairs.
+__device__ __forceinline__ int q8_groups(int n, int G) { return (n * G + 15) / 16; }
+
+// Work units of segment b: its column groups times its partitions (decode
+// rows: one group of G heads).  Without multi-row mode only decode rows
+// count.
+__device__ __forceinline__ int q8_units(const AttendArgs &a, int b, int G) {
   const SegInfo s = seg_info(a, b);
   if (!s.ok || (!a.multirow && s.n != 1)) return 0;
-  return (a.multirow ? s.n : 1) * q8_parts(s.L);
+  return q8_groups(s.n, G) * q8_parts(s.L);
 }
 
 template <int D, int S>
@@ -106,10 +112,10 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
   const int lg = lane >> 4;
 
   const SegInfo mine = seg_info(a, lane);
-  const int u0 = mine.ok && (a.multirow || mine.n == 1) ? (a.multirow ? mine.n : 1) * q8_parts(mine.L) : 0;
+  const int u0 = mine.ok && (a.multirow || mine.n == 1) ? q8_groups(mine.n, G) * q8_parts(mine.L) : 0;
   const int incl0 = wave_inclusive_scan(u0);
   int total = __shfl(incl0, kWave - 1);
-  if (a.num_segments > kWave) total = count_units(a.num_segments, [&](int b) { return q8_units(a, b); });
+  if (a.num_segments > kWave) total = count_units(a.num_segments, [&](int b) { return q8_units(a, b, G); });
   const int64_t items = static_cast<int64_t>(total) * a.num_kv_heads;
   const float c_log2 = a.scale_log2;
 
@@ -128,23 +134,30 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
       si.row0 = __builtin_amdgcn_readlane(mine.row0, b);
       si.ok = true;
     } else {
-      b = find_unit(a.num_segments, unit, [&](int bb) { return q8_units(a, bb); }, &rest);
+      b = find_unit(a.num_segments, unit, [&](int bb) { return q8_units(a, bb, G); }, &rest);
       si = seg_info(a, b);
       if (!si.ok) continue;
     }
     const int np = q8_parts(si.L);
-    const int ri = a.multirow ? rest / np : 0;         // row of the segment
-    const int part = rest - ri * np;
+    const int cg = rest / np;                          // column group
+    const int part = rest - cg * np;
+    // MFMA column l16 = (row, head) pair cg * 16 + l16 of the segment
+    const int pair = cg * 16 + l16;
+    const bool hv = pair < si.n * G;
+    const int ri = hv ? pair / G : 0;
+    const int hq = g * G + (hv ? pair - ri * G : 0);
     const int row = si.row0 + ri;
     const int prow = a.multirow ? row : b;             // partials index
-    const int limit = si.L - si.n + ri + 1;            // keys visible to this row
+    const int limit = si.L - si.n + ri + 1;            // keys visible to this column's row
+    // wave-uniform bounds: keys the group's last and first rows see
+    const int ri_hi = min(si.n - 1, (cg * 16 + 15) / G);
+    const int ri_lo = min(si.n - 1, (cg * 16) / G);
     const int tok0 = part * PT;
-    const int tok1 = min(limit, tok0 + PT);            // tok0 >= tok1: an empty partition
+    const int tok1 = min(si.L - si.n + ri_hi + 1, tok0 + PT);   // tok0 >= tok1: an empty partition
+    const int tok_full = min(si.L - si.n + ri_lo + 1, tok1);    // every column sees keys below this
+    const int lim = hv ? min(limit, tok1) : tok1;
     const int j0 = tok0 / kBlockTokens;
     const int nb = tok1 > tok0 ? (tok1 + kBlockTokens - 1) / kBlockTokens - j0 : 0;
-    const int head = l16;                    // MFMA column = query head of the group
-    const bool hv = head < G;
-    const int hq = g * G + (hv ? head : 0);
 
     int phys_lane = 0;
     if (lane < nb) {
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
                        auto partial_tag) {
       constexpr bool PARTIAL = decltype(partial_tag)::value;
       const int tokbase = (j0 + jj) * kBlockTokens;
-      const int valid = tok1 - tokbase;       // tokens of this tile in range (< 16 only if PARTIAL)
+      const int valid = lim - tokbase;        // this column's tokens of the tile (< 16 only if PARTIAL)
       floatx4_t s = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < M::kKSteps; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kk], qh[kk], s, 0, 0, 0);
@@ -320,7 +333,7 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if constexpr (S > 1) issue(st, min(jj + st + S, nb - 1));
         else if (jj + 1 < nb) issue(0, jj + 1);
-        if ((j0 + jj + st + 1) * kBlockTokens > tok1)
+        if ((j0 + jj + st + 1) * kBlockTokens > tok_full)
           compute(ka, ks, vs, jj + st, std::true_type{});
         else
           compute(ka, ks, vs, jj + st, std::false_type{});

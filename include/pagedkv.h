@@ -179,10 +179,11 @@ int pkv_gather_kv(const int32_t *row_to_slot, int32_t num_segments, const int32_
  *                 nearest even).
  *   workspace     device scratch of at least pkv_paged_attend_workspace_bytes
  *                 bytes (may be NULL when that is 0); contents on entry ignored.
- * Rows not covered by any segment are not written.  Returns PKV_OK,
- * PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (shape not built: num_q_heads /
- * num_kv_heads > 8, head_dim not 64/128, block_size not 16, query_len > 1 with
- * an fp32 pool beyond the simple path's limits), PKV_ERR_WORKSPACE or
+ * Rows not covered by any segment are not written.  Multi-row segments on
+ * an fp32 pool run row by row on the decode path (any length; each row reads
+ * its own window).  Returns PKV_OK, PKV_ERR_INVALID_ARG,
+ * PKV_ERR_UNSUPPORTED (shape not built: num_q_heads / num_kv_heads > 8,
+ * head_dim not 64/128, block_size not 16), PKV_ERR_WORKSPACE or
  * PKV_ERR_HIP. */
 int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
                      const int32_t *row_to_slot, const int32_t *query_start,

@@ -460,3 +460,49 @@ def test_q8_config5(fused, gpu_available):
     _q8_pool_check(eng, pools)
     for i, ((out, _), r) in enumerate(zip(outs, res)):
         _check_close(f"q8 config 5 step {i}", out, r["out"], TOL["bf16"])
+
+
+# ------------------------------------------------------------------ randomized mixes
+def _random_mix(seed):
+    """A seeded random step: 1-9 segments mixing decode rows, short drafts
+    and chunks, random contexts (block and partition edges likely), a random
+    head layout, head dim, pool type and slot numbering."""
+    rng = np.random.default_rng(9000 + seed)
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 5, 8]))
+    kind = ["f32", "bf16", "bf16", "q8"][int(rng.integers(0, 4))]
+    nseg = int(rng.integers(1, 10))
+    slots = rng.choice(32, size=nseg, replace=False)
+    seqs = []
+    for s in slots:
+        r = rng.random()
+        n = 1 if r < 0.5 else (int(rng.integers(2, 17)) if r < 0.8 else int(rng.integers(17, 200)))
+        if kind == "f32" and n > 1:
+            n = min(n, 8)
+        edge = int(rng.choice([0, 1, 15, 16, 17, 511, 512, 513, 1023, 1024]))
+        hist = int(rng.integers(0, 2500)) if rng.random() < 0.6 else edge
+        seqs.append((int(s), hist, n))
+    w = make_custom(seqs, dtype="f32" if kind == "f32" else "bf16", hq=g * hkv, hkv=hkv, d=d, seed=seed,
+                    max_slots=32)
+    if kind == "q8":
+        w.kv_quant = "q8"
+    return w, kind
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_mixed_steps(seed, gpu_available):
+    w, kind = _random_mix(seed)
+    _log(f"random mix {seed}: {kind} D{w.head_dim} {w.num_q_heads}/{w.num_kv_heads} "
+         f"segs {[(s.slot, s.n) for s in w.steps[0].segments]}")
+    fused = bool(seed % 2)
+    eng, outs = _run_gpu(w, fused=fused)
+    res, pools = run_workload(w)
+    tol = TOL["f32"] if kind == "f32" else TOL["bf16"]
+    _check_close(f"random mix {seed}", outs[0][0], res[0]["out"], tol)
+    if kind == "q8":
+        _q8_pool_check(eng, pools)
+    else:
+        ok, ov = pools
+        assert np.array_equal(_pool_bits(eng.pool.k), _oracle_bits(ok))
+        assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))

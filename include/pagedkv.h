@@ -26,8 +26,10 @@
  *   - All integers are int32 unless stated.  Pointers marked "device" are HIP
  *     device pointers; "host" pointers are ordinary process memory.
  *   - The caller owns every buffer (pool, inputs, outputs, workspace).  The
- *     library never allocates or frees device memory and keeps no mutable
- *     global state.
+ *     library never allocates or frees device memory.  Its only global state
+ *     is, per device, one auxiliary stream (default priority) and two events,
+ *     created on first use by pkv_mixed_step and kept for the life of the
+ *     process.
  *   - Device calls are asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL = the null stream).  Argument errors are returned before
  *     anything is launched; launch failures return PKV_ERR_HIP; faults show

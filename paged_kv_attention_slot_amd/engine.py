@@ -14,7 +14,10 @@ Metadata travels in one pinned host buffer per step, copied on the step's
 own stream (so stream order protects the device copy).  A ring of buffers
 is used in turn; a host buffer is rewritten only after the copy that last
 read it has finished, which with a ring this deep has always happened
-already - the host never sleeps on the GPU inside the step loop.  The device
+already - the host never sleeps on the GPU inside the step loop.  One-call
+steps share one completion event per group of STEP_GROUP steps (an event
+record costs the GPU a few microseconds per step); a buffer whose group is
+still open when its turn comes records the group's event first.  The device
 block tables are re-sent only when a table changed (a block was reserved,
 released or truncated); slots that reserved decode headroom ahead of time
 (§Admission and step planning: capacity for the prompt and rolling decode
@@ -72,12 +75,14 @@ class _Staging:
         self.host = torch.empty(n, dtype=torch.int32, pin_memory=True)
         self.dev = torch.empty(n, dtype=torch.int32, device=device)
         self.np = self.host.numpy()
-        self.copied = torch.cuda.Event()
+        self.own = torch.cuda.Event()   # this buffer's event (split-call steps)
+        self.copied = self.own          # the event that marks the buffer's last reader done
         self.used = False
 
 
 class PagedKVEngine:
-    STAGING_RING = 8
+    STAGING_RING = 16
+    STEP_GROUP = 4          # one-call steps per completion event (<= STAGING_RING / 2)
 
     def __init__(self, *, num_blocks, num_kv_heads, num_q_heads, head_dim, dtype, max_slots,
                  max_blocks_per_seq, free_order=None, device="cuda", poison=True):
@@ -94,6 +99,9 @@ class PagedKVEngine:
         self._tables_dirty = True
         self._staging = []
         self._turn = 0
+        self._group_event = None        # event shared by the open group of one-call steps
+        self._group_n = 0
+        self._group_stream = None
         self._workspace = None
         self._ws_key = None
         self._ws_bytes = 0
@@ -128,9 +136,18 @@ class PagedKVEngine:
             self._staging = [_Staging(torch, self.device, cap) for _ in range(self.STAGING_RING)]
         st = self._staging[self._turn]
         self._turn = (self._turn + 1) % self.STAGING_RING
-        if st.used and not st.copied.query():
-            st.copied.synchronize()         # the DMA that last read this host buffer is done
+        if st.used:
+            if st.copied is self._group_event:
+                self._close_group()         # its group is still open: record the event now
+            if not st.copied.query():
+                st.copied.synchronize()     # the kernels that last read this host buffer are done
         return st
+
+    def _close_group(self):
+        if self._group_event is not None and self._group_n > 0:
+            self._group_event.record(self._group_stream)
+        self._group_event = None
+        self._group_n = 0
 
     def _refresh_tables(self):
         """Rebuild the host mirror of every table and send it to the device."""
@@ -184,6 +201,7 @@ class PagedKVEngine:
         """Lower the step and copy its metadata to the device (stream order)."""
         meta, st, offs, stream = self._lower_host(entries)
         st.dev[:offs[-1]].copy_(st.host[:offs[-1]], non_blocking=True)
+        st.copied = st.own
         st.copied.record(stream)
         st.used = True
         return meta
@@ -213,8 +231,17 @@ class PagedKVEngine:
         """One library call (pkv_mixed_step): the append kernel stages the
         metadata to the device and appends; attention follows."""
         B.mixed_step(prep.desc, self.pool, prep.meta.stream)
-        prep.staging.copied.record(prep.stream)   # the step's kernels have read the host buffer after this
+        # the step's kernels have read the host buffer once the group's event,
+        # recorded after this step or a later one on the same stream, completes
+        if self._group_event is None or self._group_stream != prep.stream:
+            self._close_group()
+            self._group_event = self.torch.cuda.Event()
+            self._group_stream = prep.stream
+        prep.staging.copied = self._group_event
         prep.staging.used = True
+        self._group_n += 1
+        if self._group_n >= self.STEP_GROUP:
+            self._close_group()
         return prep.out
 
     def fused_step(self, entries, k_new, v_new, q, scale, out=None, out_dtype=None):

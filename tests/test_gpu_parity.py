@@ -506,3 +506,24 @@ def test_random_mixed_steps(seed, gpu_available):
         ok, ov = pools
         assert np.array_equal(_pool_bits(eng.pool.k), _oracle_bits(ok))
         assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
+
+
+@pytest.mark.parametrize("name", ["1", "2", "3", "3v", "4a", "4b", "5", "3q", "5q", "prefix"])
+def test_one_call_step_equals_split_calls_bitwise(name, gpu_available):
+    """pkv_mixed_step picks prefetch depths, column tiles, skipped launches
+    and the auxiliary stream from the host's view of the step; the split
+    calls (pkv_kv_append, then pkv_paged_attend) know none of that.  Neither
+    choice may change arithmetic: outputs and pools are bit-identical."""
+    _log(f"one-call vs split {name}")
+    w = _workload(name)
+    e1, o1 = _run_gpu(w, fused=True)
+    e2, o2 = _run_gpu(w, fused=False)
+    for i, ((a, _), (b, _)) in enumerate(zip(o1, o2)):
+        assert np.array_equal(a.cpu().numpy().view(np.int32), b.cpu().numpy().view(np.int32)), f"step {i}"
+    assert np.array_equal(e1.pool.k.cpu().view(torch_int_view(e1.pool.k)).numpy(),
+                          e2.pool.k.cpu().view(torch_int_view(e2.pool.k)).numpy())
+
+
+def torch_int_view(t):
+    import torch
+    return {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.int8: torch.int8}[t.dtype]

@@ -247,7 +247,8 @@ int pkv_lower_step_cow(pkv_alloc *a, int32_t num_entries, const int32_t *entry_s
     for (int32_t s = 0; s < a->max_slots; ++s) {
       if (!a->in_use[s]) continue;
       const std::vector<int32_t> &t = a->tables[s];
-      std::memcpy(block_tables + static_cast<size_t>(s) * a->max_blocks, t.data(), t.size() * sizeof(int32_t));
+      if (!t.empty())
+        std::memcpy(block_tables + static_cast<size_t>(s) * a->max_blocks, t.data(), t.size() * sizeof(int32_t));
     }
   }
   if (num_copies) *num_copies = ncopy;
@@ -278,7 +279,7 @@ int pkv_slot_table(const pkv_alloc *a, int32_t slot, int32_t *table, int32_t cap
   if (!a->in_use[slot]) return PKV_ERR_STATE;
   const std::vector<int32_t> &t = a->tables[slot];
   if (static_cast<int64_t>(t.size()) > capacity) return PKV_ERR_INVALID_ARG;
-  std::memcpy(table, t.data(), t.size() * sizeof(int32_t));
+  if (!t.empty()) std::memcpy(table, t.data(), t.size() * sizeof(int32_t));   // an empty table's data() may be null
   return PKV_OK;
 }
 

@@ -20,7 +20,7 @@ Prints one JSON line:
                  algorithmic bytes per call / mean duration vs 8 TB/s
   cpu_baseline = the CPU oracle on a bounded sample of the same step
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--step N] [--no-cpu-baseline]
     python bench.py --ablation gather|prefix     (one JSON line of ablation rows)
 """
 from __future__ import annotations
@@ -51,6 +51,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="3")
+    ap.add_argument("--step", type=int, default=0,
+                    help="mixed-step configs: time this step of the workload (earlier steps run once first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--cpu-repeats", type=int, default=3)
@@ -87,12 +89,17 @@ def chunk_flops(w, segments, lens):
 def run_mixed(args, w, pk, torch, dev):
     """Replay one mixed step - the one-call pkv_mixed_step (append, then
     attention) on fixed lowered metadata - and time it; for the chunk-bearing
-    configs."""
-    from workloads.drive import make_engine, place_history, step_tensors
+    configs.  Steps before `args.step` run once, untimed."""
+    from workloads.drive import apply_ops, make_engine, place_history, run_step, step_tensors
     eng = make_engine(pk.PagedKVEngine, w, device=dev)
     place_history(eng, w, device=dev)
-    st = w.steps[0]
-    k_new, v_new, q = step_tensors(w, 0, device=dev)
+    if not 0 <= args.step < len(w.steps):
+        raise SystemExit(f"config {w.name} has steps 0..{len(w.steps) - 1}")
+    for i in range(args.step):
+        run_step(eng, w, i, device=dev)
+    st = w.steps[args.step]
+    apply_ops(eng, st.ops)
+    k_new, v_new, q = step_tensors(w, args.step, device=dev)
     prep = eng.prepare_fused([(s.slot, s.n) for s in st.segments], k_new, v_new, q, w.scale)
     meta = prep.meta
     stream = torch.cuda.current_stream()
@@ -118,11 +125,12 @@ def run_mixed(args, w, pk, torch, dev):
     # K and V of every cached token of the multi-row segments, once
     row = w.head_dim + 4 if getattr(w, "kv_quant", "") == "q8" else w.head_dim * w.elem_bytes
     mr_kv = sum(2 * L * w.num_kv_heads * row for seg, L in zip(st.segments, lens) if seg.n > 1)
-    return {"metric": f"mixed-step latency, config {w.name}", "value": round(wall / args.steps * 1e3, 4),
+    name = w.name if args.step == 0 else f"{w.name} step {args.step + 1}"
+    return {"metric": f"mixed-step latency, config {name}", "value": round(wall / args.steps * 1e3, 4),
             "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(wall / args.steps * 1e3, 4), "step_gpu_ms_avg": round(att * 1e3, 4),
             "dtype": w.dtype, "data": "synthetic",
-            "config": {"workload": f"config {w.name}: {w.description}", "decode_rows": len(dec_lens),
+            "config": {"workload": f"config {name}: {w.description}", "decode_rows": len(dec_lens),
                        "chunk_rows": int(sum(s.n for s in st.segments if s.n > 1))},
             "decode_kv_bytes": kv, "chunk_causal_flops": fl, "multi_row_kv_bytes": mr_kv,
             "step_kv_gbs": round((kv + mr_kv) / att / 1e9, 1),
@@ -342,7 +350,7 @@ def main():
         return
     w = make_workload(args.config)
     st = w.steps[0]
-    if any(s.n != 1 for s in st.segments):
+    if any(s.n != 1 for s in st.segments) or args.step:
         print(json.dumps(run_mixed(args, w, pk, torch, dev)), flush=True)
         return
     total_steps = args.warmup + args.steps

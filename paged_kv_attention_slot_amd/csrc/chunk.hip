@@ -9,18 +9,25 @@
 //
 // Row i of a segment with n rows and L cached tokens sits at position
 // L - n + i and sees keys 0 .. L - n + i.  The contraction is dense, so it
-// runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
+// runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
 //   * "M-rows" are (query row, head of the GQA group) pairs, m = i * G + h;
 //     a workgroup of 4 wavefronts takes 128 consecutive M-rows of one
 //     segment and one KV head, so all G query heads share every K/V tile;
-//   * K/V tiles of 64 tokens (4 pool blocks, fetched through the block table)
-//     are staged in LDS once per workgroup;
-//   * scores are formed transposed, S^T = K Q^T, so each lane owns one M-row
-//     (lane % 16) and the softmax max/sum need only two cross-row shuffles;
-//   * the output is formed as O^T += V^T P^T: P^T comes straight from the
-//     S^T accumulator layout, and V^T from the natural [token][dim] tile with
-//     ds_read_b64_tr_b16 (lane j of each 16-lane group receives 4 consecutive
-//     tokens of dimension j);
+//     a wavefront's 32 M-rows are one 32-wide MFMA column tile;
+//   * K/V tiles (4 or 2 pool blocks, fetched through the block table) are
+//     staged in LDS once per workgroup;
+//   * scores are formed transposed, S^T = K Q^T: lane l owns M-row l % 32,
+//     and its half h = l / 32 holds 16 of every 32 keys (accumulator element
+//     e is key 8 (e / 4) + 4 h + e % 4), so a row max is one reduction over
+//     the lane's scores and one swap with lane l ^ 32;
+//   * the output is formed as O^T += V^T P^T.  P^T comes straight from the
+//     accumulators: the 16 keys of PV step s are elements 8 (s % 2) .. + 7
+//     of 32-key tile s / 2, i.e. keys 16 s + 4 h + {0..3} and
+//     16 s + 8 + 4 h + {0..3} for half h.  V^T is two ds_read_b64_tr_b16
+//     reads of exactly those keys from the natural [token][dim] tile (lane j
+//     of each 16-lane group receives 4 consecutive keys of dimension j);
+//   * row sums add the bf16 weights the products consume (v_dot2_f32_bf16
+//     against (1, 1)); the two halves' sums are added at the end;
 //   * the causal mask is applied per element only on tiles that reach past a
 //     wavefront's first row; rows of a segment never see past their position.
 #include <cfloat>
@@ -33,9 +40,9 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
-typedef short shortx8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Transposed LDS read: with lane i of a 16-lane group pointing at
 // tile[t0 + i / 4][d0 + 4 (i % 4)], lane j receives tile[t0 .. t0 + 3][d0 + j].
@@ -48,42 +55,11 @@ __device__ __forceinline__ shortx4_t lds_read_tr16(const unsigned char *p) {
 // with no canonicalisation of matrix-core results, unlike fmaxf.
 __device__ __forceinline__ float vmaxf(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-template <int N>
-__device__ __forceinline__ float max_of(const float (&v)[N]) {
-  float m = vmaxf(v[0], v[1]);
-#pragma unroll
-  for (int i = 2; i + 1 < N; i += 2) m = vmaxf(m, vmaxf(v[i], v[i + 1]));
-  if constexpr (N % 2 == 1) m = vmaxf(m, v[N - 1]);
-  return m;
-}
-
-// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups) with the
-// lane-swap instructions: each swap leaves x[l] and x[l ^ 32] (then
-// x[l ^ 16]) in the two returned registers of every lane.
-__device__ __forceinline__ float group4_max(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = vmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return vmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 32;                 // two 16-row MFMA column tiles
+constexpr int kRowsPerWave = 32;                 // one 32-wide MFMA column tile
 constexpr int kMTile = kWaves * kRowsPerWave;    // M-rows per workgroup
 constexpr int kKV = 64;                          // tokens per K/V tile
-constexpr int kPad = 32;                         // LDS row padding (bytes)
 constexpr int kTableWindow = PKV_CHUNK_TABLE_WINDOW;   // block-table entries staged per pass
-
-template <int D>
-struct ChunkGeo {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kStride = kRowBytes + kPad;         // LDS bytes per token row
-  static constexpr int kCPR = kRowBytes / 16;              // 16-byte chunks per row
-  static constexpr int kPerThread = kKV * kCPR / (kWaves * kWave);
-  static constexpr int kKSteps = D / 32;                   // MFMA k-steps of q . k
-  static constexpr int kDTiles = D / 16;                   // 16-wide output column tiles
-  static constexpr int kTileLds = kKV * kStride;
-};
 
 // Key-range splits of a segment: segments with few row tiles (speculative
 // drafts, short chunks) would leave most compute units idle, so their keys
@@ -136,8 +112,8 @@ struct Ring<128> {
 };
 
 // Position of 16-byte chunk c of token row t within the row, so that both the
-// K operand reads (16 rows, one chunk) and the transposed V reads (4 rows,
-// two chunks) hit distinct banks.
+// K operand reads (consecutive rows, one chunk) and the transposed V reads
+// (4 rows, two chunks) hit distinct banks.
 template <int D>
 __device__ __forceinline__ int ring_swz(int t, int c) {
   if constexpr (D == 128) return c ^ (((t & 7) << 1) | ((t >> 3) & 1));
@@ -148,26 +124,36 @@ __device__ __forceinline__ unsigned lds_addr32(const unsigned char *p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)(p)));
 }
 
+// acc + the sum of the eight bf16 values of v (pairwise against (1, 1)).
+__device__ __forceinline__ float add_bf16_pairs(const bf16x8_t &v, float acc) {
+  const bf16x2_t one2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, acc, false);
+}
+
 // OFF32: every byte of a pool tensor lies within 4 GiB of its base, so a tile
 // load addresses the tensor base (scalar) plus one 32-bit vector offset.
 template <int D, bool OFF32>
 __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendArgs a, int G) {
-  using C = ChunkGeo<D>;
   constexpr int T = Ring<D>::kTok;            // tokens per ring stage
   constexpr int S = Ring<D>::kStages;
   constexpr int kRowBytes = D * 2;
   constexpr int kCPR = kRowBytes / 16;
-  constexpr int kStageBytes = T * kRowBytes;  // K (or V) bytes per stage
-  constexpr int kPer = T * kCPR / (kWaves * kWave);   // 16-byte chunks per thread per tile
-  constexpr int kTT = T / 16;                 // 16-token MFMA tiles per stage
-  constexpr int kKS = T / 32;                 // 32-key MFMA steps per stage
+  constexpr int kStageBytes = T * kRowBytes;
+  constexpr int kPer = T * kCPR / (kWaves * kWave);
+  constexpr int kTT = T / 32;                 // 32-token MFMA tiles per stage
+  constexpr int kPS = T / 16;                 // 16-key PV steps per stage
+  constexpr int kQS = D / 16;                 // 16-dim q . k steps
+  constexpr int kDT = D / 32;                 // 32-wide output dimension tiles
   static_assert(kPer >= 1 && T % 32 == 0 && 64 % T == 0, "ring geometry");
   __shared__ __align__(16) unsigned char lds[S * 2 * kStageBytes];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
 
   auto units_fn = [&](int b) { return chunk_units<D>(a, b, G); };
   const int hkv = a.num_kv_heads;
@@ -191,53 +177,48 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   const int kv_end = L - n + m_last / G + 1;         // keys any row of the tile sees
   const int rt_begin = split * cs.tps * (kKV / T);
   const int rt_end = min(rt_begin + cs.tps * (kKV / T), (kv_end + T - 1) / T);
-  if (rt_begin >= rt_end) return;                     // no row of this tile reaches this key range
+  if (rt_begin >= rt_end) return;
   const bool partial_out = cs.splits > 1;
   if (partial_out && a.chunk_part == nullptr) return;
-  // first position among this wave's rows (rows past the segment see nothing)
   const int wave_pos0 = mw < mtot ? L - n + mw / G : -1;
 
-  // Q operands (B of S^T = K Q^T): lane holds 8 dims of its M-row per k-step,
-  // pre-multiplied by scale * log2(e) (rounded to bf16) so that the matrix
-  // cores produce scores in log2 units.
+  // Q operand (B of S^T = K Q^T): lane holds dims 16 ks + 8 hh .. + 7 of
+  // its M-row, pre-multiplied by scale * log2(e) and rounded to bf16.
   const float c_log2 = a.scale_log2;
-  int pos[2], row[2], hq[2];
-  bool valid[2];
-  bf16x8_t qv[2][C::kKSteps];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int m = mw + qt * 16 + l16;
-    valid[qt] = m < mtot;
-    const int i = valid[qt] ? m / G : 0;
-    const int h = valid[qt] ? m - i * G : 0;
-    pos[qt] = valid[qt] ? L - n + i : -1;
-    row[qt] = si.row0 + i;
-    hq[qt] = g * G + h;
+  const int m = mw + l32;
+  const bool valid = m < mtot;
+  const int qi = valid ? m / G : 0;
+  const int qh = valid ? m - qi * G : 0;
+  const int pos = valid ? L - n + qi : -1;
+  const int row = si.row0 + qi;
+  const int hq = g * G + qh;
+  bf16x8_t qv[kQS];
+  {
     const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
-                                                      (static_cast<int64_t>(row[qt]) * a.num_q_heads + hq[qt]) * D);
+                                                      (static_cast<int64_t>(row) * a.num_q_heads + hq) * D);
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk) {
-      const uint4 w = valid[qt] ? qp[kk * 4 + lg] : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < kQS; ++ks) {
+      const uint4 w = valid ? qp[2 * ks + hh] : make_uint4(0, 0, 0, 0);
       const bf16x8_t raw = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qv[qt][kk][j] = static_cast<__bf16>(static_cast<float>(raw[j]) * c_log2);
+      for (int j = 0; j < 8; ++j) qv[ks][j] = static_cast<__bf16>(static_cast<float>(raw[j]) * c_log2);
     }
   }
 
-  // Online softmax state per M-row (log2 units): running max m_run, and the
-  // reference r_ref that the score accumulators start from (-r_ref), so that
-  // a tile's accumulators hold score - r_ref and its weights are exp2 of them
-  // directly.  r_ref follows m_run once the row has seen an unmasked key (0
-  // before).  The row sums are one more output tile, lsum: the matrix cores
-  // multiply the bf16 weights by an all-ones V^T tile, so every lane holds
-  // its own row's sum of exactly the weights the products used.
-  float m_run[2] = {-FLT_MAX, -FLT_MAX};
-  floatx4_t lsum[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
-  float r_ref[2] = {0.f, 0.f};
-  floatx4_t negr[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
-  floatx4_t o[C::kDTiles][2];
+  // Online softmax state of the lane's M-row (log2 units): running max
+  // m_run, and the reference r_ref that the score accumulators start from
+  // (-r_ref), so that a tile's accumulators hold score - r_ref and its
+  // weights are exp2 of them directly.  r_ref follows m_run once the row has
+  // seen an unmasked key (0 before).  lsum: this half's row sum.
+  float m_run = -FLT_MAX, r_ref = 0.f, lsum = 0.f;
+  floatx16_t negr;
 #pragma unroll
-  for (int dt = 0; dt < C::kDTiles; ++dt) o[dt][0] = o[dt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 16; ++i) negr[i] = 0.f;
+  floatx16_t o[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
   // Direct-to-LDS staging.  Thread tid fills 16-byte chunks q = x * 256 + tid
   // of each K and V stage: token row t = q / kCPR, position p = q % kCPR,
@@ -318,180 +299,138 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   constexpr int kPassTiles = kTableWindow * kBlockTokens / T;
   static_assert(S >= 3, "V of tile t and K of tile t + 1 are resident together");
 
-  // S^T = K Q^T for the tile in stage st: kTT token tiles x 2 row tiles.
-  // Lane holds keys tt*16 + 4*lg + e of the tile for its M-rows (qt, l16).
-  auto qk = [&](int st, floatx4_t(&sc)[kTT][2]) {
+  // K operand of q . k step ks for token tile tt of stage st: key tt*32 + l32,
+  // dims 16 ks + 8 hh .. + 7 (16-byte chunk 2 ks + hh of the row).
+  auto k_operand = [&](const unsigned char *kl, int tt, int ks) {
+    const int kr = tt * 32 + l32;
+    return *reinterpret_cast<const bf16x8_t *>(kl + kr * kRowBytes + ring_swz<D>(kr, 2 * ks + hh) * 16);
+  };
+  auto qk = [&](int st, floatx16_t(&sc)[kTT]) {
     const unsigned char *kl = lds + st * 2 * kStageBytes;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      sc[tt][0] = negr[0];
-      sc[tt][1] = negr[1];
-      const int kr = tt * 16 + l16;
+      sc[tt] = negr;
 #pragma unroll
-      for (int kk = 0; kk < C::kKSteps; ++kk) {
-        const bf16x8_t ka =
-            *reinterpret_cast<const bf16x8_t *>(kl + kr * kRowBytes + ring_swz<D>(kr, kk * 4 + lg) * 16);
-        sc[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[0][kk], sc[tt][0], 0, 0, 0);
-        sc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[1][kk], sc[tt][1], 0, 0, 0);
-      }
+      for (int ks = 0; ks < kQS; ++ks)
+        sc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kl, tt, ks), qv[ks], sc[tt], 0, 0, 0);
     }
   };
   // Causal mask of tile rt; only tiles reaching past the wave's first row.
-  auto mask = [&](int rt, floatx4_t(&sc)[kTT][2]) {
+  auto mask = [&](int rt, floatx16_t(&sc)[kTT]) {
     if (rt * T + T - 1 > wave_pos0) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int tt = 0; tt < kTT; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (rt * T + tt * 16 + lg * 4 + e > pos[qt]) sc[tt][qt][e] = -INFINITY;
-    }
-  };
-  // Row max of a tile (log2 units): the candidate new running max, and
-  // whether it exceeds the current one by more than the allowed slack.
-  auto rowmax = [&](const floatx4_t(&sc)[kTT][2], float(&mnew)[2]) {
-    bool raise = false;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float v[4 * kTT];
 #pragma unroll
       for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[tt * 4 + e] = sc[tt][qt][e];
-      const float mx = r_ref[qt] + group4_max(max_of<4 * kTT>(v));
-      mnew[qt] = vmaxf(m_run[qt], mx);
-      raise |= mx > m_run[qt] + PKV_CHUNK_RESCALE_SLACK;
+        for (int i = 0; i < 16; ++i)
+          if (rt * T + tt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) > pos) sc[tt][i] = -INFINITY;
     }
-    return raise;
   };
-  // Move O and l to the new running max when any row of the wave asked.
+  // Row max of a tile (log2 units) over both halves: the candidate new
+  // running max, and whether it exceeds the current one by more than the
+  // allowed slack (the rescale vote).
+  auto finish_max = [&](float part, float &mnew) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    const float mx = r_ref + vmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    mnew = vmaxf(m_run, mx);
+    return mx > m_run + PKV_CHUNK_RESCALE_SLACK;
+  };
+  auto rowmax = [&](const floatx16_t(&sc)[kTT], float &mnew) {
+    float acc = vmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int w = 2; w < 16 * kTT; w += 2) acc = vmaxf(vmaxf(acc, sc[w / 16][w % 16]), sc[w / 16][w % 16 + 1]);
+    return finish_max(acc, mnew);
+  };
   // Move O and l to the new running max when any row of the wave asked, and
   // re-base the pending tile's accumulators `cur` to the new reference.
-  auto rescale = [&](const float(&mnew)[2], bool raise, floatx4_t(&cur)[kTT][2]) {
+  auto rescale = [&](float mnew, bool raise, floatx16_t(&cur)[kTT]) {
     if (__ballot(raise) != 0) {
+      const float alpha = fast_exp2(m_run - mnew);
+      m_run = mnew;
+      lsum *= alpha;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float alpha = fast_exp2(m_run[qt] - mnew[qt]);
-        m_run[qt] = mnew[qt];
-        lsum[qt] *= alpha;
+      for (int dt = 0; dt < kDT; ++dt) o[dt] *= alpha;
+      const float nr = mnew > -FLT_MAX ? mnew : r_ref;
+      const float d = nr - r_ref;
+      r_ref = nr;
 #pragma unroll
-        for (int dt = 0; dt < C::kDTiles; ++dt) o[dt][qt] *= alpha;
-        const float nr = mnew[qt] > -FLT_MAX ? mnew[qt] : r_ref[qt];
-        const float d = nr - r_ref[qt];
-        r_ref[qt] = nr;
-        negr[qt] = floatx4_t{-nr, -nr, -nr, -nr};
+      for (int i = 0; i < 16; ++i) negr[i] = -nr;
 #pragma unroll
-        for (int tt = 0; tt < kTT; ++tt) cur[tt][qt] -= d;
-      }
+      for (int tt = 0; tt < kTT; ++tt) cur[tt] -= d;
     }
   };
-  // V^T operands of tile stage st for phase B: keys 4*lg .. 4*lg+3 and
-  // 16 + 4*lg .. of each 32-key step, dimension dt*16 + l16, read transposed
-  // from the swizzled tile.
-  auto load_v = [&](int st, bf16x8_t(&va)[C::kDTiles][kKS]) {
+  // V^T operand of PV step ps, dimension tile dt: lane (16-lane group
+  // 2 hh + g2, j) receives keys 16 ps + 4 hh + {0..3} then 16 ps + 8 + 4 hh +
+  // {0..3} of dimension dt*32 + 16 g2 + j (two transposed reads).
+  auto load_v = [&](int st, bf16x8_t(&va)[kDT][kPS]) {
     const unsigned char *vl = lds + st * 2 * kStageBytes + kStageBytes;
+    const int i16 = lane & 15;
+    const int g2 = (lane >> 4) & 1;
 #pragma unroll
-    for (int dt = 0; dt < C::kDTiles; ++dt) {
-      const int dd = dt * 16 + 4 * (l16 & 3);
+    for (int dt = 0; dt < kDT; ++dt) {
+      const int dd = dt * 32 + 16 * g2 + 4 * (i16 & 3);
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const int r1 = ks * 32 + lg * 4 + (l16 >> 2);
-        const int r2 = r1 + 16;
+      for (int ps = 0; ps < kPS; ++ps) {
+        const int r1 = ps * 16 + 4 * hh + (i16 >> 2);
+        const int r2 = r1 + 8;
         const shortx4_t v1 = lds_read_tr16(vl + r1 * kRowBytes + ring_swz<D>(r1, dd >> 3) * 16 + (dd & 7) * 2);
         const shortx4_t v2 = lds_read_tr16(vl + r2 * kRowBytes + ring_swz<D>(r2, dd >> 3) * 16 + (dd & 7) * 2);
-        va[dt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+        va[dt][ps] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
-  // Phase A of an iteration: the matrix cores form the scores of the next
-  // tile (S^T = K Q^T from stage st_next) while the vector ALU turns the
-  // current tile's scores into bf16 weights and row sums.  The two streams
-  // are interleaved by hand, one matrix-core pair per step, each step fenced
-  // so that the scheduler keeps them side by side.
-  auto phase_a = [&](const floatx4_t(&cur)[kTT][2], int st, int st_next, floatx4_t(&nxt)[kTT][2],
-                     bf16x8_t(&pb)[kKS][2], bf16x8_t(&va)[C::kDTiles][kKS]) {
+  // Phase A: the scores of the next tile (stage st_next) on the matrix
+  // cores; the weights of the current tile on the vector ALU.
+  auto phase_a = [&](const floatx16_t(&cur)[kTT], int st, int st_next, floatx16_t(&nxt)[kTT], bf16x8_t(&pb)[kPS],
+                     bf16x8_t(&va)[kDT][kPS]) {
     const unsigned char *kl = lds + st_next * 2 * kStageBytes;
-    // K operand of matrix-core pair j (token tile j / kKSteps, k-step
-    // j % kKSteps): read at step j, used kLead steps later.
-    bf16x8_t ka[kTT * C::kKSteps];
-    auto load_k = [&](int j) {
-      const int kr = (j / C::kKSteps) * 16 + l16;
-      ka[j] = *reinterpret_cast<const bf16x8_t *>(kl + kr * kRowBytes + ring_swz<D>(kr, (j % C::kKSteps) * 4 + lg) * 16);
-    };
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
-      nxt[tt][0] = negr[0];
-      nxt[tt][1] = negr[1];
-    }
-    // The first kLead steps are weights only, covering the operand reads.
     constexpr int kLead = 2;
-    constexpr int kPairs = kTT * C::kKSteps;
+    constexpr int kPairs = kTT * kQS;
     constexpr int kSteps = kPairs + kLead;
-    constexpr int kScores = 2 * kKS * 8;
-    float p[2][kKS][8];
+    constexpr int kScores = 16 * kTT;
+    bf16x8_t ka[kPairs];
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) nxt[tt] = negr;
+    float p[kScores];
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
-      if (Ring<D>::kEarlyV && i == kSteps / 2) load_v(st, va);   // V reads of the current tile, midway
-      if (i < kPairs) load_k(i);
+      if (Ring<D>::kEarlyV && i == kSteps / 2) load_v(st, va);
+      if (i < kPairs) ka[i] = k_operand(kl, i / kQS, i % kQS);
       if (i >= kLead) {
-        const int j = i - kLead, tt = j / C::kKSteps, kk = j % C::kKSteps;
-        nxt[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qv[0][kk], nxt[tt][0], 0, 0, 0);
-        nxt[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qv[1][kk], nxt[tt][1], 0, 0, 0);
+        const int j = i - kLead;
+        nxt[j / kQS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qv[j % kQS], nxt[j / kQS], 0, 0, 0);
       }
 #pragma unroll
       for (int w = i * kScores / kSteps; w < (i + 1) * kScores / kSteps; ++w) {
-        const int qt = w / (kKS * 8), ks = (w / 8) % kKS, e8 = w % 8;
-        p[qt][ks][e8] = fast_exp2(cur[2 * ks + e8 / 4][qt][e8 % 4]);
-        if (e8 == 7) {
-          const float *q8 = p[qt][ks];
-          pb[ks][qt] = bf16x8_t{static_cast<__bf16>(q8[0]), static_cast<__bf16>(q8[1]), static_cast<__bf16>(q8[2]),
-                                static_cast<__bf16>(q8[3]), static_cast<__bf16>(q8[4]), static_cast<__bf16>(q8[5]),
-                                static_cast<__bf16>(q8[6]), static_cast<__bf16>(q8[7])};
+        p[w] = fast_exp2(cur[w / 16][w % 16]);
+        if (w % 8 == 7) {
+          const float *q8 = p + (w - 7);
+          pb[w / 8] = bf16x8_t{static_cast<__bf16>(q8[0]), static_cast<__bf16>(q8[1]), static_cast<__bf16>(q8[2]),
+                               static_cast<__bf16>(q8[3]), static_cast<__bf16>(q8[4]), static_cast<__bf16>(q8[5]),
+                               static_cast<__bf16>(q8[6]), static_cast<__bf16>(q8[7])};
         }
       }
       if constexpr (PKV_CHUNK_INTERLEAVE) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Phase B: O^T += V^T P^T of the current tile (stage st) on the matrix
-  // cores while the vector ALU takes the row max of the next tile.  Returns
-  // the rescale vote, as rowmax.
-  auto phase_b = [&](const bf16x8_t(&pb)[kKS][2], bf16x8_t(&va)[C::kDTiles][kKS], int st,
-                     const floatx4_t(&nxt)[kTT][2], float(&mnew)[2]) {
+  // Phase B: O^T += V^T P^T of the current tile; the vector ALU adds the
+  // row sums and takes the next tile's row max.
+  auto phase_b = [&](const bf16x8_t(&pb)[kPS], bf16x8_t(&va)[kDT][kPS], int st, const floatx16_t(&nxt)[kTT],
+                     float &mnew) {
     if constexpr (!Ring<D>::kEarlyV) load_v(st, va);
-    // the last kKS pairs are the row sums (all-ones V^T operand)
-    constexpr int kPairs = C::kDTiles * kKS + kKS;
-    constexpr int kItems = 2 * kTT;
-    const bf16x8_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f), static_cast<__bf16>(1.f),
-                           static_cast<__bf16>(1.f), static_cast<__bf16>(1.f), static_cast<__bf16>(1.f),
-                           static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-    float acc[2] = {-INFINITY, -INFINITY};
+    constexpr int kPairs = kDT * kPS;
+    constexpr int kMax = 8 * kTT;              // max steps over the next tile's scores
+    float acc = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
-      const int dt = i / kKS, ks = i % kKS;
-      if (dt < C::kDTiles) {
-        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][0], o[dt][0], 0, 0, 0);
-        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt][ks], pb[ks][1], o[dt][1], 0, 0, 0);
-      } else {
-        lsum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][0], lsum[0], 0, 0, 0);
-        lsum[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][1], lsum[1], 0, 0, 0);
-      }
+      const int dt = i / kPS, ps = i % kPS;
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][ps], pb[ps], o[dt], 0, 0, 0);
+      if (i % kDT == 0) lsum = add_bf16_pairs(pb[i / kDT], lsum);
 #pragma unroll
-      for (int w = i * kItems / kPairs; w < (i + 1) * kItems / kPairs; ++w) {
-        const int qt = w / kTT, tt = w % kTT;
-        const floatx4_t &x = nxt[tt][qt];
-        acc[qt] = vmaxf(acc[qt], vmaxf(vmaxf(x[0], x[1]), vmaxf(x[2], x[3])));
-      }
+      for (int w = i * kMax / kPairs; w < (i + 1) * kMax / kPairs; ++w)
+        acc = vmaxf(vmaxf(acc, nxt[w / 8][(w % 8) * 2]), nxt[w / 8][(w % 8) * 2 + 1]);
       if constexpr (PKV_CHUNK_INTERLEAVE) __builtin_amdgcn_sched_barrier(0);
     }
-    bool raise = false;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float mx = r_ref[qt] + group4_max(acc[qt]);
-      mnew[qt] = vmaxf(m_run[qt], mx);
-      raise |= mx > m_run[qt] + PKV_CHUNK_RESCALE_SLACK;
-    }
-    return raise;
+    return finish_max(acc, mnew);
   };
 
   for (int pass0 = rt_begin; pass0 < rt_end; pass0 += kPassTiles) {
@@ -512,8 +451,8 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     for (int i = 0; i < S - 1; ++i) issue(i, min(pass0 + i, pass1 - 1));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 2)) : "memory");
     __syncthreads();
-    floatx4_t s0[kTT][2], s1[kTT][2];
-    float mnew[2];
+    floatx16_t s0[kTT], s1[kTT];
+    float mnew;
     qk(0, s0);
     mask(pass0, s0);
     bool raise = rowmax(s0, mnew);
@@ -521,7 +460,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     lookup(min(pass0 + S - 1, pass1 - 1), ph_next);
 
     // One iteration: tile rt's scores are in `cur`, tile rt + 1's go to `nxt`.
-    auto iter = [&](int rt, floatx4_t(&cur)[kTT][2], floatx4_t(&nxt)[kTT][2], auto masked_next) {
+    auto iter = [&](int rt, floatx16_t(&cur)[kTT], floatx16_t(&nxt)[kTT], auto masked_next) {
       const int st = (rt - pass0) % S;
       const int st_next = (rt + 1 - pass0) % S;
       // Tile rt + 1 has landed (at most S - 3 newer tiles outstanding); past
@@ -530,15 +469,15 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       __syncthreads();
       issue_ph((rt - pass0 + S - 1) % S, min(rt + S - 1, pass1 - 1), ph_next);
       rescale(mnew, raise, cur);
-      // Phase A: the weights of tile rt on the vector ALU while the matrix
-      // cores form the scores of tile rt + 1 (of a repeat of tile rt on the
-      // last iteration: computed, never used).
-      bf16x8_t pb[kKS][2];
-      bf16x8_t va[C::kDTiles][kKS];
+      bf16x8_t pb[kPS];
+      bf16x8_t va[kDT][kPS];
+      // Phase A: the weights of tile rt while the matrix cores form the
+      // scores of tile rt + 1 (of a repeat of tile rt on the last iteration:
+      // computed, never used).
       phase_a(cur, st, st_next, nxt, pb, va);
       if constexpr (decltype(masked_next)::value) mask(rt + 1, nxt);
-      // Phase B: O += V P of tile rt on the matrix cores while the vector
-      // ALU takes the row max of tile rt + 1.
+      // Phase B: O += V P of tile rt, the row sums, and the row max of tile
+      // rt + 1.
       raise = phase_b(pb, va, st, nxt, mnew) && rt + 1 < pass1;
       lookup(min(rt + S, pass1 - 1), ph_next);
     };
@@ -557,54 +496,50 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     if (rt < split_at) {
       iter(rt, s0, s1, std::false_type{});
 #pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
-        s0[tt][0] = s1[tt][0];
-        s0[tt][1] = s1[tt][1];
-      }
+      for (int tt = 0; tt < kTT; ++tt) s0[tt] = s1[tt];
       ++rt;
     }
     for (; rt < pass1; ++rt) {
       iter(rt, s0, s1, std::true_type{});
 #pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
-        s0[tt][0] = s1[tt][0];
-        s0[tt][1] = s1[tt][1];
-      }
+      for (int tt = 0; tt < kTT; ++tt) s0[tt] = s1[tt];
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain before the ring is reused
   }
 
   // Normalise and store (or store the unnormalised partial of this key range
-  // for the merge); every lane already holds its row's sum.
+  // for the merge).  Both halves' sums; lane (hh, l32) stores dims dt*32 + 8 r + 4 hh .. + 3.
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+  const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  if (!valid) return;
+  if (partial_out) {
+    const int64_t pidx = (static_cast<int64_t>(b) * hkv + g) * chunk_split_slots(D) + m * cs.splits + split;
+    float *pa = a.chunk_part + pidx * kChunkSlotFloats<D>;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float lt = lsum[qt][0];
-    if (!valid[qt]) continue;
-    if (partial_out) {
-      const int m = mw + qt * 16 + l16;
-      const int64_t pidx = (static_cast<int64_t>(b) * hkv + g) * chunk_split_slots(D) + m * cs.splits + split;
-      float *pa = a.chunk_part + pidx * kChunkSlotFloats<D>;
+    for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt)
-        *reinterpret_cast<float4 *>(pa + dt * 16 + lg * 4) =
-            make_float4(o[dt][qt][0], o[dt][qt][1], o[dt][qt][2], o[dt][qt][3]);
-      if (lg == 0) *reinterpret_cast<float2 *>(pa + D) = make_float2(m_run[qt], lt);
-      continue;
-    }
-    const float inv = 1.f / lt;
-    const int64_t ob = (static_cast<int64_t>(row[qt]) * a.num_q_heads + hq[qt]) * D + lg * 4;
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<float4 *>(pa + dt * 32 + 8 * r + 4 * hh) =
+            make_float4(o[dt][4 * r], o[dt][4 * r + 1], o[dt][4 * r + 2], o[dt][4 * r + 3]);
+    if (hh == 0) *reinterpret_cast<float2 *>(pa + D) = make_float2(m_run, lt);
+    return;
+  }
+  const float inv = 1.f / lt;
+  const int64_t ob = (static_cast<int64_t>(row) * a.num_q_heads + hq) * D + 4 * hh;
 #pragma unroll
-    for (int dt = 0; dt < C::kDTiles; ++dt) {
-      const floatx4_t v = o[dt][qt] * inv;
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v0 = o[dt][4 * r] * inv, v1 = o[dt][4 * r + 1] * inv;
+      const float v2 = o[dt][4 * r + 2] * inv, v3 = o[dt][4 * r + 3] * inv;
+      const int64_t off = ob + dt * 32 + 8 * r;
       if (a.out_bf16) {
-        uint16_t *op = static_cast<uint16_t *>(a.out) + ob + dt * 16;
-        *reinterpret_cast<uint2 *>(op) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                                    f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) =
+            make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16), f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
       } else {
-        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + ob + dt * 16) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + off) = make_float4(v0, v1, v2, v3);
       }
     }
-  }
 }
 
 // Merge the key-range partials of split segments: for M-row m (query row

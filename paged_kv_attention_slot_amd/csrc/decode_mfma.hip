@@ -180,17 +180,30 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
 #pragma unroll
     for (int dt = 0; dt < M::kDTiles; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const unsigned char *kt, const unsigned char *vt, int jj, auto partial_tag) {
+    // A landed tile's operands go to registers first, so that its stage can
+    // be refilled before the tile's arithmetic: K (lane holds key l16, dims
+    // 32 kk + 8 lg .. + 7) and V^T (lane i of each 16-lane group points at
+    // row 4 lg + i / 4, dims 16 dt + 4 (i % 4); it receives rows
+    // 4 lg .. + 3 of dim 16 dt + i).
+    const int vt_row = lg * 4 + (l16 >> 2);
+    auto read_tile = [&](const unsigned char *kt, const unsigned char *vt, bf16x8_t(&ka)[M::kKSteps],
+                         shortx4_t(&va)[M::kDTiles]) {
+#pragma unroll
+      for (int kk = 0; kk < M::kKSteps; ++kk)
+        ka[kk] = *reinterpret_cast<const bf16x8_t *>(kt + l16 * M::kRowBytes + M::swz(l16, kk * 4 + lg) * 16);
+#pragma unroll
+      for (int dt = 0; dt < M::kDTiles; ++dt) {
+        const int dd = dt * 16 + 4 * (l16 & 3);
+        va[dt] = lds_tr16(vt + vt_row * M::kRowBytes + M::swz(vt_row, dd >> 3) * 16 + (dd & 7) * 2);
+      }
+    };
+    auto compute = [&](const bf16x8_t(&ka)[M::kKSteps], shortx4_t(&va)[M::kDTiles], int jj, auto partial_tag) {
       constexpr bool PARTIAL = decltype(partial_tag)::value;
       const int tokbase = (j0 + jj) * kBlockTokens;
       const int valid = tok1 - tokbase;       // tokens of this tile in range (< 16 only if PARTIAL)
       floatx4_t s = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < M::kKSteps; ++kk) {
-        const int c = kk * 4 + lg;
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(kt + l16 * M::kRowBytes + M::swz(l16, c) * 16);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kk], s, 0, 0, 0);
-      }
+      for (int kk = 0; kk < M::kKSteps; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qb[kk], s, 0, 0, 0);
       bool ok[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) ok[e] = !PARTIAL || lg * 4 + e < valid;
@@ -216,25 +229,15 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
       const bf16x4_t pb = bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
                                    static_cast<__bf16>(p[3])};
       const shortx4_t pbs = __builtin_bit_cast(shortx4_t, pb);
-      // V^T operand: lane i of each 16-lane group points at row 4 lg + i / 4,
-      // dims 16 dt + 4 (i % 4); it receives rows 4 lg .. + 3 of dim 16 dt + i.
-      const int vt_row = lg * 4 + (l16 >> 2);
 #pragma unroll
       for (int dt = 0; dt < M::kDTiles; ++dt) {
-        const int dd = dt * 16 + 4 * (l16 & 3);
-        shortx4_t va = lds_tr16(vt + vt_row * M::kRowBytes + M::swz(vt_row, dd >> 3) * 16 + (dd & 7) * 2);
+        shortx4_t v = va[dt];
         if constexpr (PARTIAL) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) va[e] = ok[e] ? va[e] : static_cast<short>(0);   // select, never multiply poison
+          for (int e = 0; e < 4; ++e) v[e] = ok[e] ? v[e] : static_cast<short>(0);   // select, never multiply poison
         }
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbs, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pbs, o[dt], 0, 0, 0);
       }
-    };
-    auto compute_any = [&](const unsigned char *kt, const unsigned char *vt, int jj) {
-      if ((j0 + jj + 1) * kBlockTokens > tok1)
-        compute(kt, vt, jj, std::true_type{});
-      else
-        compute(kt, vt, jj, std::false_type{});
     };
 
     // kDecodeMfmaStages tiles in flight.  Past the last tile the prefetch re-reads
@@ -252,12 +255,18 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
         if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * M::kLoads) : "memory");
         const unsigned char *kt = st == 0 ? k0 : (st == 1 ? k1 : k2);
         const unsigned char *vt = st == 0 ? v0 : (st == 1 ? v1 : v2);
-        compute_any(kt, vt, jj + st);
-        // refill this stage with the tile S ahead, once every LDS read of the
-        // tile just used has returned
+        bf16x8_t ka[M::kKSteps];
+        shortx4_t va[M::kDTiles];
+        read_tile(kt, vt, ka, va);
+        // every LDS read of the tile has returned: refill its stage with the
+        // tile S ahead, then do the tile's arithmetic from registers
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if constexpr (S > 1) issue(st, min(jj + st + S, nb - 1));
         else if (jj + 1 < nb) issue(0, jj + 1);
+        if ((j0 + jj + st + 1) * kBlockTokens > tok1)
+          compute(ka, va, jj + st, std::true_type{});
+        else
+          compute(ka, va, jj + st, std::false_type{});
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -114,7 +114,7 @@ constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 // Verify prefetch depth (tiles in flight per wavefront) for launches with
 // many wavefronts; launches with fewer than PKV_DECODE_FEW_WAVES take 3.
 #ifndef PKV_VERIFY_SHALLOW_STAGES
-#define PKV_VERIFY_SHALLOW_STAGES 2
+#define PKV_VERIFY_SHALLOW_STAGES 1
 #endif
 #ifndef PKV_VERIFY_RESCALE_SLACK
 #define PKV_VERIFY_RESCALE_SLACK 8.0f

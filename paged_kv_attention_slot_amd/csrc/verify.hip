@@ -83,7 +83,7 @@ __device__ __forceinline__ int verify_units(const AttendArgs &a, int b, int G) {
 // its largest segment); S: K/V tiles in flight per wavefront.  Neither
 // changes the arithmetic of any pair.
 template <int D, int NC, int S>
-__global__ __launch_bounds__(64, 2) void verify_kernel(AttendArgs a, int G) {
+__global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs a, int G) {
   using M = VGeo<D>;
   static_assert(NC >= 1 && NC <= verify_col_tiles(D) && S >= 1 && S <= 3, "verify geometry");
   __shared__ __align__(16) unsigned char kst[S][M::kTile];
@@ -188,20 +188,34 @@ __global__ __launch_bounds__(64, 2) void verify_kernel(AttendArgs a, int G) {
       for (int dt = 0; dt < M::kDTiles; ++dt) o[c][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto compute = [&](int stage, int jj, auto masked_tag) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
+    // A landed tile's operands go to registers first, so that its stage can
+    // be refilled before the tile's arithmetic: K (lane holds key l16, dims
+    // 32 kk + 8 lg .. + 7) and V^T (lane i of each 16-lane group points at
+    // row 4 lg + i / 4, dims 16 dt + 4 (i % 4); it receives rows
+    // 4 lg .. + 3 of dim 16 dt + i).
+    const int vt_row = lg * 4 + (l16 >> 2);
+    auto read_tile = [&](int stage, bf16x8_t(&ka)[M::kKSteps], shortx4_t(&va)[M::kDTiles]) {
       const unsigned char *kt = kst[stage];
       const unsigned char *vt = vst[stage];
+#pragma unroll
+      for (int kk = 0; kk < M::kKSteps; ++kk)
+        ka[kk] = *reinterpret_cast<const bf16x8_t *>(kt + l16 * M::kRowBytes + M::swz(l16, kk * 4 + lg) * 16);
+#pragma unroll
+      for (int dt = 0; dt < M::kDTiles; ++dt) {
+        const int dd = dt * 16 + 4 * (l16 & 3);
+        va[dt] = vlds_tr16(vt + vt_row * M::kRowBytes + M::swz(vt_row, dd >> 3) * 16 + (dd & 7) * 2);
+      }
+    };
+    auto compute = [&](const bf16x8_t(&ka)[M::kKSteps], const shortx4_t(&va)[M::kDTiles], int jj, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
       const int tokbase = (j0 + jj) * kBlockTokens;
       floatx4_t s[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) s[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < M::kKSteps; ++kk) {
-        const bf16x8_t ka =
-            *reinterpret_cast<const bf16x8_t *>(kt + l16 * M::kRowBytes + M::swz(l16, kk * 4 + lg) * 16);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) s[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c][kk], s[c], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) s[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qb[c][kk], s[c], 0, 0, 0);
       }
       // lane holds tokens tokbase + 4 lg + e of pair column l16
       bool tv[4];
@@ -243,19 +257,15 @@ __global__ __launch_bounds__(64, 2) void verify_kernel(AttendArgs a, int G) {
         pbs[c] = __builtin_bit_cast(shortx4_t, bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
                                                         static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])});
       }
-      // V^T operand: lane i of each 16-lane group points at row 4 lg + i / 4,
-      // dims 16 dt + 4 (i % 4); it receives rows 4 lg .. + 3 of dim 16 dt + i.
-      const int vt_row = lg * 4 + (l16 >> 2);
 #pragma unroll
       for (int dt = 0; dt < M::kDTiles; ++dt) {
-        const int dd = dt * 16 + 4 * (l16 & 3);
-        shortx4_t va = vlds_tr16(vt + vt_row * M::kRowBytes + M::swz(vt_row, dd >> 3) * 16 + (dd & 7) * 2);
+        shortx4_t v = va[dt];
         if constexpr (MASKED) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) va[e] = tv[e] ? va[e] : static_cast<short>(0);   // select, never multiply poison
+          for (int e = 0; e < 4; ++e) v[e] = tv[e] ? v[e] : static_cast<short>(0);   // select, never multiply poison
         }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbs[c], o[c][dt], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pbs[c], o[c][dt], 0, 0, 0);
       }
     };
 
@@ -271,14 +281,18 @@ __global__ __launch_bounds__(64, 2) void verify_kernel(AttendArgs a, int G) {
       // tile jj sits in stage st: landed once at most S - 1 newer tiles'
       // loads are outstanding
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * M::kLoads * (S - 1)) : "memory");
-      const int tokbase = (j0 + jj) * kBlockTokens;
-      if (tokbase + kBlockTokens > tok1 || tokbase + kBlockTokens - 1 > first_pos)
-        compute(st, jj, std::true_type{});
-      else
-        compute(st, jj, std::false_type{});
-      // refill this stage once every LDS read of it has returned
+      bf16x8_t ka[M::kKSteps];
+      shortx4_t va[M::kDTiles];
+      read_tile(st, ka, va);
+      // every LDS read of the tile has returned: refill its stage, then do
+      // the tile's arithmetic from registers
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(st, min(jj + S, nb - 1));
+      const int tokbase = (j0 + jj) * kBlockTokens;
+      if (tokbase + kBlockTokens > tok1 || tokbase + kBlockTokens - 1 > first_pos)
+        compute(ka, va, jj, std::true_type{});
+      else
+        compute(ka, va, jj, std::false_type{});
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

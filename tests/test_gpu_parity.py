@@ -123,7 +123,8 @@ EDGE_SEQS = [
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 8), (128, 40, 8), (64, 8, 1)])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 8), (128, 40, 8), (64, 8, 1),
+                                      (128, 24, 8), (64, 12, 2), (128, 14, 2)])   # G 4, 1, 5, 8, 3, 6, 7
 @pytest.mark.parametrize("case", range(len(EDGE_SEQS)))
 def test_edge_cases(dtype, d, hq, hkv, case, gpu_available):
     seqs = EDGE_SEQS[case]
@@ -385,7 +386,8 @@ def test_q8_config3_append_bit_exact_and_attention(fused, gpu_available):
     _check_close("config 3q", outs[0][0], res[0]["out"], TOL["bf16"])
 
 
-@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 8), (128, 40, 8), (64, 8, 1), (128, 32, 4)])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 8), (128, 40, 8), (64, 8, 1), (128, 32, 4),
+                                      (128, 24, 8), (64, 14, 2)])   # G 4, 1, 5, 8, 8, 3, 7
 @pytest.mark.parametrize("case", range(len(Q8_EDGE)))
 def test_q8_edge_cases(d, hq, hkv, case, gpu_available):
     _log(f"q8 edge case {case} D{d} {hq}/{hkv}")

@@ -14,10 +14,14 @@ Each timed step is a real decode step: every sequence grows by one token.
 Prints one JSON line:
   value        = decode KV bytes read per step x steps / wall time  (GB/s)
   ms_per_step  = wall time / steps (host lowering included)
+  step_gpu_ms  = each timed step's GPU work (append + attention) between HIP
+                 events on the stream, p10 / p50 / p90
   roofline     = the attention launch (decode kernel + partition reduce),
                  replayed 20 times on the last step's metadata after the timed
-                 steps, each call bracketed by HIP events on its stream;
-                 algorithmic bytes per call / mean duration vs 8 TB/s
+                 steps with the caches flushed before each call (a 1 GiB
+                 fill, outside the events), each call bracketed by HIP events
+                 on its stream; algorithmic bytes per call / mean duration vs
+                 8 TB/s (attend_ms_warm_avg: the same calls back to back)
   cpu_baseline = the CPU oracle on a bounded sample of the same step
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--step N] [--no-cpu-baseline]
@@ -374,14 +378,20 @@ def main():
         one_step()
     torch.cuda.synchronize()
     metas = []
+    # each timed step's GPU work (append + attention) bracketed by HIP events
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     gc.collect()
     gc.disable()            # no collector pauses inside the timed region
     t0 = time.perf_counter()
     for i in range(args.steps):
+        step_ev[i][0].record(stream)
         metas.append(one_step())
+        step_ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
+    step_gpu = sorted(a_.elapsed_time(b_) for a_, b_ in step_ev)
     for meta in metas:
         lens = meta.host["context_lens"][meta.host["row_to_slot"]].tolist()
         kv, alg = decode_bytes(w, lens, w.elem_bytes)
@@ -389,19 +399,34 @@ def main():
         lens_hist.append(sum(lens))
     # Roofline of the attention launch (decode kernel + partition reduce):
     # replay it on the last step's metadata, each call bracketed by HIP events
-    # recorded on the stream the kernels run on.
+    # recorded on the stream the kernels run on.  Cold: before each call a
+    # 1 GiB fill (4x the 256 MB Infinity Cache) evicts the caches, outside
+    # the events; the roofline uses the cold calls.  Warm: back to back.
     last = metas[-1]
     lens = last.host["context_lens"][last.host["row_to_slot"]].tolist()
     _, alg_attend = decode_bytes(w, lens, w.elem_bytes)
     reps = 20
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a_, b_ in ev:
-        a_.record(stream)
-        eng.attend(last, q, w.scale, out=out)
-        b_.record(stream)
-    torch.cuda.synchronize()
-    attend_avg_s = sum(a_.elapsed_time(b_) for a_, b_ in ev) / reps / 1e3
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def replay(cold):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a_, b_) in enumerate(ev):
+            if cold:
+                flush.fill_(i & 0xFF)
+            a_.record(stream)
+            eng.attend(last, q, w.scale, out=out)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        return sorted(a_.elapsed_time(b_) for a_, b_ in ev)
+
+    warm_ms = replay(False)
+    cold_ms = replay(True)
+    del flush
+    attend_avg_s = sum(cold_ms) / reps / 1e3
     achieved = alg_attend / attend_avg_s / 1e9
+
+    def pct(v, f):
+        return round(v[min(len(v) - 1, int(f * len(v)))], 4)
     q8 = getattr(w, "kv_quant", "") == "q8"
     src = source_hash(*(TRAFFIC_SOURCES_Q8 if q8 else TRAFFIC_SOURCES))
     traffic = measured_traffic(f"decode_config{w.name}", src)
@@ -423,7 +448,10 @@ def main():
                    "cached_tokens_per_step": int(sum(lens_hist) / len(lens_hist)),
                    "decode_partition_tokens": pk.decode_partition_tokens()},
         "pct_hbm_peak": round(100.0 * kv_total / wall / 1e9 / HBM_PEAK_GBS, 2),
+        "step_gpu_ms": {"p10": pct(step_gpu, 0.1), "p50": pct(step_gpu, 0.5), "p90": pct(step_gpu, 0.9)},
         "attend_ms_avg": round(attend_avg_s * 1e3, 4),
+        "attend_ms_cold": {"p10": pct(cold_ms, 0.1), "p50": pct(cold_ms, 0.5), "p90": pct(cold_ms, 0.9)},
+        "attend_ms_warm_avg": round(sum(warm_ms) / reps, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("pkv decode_q8_kernel" if q8 else "pkv decode_mfma_kernel")

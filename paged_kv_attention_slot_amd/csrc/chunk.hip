@@ -220,18 +220,20 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-  // Direct-to-LDS staging.  Thread tid fills 16-byte chunks q = x * 256 + tid
-  // of each K and V stage: token row t = q / kCPR, position p = q % kCPR,
-  // taking chunk ring_swz(t, p) of that row.  One wavefront's 64 chunks of a
-  // step x are kRowsW consecutive token rows (8 for D = 64, 4 for D = 128)
-  // inside a single pool block, so the block lookup and the 64-bit base are
-  // wave-uniform (scalar registers) and each lane adds a fixed 32-bit offset.
-  // Tokens past the sequence read the last token (finite data; their scores
-  // are masked and their weights are exactly zero).
-  constexpr int kRowsX = kWaves * kWave / kCPR;     // token rows per step x
-  constexpr int kRowsW = kWave / kCPR;              // of which one wavefront's
+  // Direct-to-LDS staging.  Wavefront w fills token rows w R .. w R + R - 1
+  // of each K and V stage (R = T / 4: 16 at D = 64, 8 at D = 128), all inside
+  // one pool block: load x covers kRowsW of them, lane l row
+  // t = w R + x kRowsW + l / kCPR, position p = l % kCPR, taking chunk
+  // ring_swz(t, p) of that row.  So one block lookup per tile serves the
+  // wavefront, the 64-bit base is wave-uniform (scalar registers) and each
+  // lane adds a fixed 32-bit offset.  Tokens past the sequence read the last
+  // token (finite data; their scores are masked and their weights are
+  // exactly zero).
+  constexpr int kRowsW = kWave / kCPR;              // token rows per load
+  constexpr int kR = T / kWaves;                    // token rows per wavefront
   constexpr int kBlockBytes = kBlockTokens * kRowBytes;
-  static_assert(kBlockTokens % kRowsW == 0 && T % kBlockTokens == 0, "a wavefront's rows stay inside one block");
+  static_assert(kR == kPer * kRowsW && kBlockTokens % kR == 0 && T % kBlockTokens == 0,
+                "a wavefront's rows stay inside one block");
   const int32_t *bt = a.block_tables + static_cast<int64_t>(si.slot) * a.max_blocks;
   const char *kbase = static_cast<const char *>(a.k);
   const char *vbase = static_cast<const char *>(a.v);
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   unsigned voff[kPer], col_off[kPer];
 #pragma unroll
   for (int x = 0; x < kPer; ++x) {
-    const int t = x * kRowsX + wave * kRowsW + lane_row;          // row within the stage
+    const int t = wave * kR + x * kRowsW + lane_row;              // row within the stage
     col_off[x] = static_cast<unsigned>(ring_swz<D>(t, lane - lane_row * kCPR) * 16);
     voff[x] = static_cast<unsigned>((t % kBlockTokens) * kRowBytes) + col_off[x];
   }
@@ -251,27 +253,26 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   // slice staged in LDS per pass, so no other vector load sits in the loop.
   __shared__ int bt_lds[kTableWindow];
   int blk0 = 0;
-  // Block-table entries (from the staged slice) of tile rt's rows that this
-  // wavefront loads; read one iteration before the loads that use them.
-  auto lookup = [&](int rt, int(&ph)[kPer]) {
-#pragma unroll
-    for (int x = 0; x < kPer; ++x)
-      ph[x] = __builtin_amdgcn_readfirstlane(bt_lds[min(rt * T + x * kRowsX + wave * kRowsW, L - 1) / kBlockTokens - blk0]);
+  // Block-table entry (from the staged slice) of the block holding tile rt's
+  // rows that this wavefront loads; read one iteration before the loads that
+  // use it.
+  auto lookup = [&](int rt) {
+    return __builtin_amdgcn_readfirstlane(bt_lds[min(rt * T + wave * kR, L - 1) / kBlockTokens - blk0]);
   };
-  auto issue_ph = [&](int stage, int rt, const int(&ph)[kPer]) {
+  auto issue_ph = [&](int stage, int rt, int phys) {
     unsigned char *kd = lds + stage * 2 * kStageBytes;
     unsigned char *vd = kd + kStageBytes;
     const bool tail = rt * T + T > L;                // uniform
+    const int row0 = rt * T + wave * kR;             // wavefront's first row
+    const int blk = min(row0, L - 1) / kBlockTokens;
 #pragma unroll
     for (int x = 0; x < kPer; ++x) {
-      const int tok0 = rt * T + x * kRowsX + wave * kRowsW;       // wavefront's first row
-      const int blk = min(tok0, L - 1) / kBlockTokens;
-      const int phys = ph[x];
       unsigned off = voff[x];
       if (tail)
-        off = static_cast<unsigned>((min(tok0 + lane_row, L - 1) - blk * kBlockTokens) * kRowBytes) + col_off[x];
-      const unsigned dst = lds_addr32(kd) + (x * (kWaves * kWave) + wave * kWave) * 16;
-      const unsigned dstv = lds_addr32(vd) + (x * (kWaves * kWave) + wave * kWave) * 16;
+        off = static_cast<unsigned>((min(row0 + x * kRowsW + lane_row, L - 1) - blk * kBlockTokens) * kRowBytes) +
+              col_off[x];
+      const unsigned dst = lds_addr32(kd) + (wave * kR + x * kRowsW) * kRowBytes;
+      const unsigned dstv = lds_addr32(vd) + (wave * kR + x * kRowsW) * kRowBytes;
       const char *gk, *gv;
       if constexpr (OFF32) {
         off += static_cast<unsigned>(phys) * static_cast<unsigned>(blk_stride) + static_cast<unsigned>(head_off);
@@ -290,11 +291,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
                    : "memory");
     }
   };
-  auto issue = [&](int stage, int rt) {
-    int ph[kPer];
-    lookup(rt, ph);
-    issue_ph(stage, rt, ph);
-  };
+  auto issue = [&](int stage, int rt) { issue_ph(stage, rt, lookup(rt)); };
   const int last_blk = (L - 1) / kBlockTokens;
   constexpr int kPassTiles = kTableWindow * kBlockTokens / T;
   static_assert(S >= 3, "V of tile t and K of tile t + 1 are resident together");
@@ -456,8 +453,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     qk(0, s0);
     mask(pass0, s0);
     bool raise = rowmax(s0, mnew);
-    int ph_next[kPer];
-    lookup(min(pass0 + S - 1, pass1 - 1), ph_next);
+    int ph_next = lookup(min(pass0 + S - 1, pass1 - 1));
 
     // One iteration: tile rt's scores are in `cur`, tile rt + 1's go to `nxt`.
     auto iter = [&](int rt, floatx16_t(&cur)[kTT], floatx16_t(&nxt)[kTT], auto masked_next) {
@@ -479,7 +475,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       // Phase B: O += V P of tile rt, the row sums, and the row max of tile
       // rt + 1.
       raise = phase_b(pb, va, st, nxt, mnew) && rt + 1 < pass1;
-      lookup(min(rt + S, pass1 - 1), ph_next);
+      ph_next = lookup(min(rt + S, pass1 - 1));
     };
     // Tiles before `unmasked_end` need no causal mask for any row of this
     // wave.  Iterations whose next tile is among them run branch-free, two at

@@ -275,8 +275,7 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
     // hold the register budget).
 #pragma unroll
     for (int st = 0; st < S; ++st) issue(st, min(st, nb - 1));
-#pragma unroll 1
-    for (int jj = 0; jj < nb; ++jj) {
+    auto step = [&](int jj, auto masked_tag) {
       const int st = jj % S;
       // tile jj sits in stage st: landed once at most S - 1 newer tiles'
       // loads are outstanding
@@ -288,12 +287,17 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
       // the tile's arithmetic from registers
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(st, min(jj + S, nb - 1));
-      const int tokbase = (j0 + jj) * kBlockTokens;
-      if (tokbase + kBlockTokens > tok1 || tokbase + kBlockTokens - 1 > first_pos)
-        compute(ka, va, jj, std::true_type{});
-      else
-        compute(ka, va, jj, std::false_type{});
-    }
+      compute(ka, va, jj, masked_tag);
+    };
+    // Tiles needing no mask (wholly before tok1 and before the first row's
+    // position) come first: a loop of those, then the masked rest, so that
+    // neither loop branches per tile.
+    const int unmasked = max(0, min(nb, min(tok1, first_pos + 1) / kBlockTokens - j0));
+    int jj = 0;
+#pragma unroll 1
+    for (; jj < unmasked; ++jj) step(jj, std::false_type{});
+#pragma unroll 1
+    for (; jj < nb; ++jj) step(jj, std::true_type{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Lane groups hold disjoint tokens: combine their sums, then store.

@@ -179,6 +179,8 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   const int rt_end = min(rt_begin + cs.tps * (kKV / T), (kv_end + T - 1) / T);
   if (rt_begin >= rt_end) return;
   const bool partial_out = cs.splits > 1;
+  // tiles nobody else reads in this launch stream past the caches
+  const bool stream_tiles = PKV_CHUNK_STREAM_LOADS == 1 || (PKV_CHUNK_STREAM_LOADS == 2 && cs.mtiles == 1);
   if (partial_out && a.chunk_part == nullptr) return;
   const int wave_pos0 = mw < mtot ? L - n + mw / G : -1;
 
@@ -259,7 +261,9 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   auto lookup = [&](int rt) {
     return __builtin_amdgcn_readfirstlane(bt_lds[min(rt * T + wave * kR, L - 1) / kBlockTokens - blk0]);
   };
-  auto issue_ph = [&](int stage, int rt, int phys) {
+  // One tile's loads, with or without the streaming hint (a compile-time
+  // string in the instruction): the choice is one uniform branch per tile.
+  auto issue_loads = [&](int stage, int rt, int phys, auto stream_tag) {
     unsigned char *kd = lds + stage * 2 * kStageBytes;
     unsigned char *vd = kd + kStageBytes;
     const bool tail = rt * T + T > L;                // uniform
@@ -283,13 +287,18 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
         gk = kbase + boff;
         gv = vbase + boff;
       }
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 " PKV_CHUNK_DMA_HINT ::"s"(dst), "v"(off),
-                   "s"(gk)
-                   : "memory");
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 " PKV_CHUNK_DMA_HINT ::"s"(dstv), "v"(off),
-                   "s"(gv)
-                   : "memory");
+      if constexpr (decltype(stream_tag)::value) {
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(dst), "v"(off), "s"(gk) : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(dstv), "v"(off), "s"(gv) : "memory");
+      } else {
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(gk) : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dstv), "v"(off), "s"(gv) : "memory");
+      }
     }
+  };
+  auto issue_ph = [&](int stage, int rt, int phys) {
+    if (stream_tiles) issue_loads(stage, rt, phys, std::true_type{});
+    else issue_loads(stage, rt, phys, std::false_type{});
   };
   auto issue = [&](int stage, int rt) { issue_ph(stage, rt, lookup(rt)); };
   const int last_blk = (L - 1) / kBlockTokens;

@@ -44,15 +44,11 @@ constexpr int kDecodeMfmaMinWaves = PKV_DECODE_MFMA_MIN_WAVES;
 #else
 #define PKV_LDS_DMA_HINT ""
 #endif
-// Chunk K/V tiles are read again by every row tile of their segment (hits
-// in L2), so by default they are loaded without the streaming hint.
+// Chunk kernel tile loads: 0 cached, 1 nontemporal, 2 nontemporal for
+// segments with one row tile (each K/V byte read by one workgroup per KV
+// head) and cached for longer ones (row tiles re-read the same tiles).
 #ifndef PKV_CHUNK_STREAM_LOADS
-#define PKV_CHUNK_STREAM_LOADS 0
-#endif
-#if PKV_CHUNK_STREAM_LOADS
-#define PKV_CHUNK_DMA_HINT "nt"
-#else
-#define PKV_CHUNK_DMA_HINT ""
+#define PKV_CHUNK_STREAM_LOADS 2
 #endif
 // Fence the chunk kernel's hand-interleaved matrix-core / vector-ALU steps
 // so that the scheduler keeps them side by side (1), or leave the order of
@@ -101,10 +97,12 @@ constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 // verify kernel (short speculative drafts); longer ones to the chunk kernel.
 // The choice depends only on the segment's own (n, G) and the head dim.
 // PKV_VERIFY_MAX_PAIRS, when set, lowers the limit (0 turns the path off).
-// The column groups of a verify partition read the same tiles: loaded with
-// default caching (later groups hit in L2) unless PKV_VERIFY_STREAM_LOADS.
+// A verify wavefront's tiles are read once per launch (the launch's column
+// tiles hold every segment's pairs, so no two wavefronts share a tile):
+// nontemporal loads (PKV_VERIFY_STREAM_LOADS 1) keep them from displacing
+// reused lines, and cold-cache steps stay as fast as warm ones.
 #ifndef PKV_VERIFY_STREAM_LOADS
-#define PKV_VERIFY_STREAM_LOADS 0
+#define PKV_VERIFY_STREAM_LOADS 1
 #endif
 #if PKV_VERIFY_STREAM_LOADS
 #define PKV_VERIFY_DMA_HINT "nt"

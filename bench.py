@@ -16,6 +16,8 @@ Prints one JSON line:
   ms_per_step  = wall time / steps (host lowering included)
   step_gpu_ms  = each timed step's GPU work (append + attention) between HIP
                  events on the stream, p10 / p50 / p90
+  host_ms_per_step = host time inside the step calls (lowering, the library
+                 call, staging-ring waits)
   roofline     = the attention launch (decode kernel + partition reduce),
                  replayed 20 times on the last step's metadata after the timed
                  steps with the caches flushed before each call (a 1 GiB
@@ -396,11 +398,14 @@ def main():
                for _ in range(args.steps)]
     gc.collect()
     gc.disable()            # no collector pauses inside the timed region
+    host = 0.0
     t0 = time.perf_counter()
     for i in range(args.steps):
+        h0 = time.perf_counter()
         step_ev[i][0].record(stream)
         metas.append(one_step())
         step_ev[i][1].record(stream)
+        host += time.perf_counter() - h0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
@@ -462,6 +467,7 @@ def main():
                    "decode_partition_tokens": pk.decode_partition_tokens()},
         "pct_hbm_peak": round(100.0 * kv_total / wall / 1e9 / HBM_PEAK_GBS, 2),
         "step_gpu_ms": {"p10": pct(step_gpu, 0.1), "p50": pct(step_gpu, 0.5), "p90": pct(step_gpu, 0.9)},
+        "host_ms_per_step": round(host / args.steps * 1e3, 4),
         "attend_ms_avg": round(attend_avg_s * 1e3, 4),
         "attend_ms_cold": {"p10": pct(cold_ms, 0.1), "p50": pct(cold_ms, 0.5), "p90": pct(cold_ms, 0.9)},
         "attend_ms_warm_avg": round(sum(warm_ms) / reps, 4),

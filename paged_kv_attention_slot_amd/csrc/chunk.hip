@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   // rows that this wavefront loads; read one iteration before the loads that
   // use it.
   auto lookup = [&](int rt) {
-    return __builtin_amdgcn_readfirstlane(bt_lds[min(rt * T + wave * kR, L - 1) / kBlockTokens - blk0]);
+    return __builtin_amdgcn_readfirstlane(bt_lds[static_cast<int>(static_cast<unsigned>(min(rt * T + wave * kR, L - 1)) / kBlockTokens) - blk0]);
   };
   // One tile's loads, with or without the streaming hint (a compile-time
   // string in the instruction): the choice is one uniform branch per tile.
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     unsigned char *vd = kd + kStageBytes;
     const bool tail = rt * T + T > L;                // uniform
     const int row0 = rt * T + wave * kR;             // wavefront's first row
-    const int blk = min(row0, L - 1) / kBlockTokens;
+    const int blk = static_cast<int>(static_cast<unsigned>(min(row0, L - 1)) / kBlockTokens);
 #pragma unroll
     for (int x = 0; x < kPer; ++x) {
       unsigned off = voff[x];
@@ -466,13 +466,13 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
 
     // One iteration: tile rt's scores are in `cur`, tile rt + 1's go to `nxt`.
     auto iter = [&](int rt, floatx16_t(&cur)[kTT], floatx16_t(&nxt)[kTT], auto masked_next) {
-      const int st = (rt - pass0) % S;
-      const int st_next = (rt + 1 - pass0) % S;
+      const int st = static_cast<int>(static_cast<unsigned>(rt - pass0) % S);
+      const int st_next = static_cast<int>(static_cast<unsigned>(rt + 1 - pass0) % S);
       // Tile rt + 1 has landed (at most S - 3 newer tiles outstanding); past
       // the barrier every wave is done with tile rt - 1, whose stage refills.
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 3)) : "memory");
       __syncthreads();
-      issue_ph((rt - pass0 + S - 1) % S, min(rt + S - 1, pass1 - 1), ph_next);
+      issue_ph(static_cast<int>(static_cast<unsigned>(rt - pass0 + S - 1) % S), min(rt + S - 1, pass1 - 1), ph_next);
       rescale(mnew, raise, cur);
       bf16x8_t pb[kPS];
       bf16x8_t va[kDT][kPS];

@@ -135,6 +135,55 @@ def test_edge_cases(dtype, d, hq, hkv, case, gpu_available):
     _check_close(f"edge {case}", outs[0][0], res[0]["out"], TOL[dtype])
 
 
+def _rising_scores(w, seed, top=24.0, spike=12.0, spikes=3):
+    """Rewrite Q and K of a one-step bf16 workload so that each sequence's
+    scores (log2 units: q.k * scale * log2 e) climb about `top` from its first
+    key to its last, with `spikes` isolated keys `spike` above the climb.  The
+    running max then moves past any rescale slack in tiles well after the
+    first, and some of those moves happen inside one tile."""
+    from workloads.configs import bf16_bits_from_f32
+    rng = np.random.default_rng(seed)
+    d, hkv, hq = w.head_dim, w.num_kv_heads, w.num_q_heads
+    to_qk = 1.0 / (w.scale * np.log2(np.e))            # log2 units -> q.k units
+    u = rng.standard_normal((hkv, d)).astype(np.float32)
+    unit = u / (u * u).sum(-1, keepdims=True)            # q . (b unit) = b for q = u
+    step = w.steps[0]
+    k_new = np.zeros(step.k_new.shape, np.float32)
+    q = np.zeros(step.q.shape, np.float32)
+    hist = {slot: kh for slot, kh, _ in w.history}
+    new_k_hist = {}
+    off = 0
+    for seg in step.segments:
+        h = hist[seg.slot].shape[0]
+        L = h + seg.n
+        b = top * np.arange(L) / max(L - 1, 1)
+        b[rng.choice(L, size=min(spikes, L), replace=False)] += spike
+        keys = (b * to_qk)[:, None, None] * unit[None] + 0.1 * rng.standard_normal((L, hkv, d))
+        new_k_hist[seg.slot] = keys[:h]
+        k_new[off:off + seg.n] = keys[h:]
+        q[off:off + seg.n] = u[np.arange(hq) // (hq // hkv)][None] + 0.1 * rng.standard_normal((seg.n, hq, d))
+        off += seg.n
+    conv = bf16_bits_from_f32 if w.dtype == "bf16" else (lambda x: x.astype(np.float32))
+    w.history = [(slot, conv(new_k_hist[slot].astype(np.float32)), vh) for slot, _, vh in w.history]
+    step.k_new = conv(k_new)
+    step.q = conv(q)
+    return w
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (64, 8, 8), (128, 40, 8), (128, 8, 1)])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_rising_scores_move_the_running_max(d, hq, hkv, seed, gpu_available):
+    """Scores that climb along the sequence, with isolated spikes: every
+    kernel's lazy rescale (and any vote that triggers it) fires repeatedly
+    after the first tile, for a prompt chunk, short drafts and decode rows."""
+    seqs = [(0, 900, 300), (1, 2000, 40), (2, 60, 5), (3, 3000, 1), (4, 0, 200)]
+    _log(f"rising scores D{d} {hq}/{hkv} seed {seed}")
+    w = _rising_scores(make_custom(seqs, dtype="bf16", hq=hq, hkv=hkv, d=d, seed=300 + seed), seed)
+    _, outs = _run_gpu(w)
+    res, _ = run_workload(w)
+    _check_close("rising", outs[0][0], res[0]["out"], TOL["bf16"])
+
+
 def test_single_token_context_is_v0(gpu_available):
     """One visible key: the output is that key's V.  The kernel forms the
     softmax weight as exp2(fma(s, c, -round(s c))), i.e. 1 + (rounding residue

@@ -134,9 +134,10 @@ __host__ __device__ constexpr int verify_rows_cap(int G, int head_dim) {
   return G > 0 ? verify_max_pairs(head_dim) / G : 0;
 }
 
-// Fewest 64-token K/V tiles per key range of a split segment.
+// Fewest 64-token K/V tiles per key range of a split segment (1,024 keys):
+// long enough to amortize a workgroup's prologue and its partial's merge.
 #ifndef PKV_CHUNK_MIN_TILES_PER_SPLIT
-#define PKV_CHUNK_MIN_TILES_PER_SPLIT 6
+#define PKV_CHUNK_MIN_TILES_PER_SPLIT 16
 #endif
 #ifndef PKV_CHUNK_SPLIT_ROW_TILES_D64
 #define PKV_CHUNK_SPLIT_ROW_TILES_D64 64

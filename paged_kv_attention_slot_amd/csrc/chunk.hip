@@ -639,14 +639,18 @@ bool chunk_supported(int32_t dtype, int32_t head_dim, int32_t group) {
 
 int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, int32_t max_context_len,
                  hipStream_t stream) {
-  (void)max_context_len;
   const int G = a.num_q_heads / a.num_kv_heads;
   // Upper bound on workgroups: per segment, row tiles x splits is at most
-  // max(row tiles, the split target) and row tiles <= n G / 128 + 1;
-  // surplus workgroups exit at once.
-  const int64_t bound =
-      (static_cast<int64_t>(a.total_q) * G / kMTile + static_cast<int64_t>(a.num_segments) * (chunk_split_row_tiles(head_dim) + 1)) *
-      a.num_kv_heads;
+  // max(row tiles, the split target) and row tiles <= n G / 128 + 1; the
+  // splits are also at most ceil(K/V tiles / the range floor) for the
+  // longest context.  Surplus workgroups exit at once.
+  const int64_t row_tiles = static_cast<int64_t>(a.total_q) * G / kMTile + a.num_segments;
+  const int64_t kv_tiles = (static_cast<int64_t>(max_context_len > 0 ? max_context_len : 1) + kKV - 1) / kKV;
+  const int64_t max_splits = (kv_tiles + PKV_CHUNK_MIN_TILES_PER_SPLIT - 1) / PKV_CHUNK_MIN_TILES_PER_SPLIT;
+  const int64_t by_target =
+      static_cast<int64_t>(a.total_q) * G / kMTile + static_cast<int64_t>(a.num_segments) * (chunk_split_row_tiles(head_dim) + 1);
+  const int64_t by_splits = row_tiles * (max_splits > 1 ? max_splits : 1);
+  const int64_t bound = (by_target < by_splits ? by_target : by_splits) * a.num_kv_heads;
   if (bound <= 0) return PKV_OK;
   if (bound > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(bound)), block(kWaves * kWave);

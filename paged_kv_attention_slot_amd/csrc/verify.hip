@@ -344,11 +344,11 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
 // partitions 0 .. (L - n + i) / 512; combined in partition order.  One
 // wavefront per (segment, query head, row of the segment).
 template <int D>
-__global__ __launch_bounds__(64) void verify_merge_kernel(AttendArgs a, int G) {
+__global__ __launch_bounds__(64) void verify_merge_kernel(AttendArgs a, int G, int grid_rows) {
   const int lane = threadIdx.x;
-  const int rows = a.verify_rows;
-  const int bh = blockIdx.x / rows;
-  const int i = blockIdx.x - bh * rows;
+  const int rows = a.verify_rows;                     // row stride of the partials
+  const int bh = blockIdx.x / grid_rows;              // grid_rows <= rows: rows some segment has
+  const int i = blockIdx.x - bh * grid_rows;
   const int b = bh / a.num_q_heads;
   const int hq = bh - b * a.num_q_heads;
   const SegInfo si = seg_info(a, b);
@@ -419,13 +419,17 @@ int launch_verify(const AttendArgs &a, int32_t head_dim, int32_t max_context_len
   }
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   if (!need_merge || a.verify_acc == nullptr || a.part_max <= 1) return PKV_OK;
-  const int64_t mgrid = static_cast<int64_t>(a.num_segments) * a.num_q_heads * a.verify_rows;
+  // One workgroup per (segment, head, row) up to the most rows a verify
+  // segment of this launch has (from the host's pair count when known).
+  int grid_rows = a.verify_rows;
+  if (max_pairs > 0 && (max_pairs + G - 1) / G < grid_rows) grid_rows = (max_pairs + G - 1) / G;
+  const int64_t mgrid = static_cast<int64_t>(a.num_segments) * a.num_q_heads * grid_rows;
   if (mgrid <= 0) return PKV_OK;
   if (mgrid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   if (head_dim == 128)
-    verify_merge_kernel<128><<<dim3(static_cast<unsigned>(mgrid)), dim3(kWave), 0, stream>>>(a, G);
+    verify_merge_kernel<128><<<dim3(static_cast<unsigned>(mgrid)), dim3(kWave), 0, stream>>>(a, G, grid_rows);
   else
-    verify_merge_kernel<64><<<dim3(static_cast<unsigned>(mgrid)), dim3(kWave), 0, stream>>>(a, G);
+    verify_merge_kernel<64><<<dim3(static_cast<unsigned>(mgrid)), dim3(kWave), 0, stream>>>(a, G, grid_rows);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

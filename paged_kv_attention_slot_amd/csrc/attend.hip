@@ -80,7 +80,8 @@ WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t 
 struct StepFacts {
   bool known = false;
   int32_t decode_rows = 0;         // segments with query_len == 1
-  int32_t chunk_segments = 0;      // segments with query_len > 1
+  int32_t chunk_segments = 0;      // segments with query_len > 1 on the chunk kernel
+  int32_t chunk_split = 0;         // of those, segments cut into key ranges
   int32_t max_decode_context = 0;  // longest context among the decode rows
   int64_t decode_parts = 0;        // split-context partitions over the decode rows
   int32_t verify_segments = 0;     // multi-row segments on the verify kernel
@@ -246,6 +247,9 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
         }
       } else {
         ++f.chunk_segments;
+        // the unclamped context: at least the kernel's count of ranges
+        if (hs[b] < 0 || hs[b] >= d->num_slots || chunk_segment_splits(hq[b], hl[hs[b]], G, pool->head_dim))
+          ++f.chunk_split;
       }
     }
   }
@@ -354,13 +358,14 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
       // the join is recorded even after a failed launch, so `s` never waits
       // on a stale event
       if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PKV_ERR_HIP;
-      const int sc = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, s);
+      const int sc = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, facts.chunk_split > 0, s);
       if (hipStreamWaitEvent(s, ax->join, 0) != hipSuccess) return PKV_ERR_HIP;
       return sd != PKV_OK ? sd : sc;
     }
   }
   if (run_chunk) {
-    const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, s);
+    const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len,
+                                !facts.known || facts.chunk_split > 0, s);
     if (st != PKV_OK) return st;
   }
   return launch_streaming(s);

@@ -73,14 +73,16 @@ struct ChunkShape {
 };
 
 template <int D>
-__device__ __forceinline__ ChunkShape chunk_shape(int n, int L, int G) {
+__host__ __device__ __forceinline__ ChunkShape chunk_shape(int n, int L, int G) {
   ChunkShape c;
   c.mtiles = (n * G + kMTile - 1) / kMTile;
   const int kv_tiles = (L + kKV - 1) / kKV;
   constexpr int kRT = chunk_split_row_tiles(D);
   int splits = c.mtiles >= kRT ? 1 : kRT / c.mtiles;
   constexpr int kMin = PKV_CHUNK_MIN_TILES_PER_SPLIT;
-  splits = max(1, min(splits, (kv_tiles + kMin - 1) / kMin));   // at least kMin K/V tiles per range
+  const int by_len = (kv_tiles + kMin - 1) / kMin;              // at least kMin K/V tiles per range
+  splits = splits < by_len ? splits : by_len;
+  splits = splits > 1 ? splits : 1;
   c.tps = (kv_tiles + splits - 1) / splits;
   c.splits = (kv_tiles + c.tps - 1) / c.tps;
   return c;
@@ -637,8 +639,14 @@ bool chunk_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   return dtype == PKV_BF16 && (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 8;
 }
 
+bool chunk_segment_splits(int32_t n, int32_t L, int32_t G, int32_t head_dim) {
+  if (n < 2 || L < n || G < 1) return false;
+  const ChunkShape c = head_dim == 128 ? chunk_shape<128>(n, L, G) : chunk_shape<64>(n, L, G);
+  return c.splits > 1;
+}
+
 int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, int32_t max_context_len,
-                 hipStream_t stream) {
+                 bool need_merge, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   // Upper bound on workgroups: per segment, row tiles x splits is at most
   // max(row tiles, the split target) and row tiles <= n G / 128 + 1; the
@@ -665,7 +673,7 @@ int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, i
     else chunk_kernel<64, false><<<grid, block, 0, stream>>>(a, G);
   }
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
-  if (a.chunk_part == nullptr) return PKV_OK;
+  if (a.chunk_part == nullptr || !need_merge) return PKV_OK;
   // Merge: at most total_q * G M-rows in split segments, padded to whole
   // units per segment.
   const int64_t units = (static_cast<int64_t>(a.total_q) * G) / kMergeRowsPerWave + a.num_segments;

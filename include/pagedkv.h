@@ -25,11 +25,10 @@
  * Conventions
  *   - All integers are int32 unless stated.  Pointers marked "device" are HIP
  *     device pointers; "host" pointers are ordinary process memory.
- *   - The caller owns every buffer (pool, inputs, outputs, workspace).  The
- *     library never allocates or frees device memory.  Its only global state
- *     is, per device, one auxiliary stream (default priority) and two events,
- *     created on first use by pkv_mixed_step and kept for the life of the
- *     process.
+ *   - The caller owns every buffer (pool, inputs, outputs, workspace), and
+ *     every stream and event the library uses.  The library never allocates
+ *     or frees device memory and creates no streams or events; it keeps no
+ *     mutable global state.
  *   - Device calls are asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL = the null stream).  Argument errors are returned before
  *     anything is launched; launch failures return PKV_ERR_HIP; faults show
@@ -172,8 +171,12 @@ int pkv_gather_kv(const int32_t *row_to_slot, int32_t num_segments, const int32_
  *   context_lens  device int32 [num_slots], indexed by slot.
  *   block_tables  device int32 [num_slots][max_blocks_per_seq], by slot.
  *   max_query_len, max_context_len   host upper bounds over the segments
- *                 (used for grid and workspace sizing only; a value smaller
- *                 than the truth gives unspecified results).
+ *                 (they size the grid and the workspace).  A bound below the
+ *                 truth gives wrong but deterministic results and no access
+ *                 outside the buffers: a segment with query_len >
+ *                 max_query_len is skipped (its rows are not written), a
+ *                 context longer than max_context_len is cut to it.
+ *                 pkv_mixed_step rejects such bounds (PKV_ERR_INVALID_ARG).
  *   scale         softmax scale (1/sqrt(head_dim) for standard attention);
  *                 finite and > 0, else PKV_ERR_INVALID_ARG.
  *   out           device [total_q][num_q_heads][head_dim]; out_dtype PKV_F32,
@@ -216,6 +219,21 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
  *                 (read from host_meta; ignored when num_copies == 0).
  *   block_tables  device, as for pkv_paged_attend (kept on the device across
  *                 steps; only changed tables need re-sending).
+ *   max_query_len, max_context_len   must hold for every segment (checked on
+ *                 the host copy; PKV_ERR_INVALID_ARG otherwise).
+ *   aux_stream, aux_fork_event, aux_join_event   optional, caller-owned
+ *                 (hipStream_t, hipEvent_t as void*; default priority).  When
+ *                 aux_stream is set (both events then required) and a step
+ *                 holds both prompt-chunk segments and decode or draft rows,
+ *                 the HBM-bound decode/draft kernels run on aux_stream beside
+ *                 the chunk kernels on `stream`: the call records
+ *                 aux_fork_event on `stream`, makes aux_stream wait on it,
+ *                 records aux_join_event on aux_stream after its kernels and
+ *                 makes `stream` wait on that, so all of the step's work is
+ *                 still ordered before later work on `stream`.  The choice
+ *                 changes no result bit.  Calls that share these objects must
+ *                 not run concurrently from several host threads.  NULL: one
+ *                 stream.
  * Other arguments as for pkv_kv_append and pkv_paged_attend; same status codes.
  * Argument errors (a bad scale included) are returned before anything is
  * appended. */
@@ -234,6 +252,8 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
   int32_t copy_off, num_copies;
+  void *aux_stream;
+  void *aux_fork_event, *aux_join_event;
 } pkv_step_desc;
 
 int pkv_mixed_step(const pkv_step_desc *step, const pkv_pool *pool, void *stream);

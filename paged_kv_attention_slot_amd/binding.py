@@ -50,7 +50,8 @@ class StepDesc(ctypes.Structure):
                 ("max_context_len", _i32), ("k_new", _p), ("v_new", _p), ("q_packed", _p),
                 ("block_tables", _p), ("scale", ctypes.c_float), ("out", _p), ("out_dtype", _i32),
                 ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
-                ("copy_off", _i32), ("num_copies", _i32)]
+                ("copy_off", _i32), ("num_copies", _i32),
+                ("aux_stream", _p), ("aux_fork_event", _p), ("aux_join_event", _p)]
 
 
 class PagedKVError(RuntimeError):

@@ -1,7 +1,6 @@
 // C-ABI entry points for the device side: argument checks, workspace sizing
 // and kernel dispatch on the caller's stream.
 #include <cmath>
-#include <mutex>
 
 #include "pagedkv.h"
 #include "pkv_internal.h"
@@ -35,7 +34,7 @@ bool multirow_on_decode_path(int32_t dtype, int32_t head_dim, int32_t group, int
 }
 
 struct WorkspaceLayout {
-  int64_t rows = 0, part_max = 0, verify_rows = 0;
+  int64_t rows = 0, part_max = 0, verify_rows = 0, chunk_slots = 0;
   size_t acc_bytes = 0, ml_bytes = 0, chunk_bytes = 0, vacc_bytes = 0, vml_bytes = 0;
   size_t decode_bytes() const { return acc_bytes + ml_bytes; }
   size_t total() const { return acc_bytes + ml_bytes + chunk_bytes + vacc_bytes + vml_bytes; }
@@ -59,14 +58,25 @@ WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t 
     w.ml_bytes = (w.ml_bytes + 255) & ~static_cast<size_t>(255);
   }
   if (max_query_len > 1 && !multirow && group > 0) {
-    // key-range partials of split multi-row segments (see chunk.hip)
+    // Multi-row segments cover disjoint rows of at least two each.
+    const int64_t multi_segs = std::min<int64_t>(num_segments, total_q / 2);
+    // Key-range partials of split multi-row segments (see chunk.hip): per KV
+    // head, a split segment holds (M-rows x ranges) slots, at most one
+    // split target's worth (chunk_split_slots), and each M-row has at most
+    // as many ranges as the longest context allows.
     const int64_t kv_heads = num_q_heads / group;
-    w.chunk_bytes = align256(static_cast<size_t>(num_segments) * kv_heads * chunk_split_slots(head_dim) *
-                             (head_dim + 4) * sizeof(float));
-    // partition partials of the rows of verify segments (see verify.hip)
+    const int64_t kv_tiles = (static_cast<int64_t>(max_context_len) + 63) / 64;
+    int64_t max_splits = (kv_tiles + PKV_CHUNK_MIN_TILES_PER_SPLIT - 1) / PKV_CHUNK_MIN_TILES_PER_SPLIT;
+    max_splits = std::min<int64_t>(max_splits, chunk_split_row_tiles(head_dim));
+    if (max_splits > 1) {
+      w.chunk_slots = std::min<int64_t>(multi_segs * chunk_split_slots(head_dim),
+                                        static_cast<int64_t>(total_q) * group * max_splits);
+      w.chunk_bytes = align256(static_cast<size_t>(kv_heads * w.chunk_slots) * (head_dim + 4) * sizeof(float));
+    }
+    // Partition partials of the rows of verify segments (see verify.hip).
     if (w.part_max > 1) {
-      w.verify_rows = verify_rows_cap(group, head_dim);
-      const int64_t n = static_cast<int64_t>(num_segments) * w.verify_rows * num_q_heads * w.part_max;
+      w.verify_rows = std::min<int64_t>(total_q, multi_segs * verify_rows_cap(group, head_dim));
+      const int64_t n = w.verify_rows * num_q_heads * w.part_max;
       w.vacc_bytes = align256(static_cast<size_t>(n) * head_dim * sizeof(float));
       w.vml_bytes = align256(static_cast<size_t>(n) * 2 * sizeof(float));
     }
@@ -90,38 +100,20 @@ struct StepFacts {
   int64_t verify_parts = 0;        // their partitions
 };
 
-// Per-device auxiliary stream (default priority) and fork/join events that
-// let a step's decode rows run beside its chunk kernels.  Created on first
-// use and kept for the life of the process; the mutex makes each fork/join
-// sequence atomic for callers on several host threads.
+// A caller-owned second stream and fork/join events that let a step's
+// HBM-bound kernels (decode rows, verify drafts) run beside its chunk
+// kernels (pkv_step_desc.aux_*); absent, everything runs on one stream.
 struct AuxStream {
-  bool tried = false, ok = false;
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
-constexpr int kMaxDevices = 64;
-std::mutex g_aux_mutex;
-AuxStream g_aux[kMaxDevices];
-
-// Call with g_aux_mutex held.
-AuxStream *aux_for_current_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  AuxStream &x = g_aux[dev];
-  if (!x.tried) {
-    x.tried = true;
-    x.ok = hipStreamCreateWithFlags(&x.stream, hipStreamNonBlocking) == hipSuccess &&
-           hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return x.ok ? &x : nullptr;
-}
 
 int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int32_t *row_to_slot,
            const int32_t *query_start, const int32_t *query_len, int32_t num_segments, const int32_t *context_lens,
            const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq, int32_t max_query_len,
            int32_t max_context_len, const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
-           size_t workspace_bytes, hipStream_t s, const StepFacts &facts, bool check_only = false);
+           size_t workspace_bytes, hipStream_t s, const StepFacts &facts, bool check_only = false,
+           const AuxStream *aux = nullptr);
 
 }  // namespace
 }  // namespace pkv
@@ -206,6 +198,20 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
     return PKV_ERR_INVALID_ARG;
   if (!pool_supported(pool)) return PKV_ERR_UNSUPPORTED;
   if (d->num_tokens > 0 && (!d->k_new || !d->v_new)) return PKV_ERR_INVALID_ARG;
+  // the second stream needs both events
+  const bool has_aux = d->aux_stream != nullptr;
+  if (has_aux && (!d->aux_fork_event || !d->aux_join_event)) return PKV_ERR_INVALID_ARG;
+  // The host bounds must hold for every segment (the host copy of the
+  // metadata is at hand here; pkv_paged_attend cannot check them).
+  {
+    const int32_t *hq = d->host_meta + d->query_len_off;
+    const int32_t *hs = d->host_meta + d->row_to_slot_off;
+    const int32_t *hl = d->host_meta + d->context_lens_off;
+    for (int32_t b = 0; b < d->num_segments; ++b) {
+      if (hq[b] > d->max_query_len) return PKV_ERR_INVALID_ARG;
+      if (hs[b] >= 0 && hs[b] < d->num_slots && hl[hs[b]] > d->max_context_len) return PKV_ERR_INVALID_ARG;
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t *m = d->dev_meta;
   // Every argument error is reported before the first launch.
@@ -255,10 +261,14 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
   }
   if (f.max_decode_context > d->max_context_len) f.max_decode_context = d->max_context_len;
   if (f.max_verify_context > d->max_context_len) f.max_verify_context = d->max_context_len;
+  AuxStream aux;
+  aux.stream = static_cast<hipStream_t>(d->aux_stream);
+  aux.fork = static_cast<hipEvent_t>(d->aux_fork_event);
+  aux.join = static_cast<hipEvent_t>(d->aux_join_event);
   return attend(d->q_packed, d->total_q, d->num_q_heads, m + d->row_to_slot_off, m + d->query_start_off,
                 m + d->query_len_off, d->num_segments, m + d->context_lens_off, d->block_tables, d->num_slots,
                 d->max_blocks_per_seq, d->max_query_len, d->max_context_len, pool, d->scale, d->out, d->out_dtype,
-                d->workspace, d->workspace_bytes, s, f);
+                d->workspace, d->workspace_bytes, s, f, false, has_aux ? &aux : nullptr);
 }
 
 }  // extern "C"
@@ -270,7 +280,7 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
            const int32_t *query_start, const int32_t *query_len, int32_t num_segments, const int32_t *context_lens,
            const int32_t *block_tables, int32_t num_slots, int32_t max_blocks_per_seq, int32_t max_query_len,
            int32_t max_context_len, const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *workspace,
-           size_t workspace_bytes, hipStream_t s, const StepFacts &facts, bool check_only) {
+           size_t workspace_bytes, hipStream_t s, const StepFacts &facts, bool check_only, const AuxStream *aux) {
   if (!pool_ok(pool) || total_q < 0 || num_segments < 0 || num_q_heads <= 0 || num_slots <= 0 ||
       max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0)
     return PKV_ERR_INVALID_ARG;
@@ -281,6 +291,7 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   if (!q_packed || !row_to_slot || !query_start || !query_len || !context_lens || !block_tables || !out)
     return PKV_ERR_INVALID_ARG;
   if (max_query_len > total_q) max_query_len = total_q;
+  if (max_query_len < 1) max_query_len = 1;
 
   const int32_t group = num_q_heads / pool->num_kv_heads;
   const bool multirow = multirow_on_decode_path(pool->dtype, pool->head_dim, group, max_query_len);
@@ -308,6 +319,9 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   a.verify_ml =
       ws.vml_bytes ? reinterpret_cast<float *>(wsb + ws.decode_bytes() + ws.chunk_bytes + ws.vacc_bytes) : nullptr;
   a.verify_rows = static_cast<int32_t>(ws.verify_rows);
+  a.chunk_slots = ws.chunk_slots;
+  a.max_query = max_query_len;
+  a.max_context = max_context_len;
   a.num_segments = num_segments;
   a.num_slots = num_slots;
   a.max_blocks = max_blocks_per_seq;
@@ -328,8 +342,8 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   // path); decode rows on the decode kernels, whose grid and partition
   // reduce follow the decode rows' own longest context when the host knows
   // it.  Chunk work is matrix-bound, decode and verify work HBM-bound: when
-  // the host knows a step has both kinds, the HBM-bound kernels run on the
-  // auxiliary stream beside the chunk kernels.
+  // the host knows a step has both kinds and the caller lent a second
+  // stream, the HBM-bound kernels run on it beside the chunk kernels.
   const bool multi = max_query_len > 1 && !multirow;
   const bool run_chunk = multi && (!facts.known || facts.chunk_segments > 0);
   const bool run_verify = multi && (!facts.known || facts.verify_segments > 0);
@@ -348,20 +362,16 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
       r = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, st);
     return r;
   };
-  if (run_chunk && (run_decode || run_verify) && facts.known && PKV_CONCURRENT_DECODE) {
-    std::lock_guard<std::mutex> lock(g_aux_mutex);
-    AuxStream *ax = aux_for_current_device();
-    if (ax) {
-      if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
-        return PKV_ERR_HIP;
-      const int sd = launch_streaming(ax->stream);
-      // the join is recorded even after a failed launch, so `s` never waits
-      // on a stale event
-      if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PKV_ERR_HIP;
-      const int sc = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, facts.chunk_split > 0, s);
-      if (hipStreamWaitEvent(s, ax->join, 0) != hipSuccess) return PKV_ERR_HIP;
-      return sd != PKV_OK ? sd : sc;
-    }
+  if (run_chunk && (run_decode || run_verify) && facts.known && aux && PKV_CONCURRENT_DECODE) {
+    if (hipEventRecord(aux->fork, s) != hipSuccess || hipStreamWaitEvent(aux->stream, aux->fork, 0) != hipSuccess)
+      return PKV_ERR_HIP;
+    const int sd = launch_streaming(aux->stream);
+    // the join is recorded even after a failed launch, so `s` never waits
+    // on a stale event
+    if (hipEventRecord(aux->join, aux->stream) != hipSuccess) return PKV_ERR_HIP;
+    const int sc = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, facts.chunk_split > 0, s);
+    if (hipStreamWaitEvent(s, aux->join, 0) != hipSuccess) return PKV_ERR_HIP;
+    return sd != PKV_OK ? sd : sc;
   }
   if (run_chunk) {
     const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len,

@@ -9,7 +9,8 @@
 //
 // Row i of a segment with n rows and L cached tokens sits at position
 // L - n + i and sees keys 0 .. L - n + i.  The contraction is dense, so it
-// runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+// runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation of the exact bf16
+// Q and K (the softmax scale multiplies each fp32 score):
 //   * "M-rows" are (query row, head of the GQA group) pairs, m = i * G + h;
 //     a workgroup of 4 wavefronts takes 128 consecutive M-rows of one
 //     segment and one KV head, so all G query heads share every K/V tile;
@@ -94,6 +95,16 @@ __device__ __forceinline__ int chunk_units(const AttendArgs &a, int b, int G) {
   if (!s.ok || s.n < 2 || verify_segment(s.n, G, D)) return 0;
   const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.mtiles * c.splits;
+}
+
+// Partial slots (per KV head) of segment b: one per (M-row, key range) when
+// the segment is cut into key ranges, else none.
+template <int D>
+__device__ __forceinline__ int chunk_partial_slots(const AttendArgs &a, int b, int G) {
+  const SegInfo s = seg_info(a, b);
+  if (!s.ok || s.n < 2 || verify_segment(s.n, G, D)) return 0;
+  const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
+  return c.splits > 1 ? s.n * G * c.splits : 0;
 }
 
 // LDS ring of K/V tiles fed by direct-to-LDS loads: kRingTok tokens per
@@ -183,12 +194,20 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   const bool partial_out = cs.splits > 1;
   // tiles nobody else reads in this launch stream past the caches
   const bool stream_tiles = PKV_CHUNK_STREAM_LOADS == 1 || (PKV_CHUNK_STREAM_LOADS == 2 && cs.mtiles == 1);
-  if (partial_out && a.chunk_part == nullptr) return;
+  // first partial slot of this segment (uniform over the workgroup)
+  int64_t part_base = 0;
+  if (partial_out) {
+    if (a.chunk_part == nullptr) return;
+    part_base = units_before(b, [&](int bb) { return chunk_partial_slots<D>(a, bb, G); });
+    if (part_base + static_cast<int64_t>(mtot) * cs.splits > a.chunk_slots) return;   // bounds understated
+  }
   const int wave_pos0 = mw < mtot ? L - n + mw / G : -1;
 
   // Q operand (B of S^T = K Q^T): lane holds dims 16 ks + 8 hh .. + 7 of
-  // its M-row, pre-multiplied by scale * log2(e) and rounded to bf16.
+  // its M-row, the query's own bf16 values (the scale is applied in fp32 to
+  // each score, so Q carries no rounding beyond its input's).
   const float c_log2 = a.scale_log2;
+  const float slack_raw = PKV_CHUNK_RESCALE_SLACK / c_log2;   // the slack in raw score units
   const int m = mw + l32;
   const bool valid = m < mtot;
   const int qi = valid ? m / G : 0;
@@ -203,17 +222,16 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
 #pragma unroll
     for (int ks = 0; ks < kQS; ++ks) {
       const uint4 w = valid ? qp[2 * ks + hh] : make_uint4(0, 0, 0, 0);
-      const bf16x8_t raw = __builtin_bit_cast(bf16x8_t, w);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[ks][j] = static_cast<__bf16>(static_cast<float>(raw[j]) * c_log2);
+      qv[ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 
-  // Online softmax state of the lane's M-row (log2 units): running max
-  // m_run, and the reference r_ref that the score accumulators start from
-  // (-r_ref), so that a tile's accumulators hold score - r_ref and its
-  // weights are exp2 of them directly.  r_ref follows m_run once the row has
-  // seen an unmasked key (0 before).  lsum: this half's row sum.
+  // Online softmax state of the lane's M-row, in raw score units (q . k):
+  // running max m_run, and the reference r_ref that the score accumulators
+  // start from (-r_ref), so that a tile's accumulators hold q . k - r_ref and
+  // its weights are exp2(scale log2(e) x accumulator).  r_ref follows m_run
+  // once the row has seen an unmasked key (0 before).  lsum: this half's row
+  // sum.
   float m_run = -FLT_MAX, r_ref = 0.f, lsum = 0.f;
   floatx16_t negr;
 #pragma unroll
@@ -333,14 +351,14 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
           if (rt * T + tt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) > pos) sc[tt][i] = -INFINITY;
     }
   };
-  // Row max of a tile (log2 units) over both halves: the candidate new
+  // Row max of a tile (raw units) over both halves: the candidate new
   // running max, and whether it exceeds the current one by more than the
   // allowed slack (the rescale vote).
   auto finish_max = [&](float part, float &mnew) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
     const float mx = r_ref + vmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     mnew = vmaxf(m_run, mx);
-    return mx > m_run + PKV_CHUNK_RESCALE_SLACK;
+    return mx > m_run + slack_raw;
   };
   auto rowmax = [&](const floatx16_t(&sc)[kTT], float &mnew) {
     float acc = vmaxf(sc[0][0], sc[0][1]);
@@ -352,7 +370,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   // re-base the pending tile's accumulators `cur` to the new reference.
   auto rescale = [&](float mnew, bool raise, floatx16_t(&cur)[kTT]) {
     if (__ballot(raise) != 0) {
-      const float alpha = fast_exp2(m_run - mnew);
+      const float alpha = fast_exp2((m_run - mnew) * c_log2);
       m_run = mnew;
       lsum *= alpha;
 #pragma unroll
@@ -409,7 +427,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       }
 #pragma unroll
       for (int w = i * kScores / kSteps; w < (i + 1) * kScores / kSteps; ++w) {
-        p[w] = fast_exp2(cur[w / 16][w % 16]);
+        p[w] = fast_exp2(cur[w / 16][w % 16] * c_log2);
         if (w % 8 == 7) {
           const float *q8 = p + (w - 7);
           pb[w / 8] = bf16x8_t{static_cast<__bf16>(q8[0]), static_cast<__bf16>(q8[1]), static_cast<__bf16>(q8[2]),
@@ -520,7 +538,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   if (!valid) return;
   if (partial_out) {
-    const int64_t pidx = (static_cast<int64_t>(b) * hkv + g) * chunk_split_slots(D) + m * cs.splits + split;
+    const int64_t pidx = static_cast<int64_t>(g) * a.chunk_slots + part_base + m * cs.splits + split;
     float *pa = a.chunk_part + pidx * kChunkSlotFloats<D>;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -528,7 +546,8 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       for (int r = 0; r < 4; ++r)
         *reinterpret_cast<float4 *>(pa + dt * 32 + 8 * r + 4 * hh) =
             make_float4(o[dt][4 * r], o[dt][4 * r + 1], o[dt][4 * r + 2], o[dt][4 * r + 3]);
-    if (hh == 0) *reinterpret_cast<float2 *>(pa + D) = make_float2(m_run, lt);
+    // the merge takes the reference in log2 units
+    if (hh == 0) *reinterpret_cast<float2 *>(pa + D) = make_float2(m_run * c_log2, lt);
     return;
   }
   const float inv = 1.f / lt;
@@ -585,13 +604,15 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void chunk_merge_kernel(Attend
   const SegInfo si = seg_info_uniform(a, b);
   if (!si.ok) return;
   const ChunkShape cs = chunk_shape<D>(si.n, si.L, G);
+  const int64_t part_base = units_before(b, [&](int bb) { return chunk_partial_slots<D>(a, bb, G); });
+  if (part_base + static_cast<int64_t>(si.n) * G * cs.splits > a.chunk_slots) return;
   const int m = u * kMergeRowsPerWave + (lane >> 4);
   if (m >= si.n * G) return;                          // no cross-group exchange below
   const int i = m / G;
   const int h = m - i * G;
   const int pos = si.L - si.n + i;
   const int last = min(cs.splits - 1, pos / (cs.tps * kKV));
-  const float *pp = a.chunk_part + ((static_cast<int64_t>(b) * hkv + g) * chunk_split_slots(D) +
+  const float *pp = a.chunk_part + (static_cast<int64_t>(g) * a.chunk_slots + part_base +
                                     static_cast<int64_t>(m) * cs.splits) * SF;
   // Row max over the ranges: lane li reads ranges li, li + 16, ...
   float mx = -FLT_MAX;

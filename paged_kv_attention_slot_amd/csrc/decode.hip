@@ -295,21 +295,27 @@ __global__ __launch_bounds__(64) void decode_kernel(AttendArgs a) {
       }
     }
 
-    // Merge the lane rows' (m, l, acc) states.
+    // Merge the lane rows' (m, l, acc) states.  Both lanes of a pair combine
+    // (lower, upper) in the same order, so every lane row ends with the same
+    // bits and the result does not depend on which lane row stores a head.
 #pragma unroll
     for (int step = LPR; step < kWave; step <<= 1) {
+      const bool upper = (lane & step) != 0;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float mo = __shfl_xor(m[h], step);
         const float lo = __shfl_xor(l[h], step);
-        const float mx = fmaxf(m[h], mo);
-        const float fa = fast_exp2(m[h] - mx);
-        const float fb = fast_exp2(mo - mx);
-        l[h] = l[h] * fa + lo * fb;
+        const float ma = upper ? mo : m[h], mb = upper ? m[h] : mo;
+        const float la = upper ? lo : l[h], lb = upper ? l[h] : lo;
+        const float mx = fmaxf(ma, mb);
+        const float fa = fast_exp2(ma - mx);
+        const float fb = fast_exp2(mb - mx);
+        l[h] = la * fa + lb * fb;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           const float ao = __shfl_xor(acc[h][e], step);
-          acc[h][e] = acc[h][e] * fa + ao * fb;
+          const float aa = upper ? ao : acc[h][e], ab = upper ? acc[h][e] : ao;
+          acc[h][e] = aa * fa + ab * fb;
         }
         m[h] = mx;
       }

@@ -16,7 +16,8 @@
 //     columns, G of them used): lane owns head lane % 16, tokens
 //     4 (lane / 16) .. + 3;
 //   * online softmax on those values: the tile max needs two cross-row
-//     shuffles, the running sum stays per lane until the end;
+//     shuffles, the running sum (of the bf16-rounded weights the PV product
+//     consumes) stays per lane until the end;
 //   * O^T[dim][head] += V^T P^T on v_mfma_f32_16x16x16_bf16, V^T read with
 //     ds_read_b64_tr_b16 straight from the [token][dim] tile, P^T straight
 //     from the S^T accumulator (P rounded to bf16, as for any bf16 MFMA).
@@ -225,9 +226,11 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[e], c_log2, -m_run));
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
       const bf16x4_t pb = bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
                                    static_cast<__bf16>(p[3])};
+      // the row sum adds the bf16 weights the PV product consumes, so that
+      // the normalisation matches the numerator
+      l_run = add_bf16x4(pb, l_run);
       const shortx4_t pbs = __builtin_bit_cast(shortx4_t, pb);
 #pragma unroll
       for (int dt = 0; dt < M::kDTiles; ++dt) {

@@ -26,8 +26,10 @@
 //     K scale;
 //   * the V codes become an fp16 [token][dim] tile in LDS, read transposed
 //     with ds_read_b64_tr_b16; the V scale is folded into P, so
-//     O^T += V^T (P * v_scale)^T on v_mfma_f32_16x16x16_f16 while the
-//     softmax sum uses P itself.
+//     O^T += V^T fp16(P * v_scale)^T on v_mfma_f32_16x16x16_f16.  That
+//     weights the stored value code * v_scale by fp16(P v_scale) / v_scale,
+//     and the softmax sum adds exactly those weights (one reciprocal per
+//     token), so the normalisation matches the numerator.
 #include <cfloat>
 #include <type_traits>
 
@@ -290,14 +292,19 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
 #pragma unroll
         for (int dt = 0; dt < M::kDTiles; ++dt) o[dt] *= alpha;
       }
-      float p[4];
+      float p[4], w[4];
       halfx4_t ph;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         p[e] = fast_exp2(fmaf(s[e], c_log2, -m_run));
         ph[e] = static_cast<_Float16>(ok[e] ? p[e] * vs[e] : 0.f);
+        // The product weights the stored value code * vs by fp16(p vs) / vs;
+        // the row sum adds that weight (p itself for a zero row, scale 0,
+        // whose value is 0 whatever its weight; nothing for masked tokens,
+        // whose scales may be unwritten).
+        w[e] = ok[e] ? (vs[e] != 0.f ? static_cast<float>(ph[e]) * __builtin_amdgcn_rcpf(vs[e]) : p[e]) : 0.f;
       }
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+      l_run += (w[0] + w[1]) + (w[2] + w[3]);
       c_run += (static_cast<float>(ph[0]) + static_cast<float>(ph[1])) +
                (static_cast<float>(ph[2]) + static_cast<float>(ph[3]));
       const int vt_row = lg * 4 + (l16 >> 2);

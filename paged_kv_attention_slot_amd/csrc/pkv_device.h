@@ -22,6 +22,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + the sum of four bf16 values (v_dot2_f32_bf16 against (1, 1); the
+// products are exact).  A softmax row sum built this way adds exactly the
+// bf16-rounded weights that a bf16 matrix product consumes.
+typedef __bf16 pkv_bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pkv_bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float add_bf16x4(pkv_bf16x4 v, float acc) {
+  const pkv_bf16x2 one2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, acc, false);
+}
+
 // A 16-byte load of data read once (K/V tiles): marked nontemporal so it
 // streams past the caches instead of displacing reused lines.
 typedef unsigned int pkv_u32x4 __attribute__((ext_vector_type(4)));
@@ -100,9 +111,9 @@ __device__ __forceinline__ SegInfo seg_info(const AttendArgs &a, int b) {
   const int n = a.query_len[b];
   const int slot = a.row_to_slot[b];
   const int r0 = a.query_start[b];
-  if (n < 1 || slot < 0 || slot >= a.num_slots || r0 < 0 || r0 > a.total_q - n) return s;
+  if (n < 1 || n > a.max_query || slot < 0 || slot >= a.num_slots || r0 < 0 || r0 > a.total_q - n) return s;
   int L = a.context_lens[slot];
-  L = min(L, a.max_blocks * kBlockTokens);
+  L = min(min(L, a.max_blocks * kBlockTokens), a.max_context);
   if (L < n) return s;
   s.slot = slot;
   s.L = L;
@@ -133,6 +144,20 @@ __device__ __forceinline__ int count_units(int num_segments, F units_fn) {
   int total = 0;
   for (int c0 = 0; c0 < num_segments; c0 += kWave) {
     int u = units_fn(c0 + lane);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) u += __shfl_xor(u, d);
+    total += u;
+  }
+  return total;
+}
+
+// Sum of units_fn(b') over the segments b' < b (the same on every lane).
+template <typename F>
+__device__ __forceinline__ int64_t units_before(int b, F units_fn) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t total = 0;
+  for (int c0 = 0; c0 < b; c0 += kWave) {
+    int u = c0 + lane < b ? units_fn(c0 + lane) : 0;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) u += __shfl_xor(u, d);
     total += u;

@@ -204,10 +204,19 @@ struct AttendArgs {
   const int32_t *block_tables;
   float *part_acc;   // [part_rows][Hq][part_max][D]
   float *part_ml;    // [part_rows][Hq][part_max][2]  (running max in log2 units, sum)
-  float *chunk_part; // [num_segments][Hkv][chunk_split_slots(D)][D + 4]: key-range partials of split chunks
-  float *verify_acc; // [num_segments][verify_rows][Hq][part_max][D]: partition partials of verify rows
-  float *verify_ml;  // [num_segments][verify_rows][Hq][part_max][2]
-  int32_t verify_rows;  // row stride per segment of the verify partials (verify_rows_cap)
+  // Key-range partials of split multi-row segments: [Hkv][chunk_slots][D + 4].
+  // Segment b's slots start after those of the split segments before it
+  // (chunk_slot_base); M-row m, range s of it is slot base + m * splits + s.
+  float *chunk_part;
+  // Partition partials of verify rows: [verify_rows][Hq][part_max][D] and
+  // [verify_rows][Hq][part_max][2]; segment b's rows start after those of the
+  // verify segments before it (verify_row_base).
+  float *verify_acc;
+  float *verify_ml;
+  int64_t chunk_slots;  // capacity of chunk_part per KV head, in slots
+  int32_t verify_rows;  // capacity of the verify partials, in rows
+  int32_t max_query;    // host bounds: a segment longer than max_query is skipped,
+  int32_t max_context;  // a context longer than max_context is cut to it
   int32_t num_segments;
   int32_t num_slots;
   int32_t max_blocks;

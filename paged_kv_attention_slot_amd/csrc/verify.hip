@@ -19,7 +19,8 @@
 //   * the causal mask (row i sits at L - n + i) only on tiles reaching past
 //     the first row's position or the partition's end;
 //   * online softmax per pair, the running max allowed to lag by
-//     PKV_VERIFY_RESCALE_SLACK before O and l are rescaled;
+//     PKV_VERIFY_RESCALE_SLACK before O and l are rescaled; l adds the
+//     bf16-rounded weights that the PV product consumes;
 //   * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, V^T read transposed once
 //     per output tile and used for every column tile.
 // A row with one partition writes its output; otherwise partials (O, m, l)
@@ -79,6 +80,13 @@ __device__ __forceinline__ int verify_units(const AttendArgs &a, int b, int G) {
   return s.ok && verify_segment(s.n, G, D) ? vnum_parts(s.L) * vgroups<NC>(s.n, G) : 0;
 }
 
+// Rows of segment b in the verify partials (all of a verify segment's rows).
+template <int D>
+__device__ __forceinline__ int verify_partial_rows(const AttendArgs &a, int b, int G) {
+  const SegInfo s = seg_info(a, b);
+  return s.ok && verify_segment(s.n, G, D) ? s.n : 0;
+}
+
 // NC: 16-wide pair tiles per wavefront (the launch takes the fewest that hold
 // its largest segment); S: K/V tiles in flight per wavefront.  Neither
 // changes the arithmetic of any pair.
@@ -115,6 +123,8 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
     const int j0 = tok0 / kBlockTokens;
     const int nb = (tok1 + kBlockTokens - 1) / kBlockTokens - j0;
     const int first_pos = si.L - si.n;          // position of row 0
+    // first row of this segment in the verify partials (uniform)
+    const int64_t vrow0 = np > 1 ? units_before(b, [&](int bb) { return verify_partial_rows<D>(a, bb, G); }) : 0;
 
     // Column tile c of this group: pair m = (cg * NC + c) * 16 + l16.
     int pos[NC];
@@ -253,9 +263,10 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[c][e], c_log2, -m_run[c]));
-        l_run[c] += (p[0] + p[1]) + (p[2] + p[3]);
-        pbs[c] = __builtin_bit_cast(shortx4_t, bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
-                                                        static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])});
+        const bf16x4_t pb = bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                                     static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+        l_run[c] = add_bf16x4(pb, l_run[c]);     // the weights the PV product consumes
+        pbs[c] = __builtin_bit_cast(shortx4_t, pb);
       }
 #pragma unroll
       for (int dt = 0; dt < M::kDTiles; ++dt) {
@@ -327,8 +338,8 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
           }
         }
       } else {
-        if (a.verify_acc == nullptr || part >= a.part_max) continue;
-        const int64_t prow = static_cast<int64_t>(b) * a.verify_rows + i;
+        if (a.verify_acc == nullptr || part >= a.part_max || vrow0 + si.n > a.verify_rows) continue;
+        const int64_t prow = vrow0 + i;
         const int64_t pidx = (prow * a.num_q_heads + qhead) * a.part_max + part;
         float *pa = a.verify_acc + pidx * D + lg * 4;
 #pragma unroll
@@ -346,18 +357,19 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
 template <int D>
 __global__ __launch_bounds__(64) void verify_merge_kernel(AttendArgs a, int G, int grid_rows) {
   const int lane = threadIdx.x;
-  const int rows = a.verify_rows;                     // row stride of the partials
-  const int bh = blockIdx.x / grid_rows;              // grid_rows <= rows: rows some segment has
+  const int bh = blockIdx.x / grid_rows;              // grid_rows: rows the longest verify segment has
   const int i = blockIdx.x - bh * grid_rows;
   const int b = bh / a.num_q_heads;
   const int hq = bh - b * a.num_q_heads;
   const SegInfo si = seg_info(a, b);
   if (!si.ok || !verify_segment(si.n, G, D) || a.verify_acc == nullptr || i >= si.n) return;
   if (vnum_parts(si.L) <= 1) return;
+  const int64_t vrow0 = units_before(b, [&](int bb) { return verify_partial_rows<D>(a, bb, G); });
+  if (vrow0 + si.n > a.verify_rows) return;
   constexpr int DPL = D / kWave;
   const int pos = si.L - si.n + i;
   const int np = min(pos / kVPT + 1, a.part_max);
-  const int64_t base = ((static_cast<int64_t>(b) * rows + i) * a.num_q_heads + hq) * a.part_max;
+  const int64_t base = ((vrow0 + i) * a.num_q_heads + hq) * a.part_max;
   const float *ml = a.verify_ml + base * 2;
   float mx = -FLT_MAX;
   for (int p = lane; p < np; p += kWave) mx = fmaxf(mx, ml[2 * p]);
@@ -421,7 +433,7 @@ int launch_verify(const AttendArgs &a, int32_t head_dim, int32_t max_context_len
   if (!need_merge || a.verify_acc == nullptr || a.part_max <= 1) return PKV_OK;
   // One workgroup per (segment, head, row) up to the most rows a verify
   // segment of this launch has (from the host's pair count when known).
-  int grid_rows = a.verify_rows;
+  int grid_rows = verify_rows_cap(G, head_dim);
   if (max_pairs > 0 && (max_pairs + G - 1) / G < grid_rows) grid_rows = (max_pairs + G - 1) / G;
   const int64_t mgrid = static_cast<int64_t>(a.num_segments) * a.num_q_heads * grid_rows;
   if (mgrid <= 0) return PKV_OK;

@@ -83,6 +83,7 @@ class _Staging:
 class PagedKVEngine:
     STAGING_RING = 16
     STEP_GROUP = 4          # one-call steps per completion event (<= STAGING_RING / 2)
+    use_aux_stream = True   # lend pkv_mixed_step a second stream (decode beside chunks)
 
     def __init__(self, *, num_blocks, num_kv_heads, num_q_heads, head_dim, dtype, max_slots,
                  max_blocks_per_seq, free_order=None, device="cuda", poison=True):
@@ -105,6 +106,7 @@ class PagedKVEngine:
         self._workspace = None
         self._ws_key = None
         self._ws_bytes = 0
+        self._aux = None        # second stream and fork/join events lent to pkv_mixed_step
 
     # -- slot lifecycle (host allocator) --------------------------------
     def acquire(self, slot):
@@ -150,14 +152,32 @@ class PagedKVEngine:
         self._group_n = 0
 
     def _refresh_tables(self):
-        """Rebuild the host mirror of every table and send it to the device."""
-        self.h_block_tables.fill(0)
+        """Rebuild the host mirror of every table and send it to the device.
+        The mirror is a new array each time: earlier steps' snapshots keep the
+        tables they were lowered with."""
+        tables = np.zeros_like(self.h_block_tables)
         for slot in range(self.max_slots):
             t = self.alloc.slot_table(slot)
             if t:
-                self.h_block_tables[slot, :len(t)] = t
-        self.d_block_tables.copy_(self.torch.from_numpy(self.h_block_tables))
+                tables[slot, :len(t)] = t
+        self.h_block_tables = tables
+        self.d_block_tables.copy_(self.torch.from_numpy(tables))
         self._tables_dirty = False
+
+    def _aux_handles(self):
+        """Handles of the second stream (default priority) and the two events
+        that pkv_mixed_step uses to run a step's decode and draft kernels
+        beside its chunk kernels.  Created once per engine; recording each
+        event once makes torch create it."""
+        if self._aux is None:
+            torch = self.torch
+            s = torch.cuda.Stream(device=self.device)
+            fork, join = torch.cuda.Event(), torch.cuda.Event()
+            fork.record(s)
+            join.record(s)
+            self._aux = (s, fork, join)
+        s, fork, join = self._aux
+        return s.cuda_stream, fork.cuda_event, join.cuda_event
 
     def _lower_host(self, entries):
         """Lower the step into the next pinned staging buffer (host only)."""
@@ -217,12 +237,13 @@ class PagedKVEngine:
                               dtype=out_dtype or torch.float32, device=self.device)
         ws = self.workspace_for(meta)
         nseg = len(entries)
+        aux = self._aux_handles() if self.use_aux_stream else (None, None, None)
         desc = B.StepDesc(st.host.data_ptr(), st.dev.data_ptr(), offs[-1], offs[0], offs[1], offs[2], offs[3], offs[4],
                           meta.total_q, nseg, self.max_slots, meta.total_q, self.num_q_heads, self.max_blocks_per_seq,
                           meta.max_query_len, meta.max_context_len, k_new.data_ptr(), v_new.data_ptr(),
                           q.data_ptr(), self.d_block_tables.data_ptr(), float(scale), out.data_ptr(),
                           B.pkv_dtype_of(out.dtype), ws.data_ptr() if ws is not None else None,
-                          ws.numel() if ws is not None else 0, meta.copy_off, meta.num_copies)
+                          ws.numel() if ws is not None else 0, meta.copy_off, meta.num_copies, *aux)
         # the tensors are held so their memory outlives every replay
         return PreparedStep(desc=desc, staging=st, stream=stream, meta=meta, out=out,
                             keep=(k_new, v_new, q, ws))

@@ -185,27 +185,72 @@ def test_rising_scores_move_the_running_max(d, hq, hkv, seed, gpu_available):
 
 
 def test_single_token_context_is_v0(gpu_available):
-    """One visible key: the output is that key's V.  The kernel forms the
-    softmax weight as exp2(fma(s, c, -round(s c))), i.e. 1 + (rounding residue
-    of s c), so the result is V0 within one fp32 ulp rather than bit-exact."""
+    """One visible key: the output is that key's V, bit for bit (one weight,
+    normalised by the same bf16-rounded weight the product consumed)."""
     w = make_custom([(0, 0, 1)], dtype="bf16", hq=8, hkv=2, d=128, seed=5)
     _, outs = _run_gpu(w)
     out = outs[0][0].cpu().numpy()
     v = w.steps[0].v_new.astype(np.uint32) << 16
     v = v.view(np.float32)
     for h in range(8):
-        np.testing.assert_allclose(out[0, h], v[0, h // 4], rtol=2.0 ** -22, atol=0)
+        assert np.array_equal(out[0, h], v[0, h // 4])
 
 
-def test_bf16_output(gpu_available):
+@pytest.mark.parametrize("name", ["3", "3v", "2", "4a", "4b", "5", "3q", "5q"])
+def test_bf16_output(name, gpu_available):
+    """bf16 output on every store path - decode rows (direct and through the
+    partition reduce), chunks (direct and through the key-range merge), short
+    drafts (verify direct and merge), 8-bit pools - is the fp32 result
+    rounded to nearest even, bit for bit, and within 1e-2 + half a bf16 ulp
+    of the oracle (the bound for a bf16-rounded result)."""
     import torch
-    w = _workload("3")
-    _, outs = _run_gpu(w, out_dtype=torch.bfloat16)
-    res, _ = _oracle("3")
-    got = outs[0][0].float().cpu().numpy()
-    want = res[0]["out"]
-    half_ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 9)
-    assert (np.abs(got - want) <= 1e-2 + half_ulp).all()
+    _log(f"bf16 output config {name}")
+    w = _workload(name)
+    _, o32 = _run_gpu(w)
+    _, o16 = _run_gpu(w, out_dtype=torch.bfloat16)
+    res, _ = _oracle(name)
+    for i, ((a, _), (b, _), r) in enumerate(zip(o32, o16, res)):
+        assert b.dtype == torch.bfloat16
+        assert torch.equal(b.cpu(), a.cpu().to(torch.bfloat16)), f"step {i}"
+        got = b.float().cpu().numpy().astype(np.float64)
+        want = r["out"]
+        half_ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 9)
+        err = np.abs(got - want)
+        _log(f"config {name} step {i} bf16: max-abs {err.max():.3e}")
+        assert (err <= 1e-2 + half_ulp).all(), f"step {i}: max-abs {err.max()}"
+
+
+def _scale_qk(w, factor):
+    """Multiply every Q and K value of a one-step workload by a power of two
+    (exact in bf16): scores grow by factor^2."""
+    from workloads.configs import bf16_bits_from_f32
+
+    def mul(a):
+        x = (a.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+        return bf16_bits_from_f32(x)
+    w.history = [(slot, mul(kh), vh) for slot, kh, vh in w.history]
+    st = w.steps[0]
+    st.k_new, st.q = mul(st.k_new), mul(st.q)
+    return w
+
+
+LARGE_LOGIT_SEQS = [(0, 3000, 1), (1, 700, 1), (2, 1200, 4), (3, 900, 16), (4, 1024, 512), (5, 40, 100)]
+
+
+@pytest.mark.parametrize("kind", ["bf16", "q8"])
+@pytest.mark.parametrize("d,hq,hkv", [(128, 32, 8), (64, 32, 8), (128, 40, 8)])
+def test_large_logits(kind, d, hq, hkv, gpu_available):
+    """Q and K drawn N(0, 4^2): scores 16x larger than N(0,1) data, a sharply
+    peaked softmax where any rounding of q or of the scaled score shows up.
+    Decode rows, short drafts (verify kernel), 16-row drafts and chunks
+    (chunk kernel, split and unsplit) stay within the 1e-2 bound."""
+    _log(f"large logits {kind} D{d} {hq}/{hkv}")
+    w = _scale_qk(make_custom(LARGE_LOGIT_SEQS, dtype="bf16", hq=hq, hkv=hkv, d=d, seed=400 + d + hq), 4.0)
+    if kind == "q8":
+        w.kv_quant = "q8"
+    _, outs = _run_gpu(w)
+    res, _ = run_workload(w)
+    _check_close(f"large logits {kind}", outs[0][0], res[0]["out"], TOL["bf16"])
 
 
 # ------------------------------------------------------------------ invariants

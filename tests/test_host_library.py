@@ -99,6 +99,53 @@ def test_workspace_sizing():
     assert n == ((acc + 255) // 256) * 256 + 64 * 32 * 4 * 2 * 4
 
 
+def test_workspace_sizing_mixed_step_follows_rows_not_segments():
+    """Config 2's bounds (9 segments, 520 packed rows, 32/8 heads, head_dim
+    128, a 512-row chunk, contexts up to 4000): decode partials per segment
+    and partition; chunk key-range partials per (M-row, range) of the packed
+    rows, at most ceil(ceil(4000 / 64) / 16) = 4 ranges each; verify partials
+    for at most 9 segments x 8 rows (32 pairs / G 4) of the packed rows."""
+    d = pk.binding.PoolDesc(16, 16, 10, 16, 8, 128, 1)
+    lib = pk.lib()
+    n = lib.pkv_paged_attend_workspace_bytes(9, 520, 32, 512, 4000, ctypes.byref(d))
+    parts = -(-4000 // pk.decode_partition_tokens())
+    decode = 9 * 32 * parts * 128 * 4 + 9 * 32 * parts * 2 * 4
+    chunk_slots = min(9 * 32 * 128, 520 * 4 * 4)
+    chunk = 8 * chunk_slots * (128 + 4) * 4
+    vrows = min(520, 9 * 8)
+    verify = vrows * 32 * parts * 128 * 4 + vrows * 32 * parts * 2 * 4
+    assert n == decode + chunk + verify          # every part is a multiple of 256 here
+    # a decode-only step of the same size needs no chunk or verify partials
+    assert lib.pkv_paged_attend_workspace_bytes(9, 9, 32, 1, 4000, ctypes.byref(d)) == decode
+
+
+def test_mixed_step_rejects_understated_bounds_and_half_a_stream_pair():
+    """pkv_mixed_step checks the host copy of the metadata against the host
+    bounds, and a lent second stream without its events, before any launch."""
+    lib = pk.lib()
+    d4 = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, 1)
+    # one 5-row segment for slot 0 with 40 tokens: query_start | query_len |
+    # row_to_slot | context_lens
+    meta = (ctypes.c_int32 * 8)(0, 5, 0, 40)
+
+    def step(max_q, max_ctx):
+        st = pk.binding.StepDesc()
+        st.host_meta = ctypes.cast(meta, ctypes.c_void_p)
+        st.dev_meta = 16
+        st.meta_len = 8
+        st.query_start_off, st.query_len_off, st.row_to_slot_off, st.context_lens_off = 0, 1, 2, 3
+        st.num_segments, st.num_slots, st.total_q, st.num_q_heads = 1, 1, 5, 4
+        st.max_blocks_per_seq, st.max_query_len, st.max_context_len = 4, max_q, max_ctx
+        st.scale = 0.125
+        return st
+    for max_q, max_ctx in ((4, 40), (5, 39), (1, 1)):
+        st = step(max_q, max_ctx)
+        assert lib.pkv_mixed_step(ctypes.byref(st), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
+    st = step(5, 40)
+    st.aux_stream = 16                    # a stream without its fork / join events
+    assert lib.pkv_mixed_step(ctypes.byref(st), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
+
+
 def _random_ops(seed, n_ops=300, adopt=False):
     rng = np.random.default_rng(seed)
     nb, bs, slots, maxb = 64, 16, 8, 12

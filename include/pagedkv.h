@@ -27,8 +27,10 @@
  *     device pointers; "host" pointers are ordinary process memory.
  *   - The caller owns every buffer (pool, inputs, outputs, workspace), and
  *     every stream and event the library uses.  The library never allocates
- *     or frees device memory and creates no streams or events; it keeps no
- *     mutable global state.
+ *     or frees device memory and creates no streams or events.  Its only
+ *     global state is the scratch of pkv_paged_attend_noalloc (a device array
+ *     in the library's code object, one per GPU, and its device address,
+ *     looked up once per GPU).
  *   - Device calls are asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL = the null stream).  Argument errors are returned before
  *     anything is launched; launch failures return PKV_ERR_HIP; faults show
@@ -199,6 +201,29 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
                      const pkv_pool *pool, float scale,
                      void *out, int32_t out_dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* pkv_paged_attend without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The partials that pkv_paged_attend keeps
+ * in the caller's workspace (split-context, key-range and draft partitions)
+ * go instead to a scratch array inside the library: PKV_NOALLOC_SCRATCH_BYTES
+ * of device memory on every GPU the library is loaded on, held until the
+ * process ends.  A step whose pkv_paged_attend_workspace_bytes exceeds that
+ * returns PKV_ERR_WORKSPACE before anything is launched.  The call allocates
+ * nothing (no hipMalloc or hipFree).  Every call on one GPU shares that GPU's
+ * scratch, and its contents on entry are ignored: calls that overlap on one
+ * GPU (several streams or host threads) race, and the caller must order
+ * them.  Other arguments, results and status codes as for pkv_paged_attend;
+ * the results are bit-identical to pkv_paged_attend's. */
+#define PKV_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int pkv_paged_attend_noalloc(const void *q_packed, int32_t total_q, int32_t num_q_heads,
+                             const int32_t *row_to_slot, const int32_t *query_start,
+                             const int32_t *query_len, int32_t num_segments,
+                             const int32_t *context_lens, const int32_t *block_tables,
+                             int32_t num_slots, int32_t max_blocks_per_seq,
+                             int32_t max_query_len, int32_t max_context_len,
+                             const pkv_pool *pool, float scale,
+                             void *out, int32_t out_dtype, void *stream);
 
 /* One step's device half in two kernel launches (lucebox blog §Chunked prefill
  * is a slot phase: the chunk appends to the slot's paged KV, then every packed

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     kv_append,
     lib,
     paged_attend,
+    paged_attend_noalloc,
     pool_blocks_for_tokens,
     validate_step,
     workspace_bytes,

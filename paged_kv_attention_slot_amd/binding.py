@@ -70,6 +70,8 @@ _SIGNATURES = {
     "pkv_kv_append": (_i32, [_p, _p, _p, _i32, ctypes.POINTER(PoolDesc), _p]),
     "pkv_paged_attend": (_i32, [_p, _i32, _i32, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
                                 ctypes.POINTER(PoolDesc), ctypes.c_float, _p, _i32, _p, ctypes.c_size_t, _p]),
+    "pkv_paged_attend_noalloc": (_i32, [_p, _i32, _i32, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
+                                        ctypes.POINTER(PoolDesc), ctypes.c_float, _p, _i32, _p]),
     "pkv_paged_attend_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc)]),
     "pkv_decode_partition_tokens": (_i32, []),
     "pkv_mixed_step": (_i32, [ctypes.POINTER(StepDesc), ctypes.POINTER(PoolDesc), _p]),
@@ -254,6 +256,26 @@ def paged_attend(q_packed, row_to_slot, query_start, query_len, context_lens, bl
                                 _dptr(out), pkv_dtype_of(out.dtype), ws_ptr, ws_bytes,
                                 stream if stream is not None else current_stream_handle())
     _check(st, "pkv_paged_attend")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20     # PKV_NOALLOC_SCRATCH_BYTES in include/pagedkv.h
+
+
+def paged_attend_noalloc(q_packed, row_to_slot, query_start, query_len, context_lens, block_tables, pool: KVPool,
+                         scale, *, max_query_len, max_context_len, out, stream=None):
+    """paged_attend with the library's own scratch instead of a workspace
+    (pkv_paged_attend_noalloc: allocates nothing; calls overlapping on one
+    GPU race)."""
+    total_q, hq = int(q_packed.shape[0]), int(q_packed.shape[1])
+    nseg = int(row_to_slot.shape[0])
+    num_slots, maxb = int(block_tables.shape[0]), int(block_tables.shape[1])
+    st = lib().pkv_paged_attend_noalloc(_dptr(q_packed), total_q, hq, _dptr(row_to_slot), _dptr(query_start),
+                                        _dptr(query_len), nseg, _dptr(context_lens), _dptr(block_tables), num_slots,
+                                        maxb, int(max_query_len), int(max_context_len), pool._desc_ref,
+                                        float(scale), _dptr(out), pkv_dtype_of(out.dtype),
+                                        stream if stream is not None else current_stream_handle())
+    _check(st, "pkv_paged_attend_noalloc")
     return out
 
 

@@ -1,5 +1,6 @@
 // C-ABI entry points for the device side: argument checks, workspace sizing
 // and kernel dispatch on the caller's stream.
+#include <atomic>
 #include <cmath>
 
 #include "pagedkv.h"
@@ -115,6 +116,31 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
            size_t workspace_bytes, hipStream_t s, const StepFacts &facts, bool check_only = false,
            const AuxStream *aux = nullptr);
 
+// Scratch of pkv_paged_attend_noalloc: the partials that pkv_paged_attend
+// keeps in the caller's workspace, in a file-scope device array instead (one
+// copy on every GPU the library is loaded on, held until the process ends).
+// Host code never uses the array's name as an address: its device address is
+// looked up once per device with hipGetSymbolAddress (with that device
+// current) and kept in noalloc_scratch_ptr.
+constexpr size_t kNoallocScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> noalloc_scratch_ptr[kMaxScratchDevices];
+
+int noalloc_scratch_for_current_device(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return PKV_ERR_UNSUPPORTED;
+  void *p = noalloc_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // the same address on every lookup: a concurrent first call stores it too
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PKV_ERR_HIP;
+    noalloc_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -182,6 +208,36 @@ int pkv_paged_attend(const void *q_packed, int32_t total_q, int32_t num_q_heads,
   return attend(q_packed, total_q, num_q_heads, row_to_slot, query_start, query_len, num_segments, context_lens,
                 block_tables, num_slots, max_blocks_per_seq, max_query_len, max_context_len, pool, scale, out,
                 out_dtype, workspace, workspace_bytes, static_cast<hipStream_t>(stream), StepFacts{});
+}
+
+int pkv_paged_attend_noalloc(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int32_t *row_to_slot,
+                             const int32_t *query_start, const int32_t *query_len, int32_t num_segments,
+                             const int32_t *context_lens, const int32_t *block_tables, int32_t num_slots,
+                             int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_context_len,
+                             const pkv_pool *pool, float scale, void *out, int32_t out_dtype, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Argument errors first, then whether the step needs partials at all, then
+  // whether they fit the scratch (the placeholder address is only compared,
+  // never used), all before any HIP call.
+  int st = attend(q_packed, total_q, num_q_heads, row_to_slot, query_start, query_len, num_segments, context_lens,
+                  block_tables, num_slots, max_blocks_per_seq, max_query_len, max_context_len, pool, scale, out,
+                  out_dtype, nullptr, 0, s, StepFacts{}, true);
+  if (st == PKV_OK)      // no partials: nothing of the scratch is needed
+    return attend(q_packed, total_q, num_q_heads, row_to_slot, query_start, query_len, num_segments, context_lens,
+                  block_tables, num_slots, max_blocks_per_seq, max_query_len, max_context_len, pool, scale, out,
+                  out_dtype, nullptr, 0, s, StepFacts{});
+  if (st != PKV_ERR_WORKSPACE) return st;
+  void *const placeholder = reinterpret_cast<void *>(static_cast<uintptr_t>(256));
+  st = attend(q_packed, total_q, num_q_heads, row_to_slot, query_start, query_len, num_segments, context_lens,
+              block_tables, num_slots, max_blocks_per_seq, max_query_len, max_context_len, pool, scale, out,
+              out_dtype, placeholder, kNoallocScratchBytes, s, StepFacts{}, true);
+  if (st != PKV_OK) return st;   // PKV_ERR_WORKSPACE: the step's partials exceed the scratch
+  void *ws = nullptr;
+  st = noalloc_scratch_for_current_device(&ws);
+  if (st != PKV_OK) return st;
+  return attend(q_packed, total_q, num_q_heads, row_to_slot, query_start, query_len, num_segments, context_lens,
+                block_tables, num_slots, max_blocks_per_seq, max_query_len, max_context_len, pool, scale, out,
+                out_dtype, ws, kNoallocScratchBytes, s, StepFacts{});
 }
 
 int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {

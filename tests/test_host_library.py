@@ -355,3 +355,18 @@ def test_validator_accepts_good_and_names_each_rule():
         m[key] = val
         ok, bad = pk.validate_step(m, 4, 4, 16, 2)
         assert not ok and bad == bad_idx, (key, val, bad)
+
+
+def test_noalloc_rejects_steps_beyond_its_scratch_without_gpu():
+    """pkv_paged_attend_noalloc checks arguments, then whether the step's
+    partials fit its fixed scratch, before any HIP call: 1000 decode rows
+    over contexts up to 32768 need ~1 GiB of split-context partials."""
+    lib = pk.lib()
+    d = pk.binding.PoolDesc(16, 16, 10, 16, 8, 128, 1)
+    need = lib.pkv_paged_attend_workspace_bytes(1000, 1000, 32, 1, 32768, ctypes.byref(d))
+    assert need > pk.binding.NOALLOC_SCRATCH_BYTES
+    assert lib.pkv_paged_attend_noalloc(16, 1000, 32, 16, 16, 16, 1000, 16, 16, 1000, 2048, 1, 32768,
+                                        ctypes.byref(d), 0.088, 16, 0, None) == pk.binding.PKV_ERR_WORKSPACE
+    # argument errors come first (a bad scale), as for pkv_paged_attend
+    assert lib.pkv_paged_attend_noalloc(16, 1000, 32, 16, 16, 16, 1000, 16, 16, 1000, 2048, 1, 32768,
+                                        ctypes.byref(d), -1.0, 16, 0, None) == pk.binding.PKV_ERR_INVALID_ARG

@@ -24,9 +24,20 @@ Prints one JSON line:
                  fill, outside the events), each call bracketed by HIP events
                  on its stream; algorithmic bytes per call / mean duration vs
                  8 TB/s (attend_ms_warm_avg: the same calls back to back)
-  cpu_baseline = the CPU oracle on a bounded sample of the same step
+  cpu_baseline = the CPU oracle on a bounded sample of the same step (with
+                 the host's CPU model, core count and BLAS)
+  extras       = after the headline, on the same GPU: config 4a's prompt
+                 chunk alone (the chunk kernel's TFLOP/s against the bf16
+                 peak: a one-call step holding only the chunk, minus its
+                 append timed alone, both cold); the whole one-call step of
+                 configs 2, 4a, 4b, 5 and 5 step 2, cold, against its
+                 roofline time t_roof (the sum over its kernels of
+                 max(bytes / 8 TB/s, flops / 2.5 PF)); the append kernel's
+                 GB/s on three step sizes
+  cpu_baseline_configs = the oracle on configs 1, 2, 5, 4b and 4a (1-thread
+                 runs for 1 and 2)
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--step N] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--step N] [--no-cpu-baseline] [--no-extras]
     python bench.py --ablation gather|prefix     (one JSON line of ablation rows)
 """
 from __future__ import annotations
@@ -60,6 +71,8 @@ def parse_args():
     ap.add_argument("--step", type=int, default=0,
                     help="mixed-step configs: time this step of the workload (earlier steps run once first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the chunk-kernel, mixed-step and append lines after the headline")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--ablation", choices=["gather", "prefix"], default=None,
@@ -90,6 +103,147 @@ def chunk_flops(w, segments, lens):
             visible = sum(L - seg.n + i + 1 for i in range(seg.n))
             tot += 4 * w.head_dim * w.num_q_heads * visible
     return tot
+
+
+def multirow_bytes(w, segments, lens):
+    """Algorithmic bytes of the multi-row segments: K and V of every token
+    each segment sees, once, plus Q in and fp32 O out."""
+    row = w.head_dim + 4 if getattr(w, "kv_quant", "") == "q8" else w.head_dim * w.elem_bytes
+    tot = 0
+    for seg, L in zip(segments, lens):
+        if seg.n > 1:
+            tot += 2 * L * w.num_kv_heads * row + seg.n * w.num_q_heads * w.head_dim * (2 + 4)
+    return tot
+
+
+def append_bytes(w, num_tokens):
+    """Algorithmic bytes of kv_append: K and V rows read and written once,
+    plus the 4-byte slot index per token (8-bit pools write codes and a
+    4-byte scale per row)."""
+    hkv, d = w.num_kv_heads, w.head_dim
+    if getattr(w, "kv_quant", "") == "q8":
+        return num_tokens * (2 * hkv * d * 2 + 2 * hkv * (d + 4) + 4)
+    return num_tokens * (4 * hkv * d * w.elem_bytes + 4)
+
+
+def step_roofline(w, segments, lens):
+    """t_roof of one mixed step: the sum over its kernels of max(bytes / HBM
+    peak, flops / bf16 peak) - the append, the decode rows (HBM), the
+    multi-row segments (HBM or matrix, whichever binds).  Seconds."""
+    t_app = append_bytes(w, sum(s.n for s in segments)) / (HBM_PEAK_GBS * 1e9)
+    dec_lens = [L for s, L in zip(segments, lens) if s.n == 1]
+    _, dec_alg = decode_bytes(w, dec_lens, w.elem_bytes)
+    t_dec = dec_alg / (HBM_PEAK_GBS * 1e9)
+    mr_b = multirow_bytes(w, segments, lens)
+    mr_f = chunk_flops(w, segments, lens)
+    t_mr = max(mr_b / (HBM_PEAK_GBS * 1e9), mr_f / (BF16_PEAK_TFLOPS * 1e12))
+    return t_app + t_dec + t_mr, {"append_s": t_app, "decode_s": t_dec, "multirow_s": t_mr,
+                                  "multirow_bound": "mfma" if mr_f / (BF16_PEAK_TFLOPS * 1e12) >
+                                  mr_b / (HBM_PEAK_GBS * 1e9) else "hbm"}
+
+
+def _cold_times(torch, stream, fn, reps, flush):
+    """Durations of fn() (seconds), each bracketed by HIP events on `stream`
+    with the caches flushed before it (a fill of `flush`, outside the events)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        flush.fill_(i & 0xFF)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+
+
+def mixed_step_stats(w, step, pk, torch, dev, reps, flush):
+    """One workload step replayed through the one-call path: its GPU time
+    cold (median of `reps`) against its roofline time."""
+    from workloads.drive import apply_ops, make_engine, place_history, run_step, step_tensors
+    eng = make_engine(pk.PagedKVEngine, w, device=dev)
+    place_history(eng, w, device=dev)
+    for i in range(step):
+        run_step(eng, w, i, device=dev)
+    st = w.steps[step]
+    apply_ops(eng, st.ops)
+    k_new, v_new, q = step_tensors(w, step, device=dev)
+    prep = eng.prepare_fused([(s.slot, s.n) for s in st.segments], k_new, v_new, q, w.scale)
+    for _ in range(3):
+        eng.run_prepared(prep)
+    stream = torch.cuda.current_stream()
+    t = _cold_times(torch, stream, lambda: eng.run_prepared(prep), reps, flush)
+    lens = [int(prep.meta.host["context_lens"][s.slot]) for s in st.segments]
+    t_roof, parts = step_roofline(w, st.segments, lens)
+    med = t[len(t) // 2]
+    res = {"step_gpu_ms_cold": round(med * 1e3, 4), "t_roof_ms": round(t_roof * 1e3, 4),
+           "frac": round(t_roof / med, 4), "bound_of_multirow": parts["multirow_bound"],
+           "chunk_causal_gflop": round(chunk_flops(w, st.segments, lens) / 1e9, 2),
+           "kv_mb": round((decode_bytes(w, [L for s, L in zip(st.segments, lens) if s.n == 1], w.elem_bytes)[0]
+                           + multirow_bytes(w, st.segments, lens)) / 1e6, 1)}
+    del eng, prep
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunk_kernel_stats(w, pk, torch, dev, reps, flush):
+    """The chunk kernel on one config's multi-row segment alone: a one-call
+    step holding only that segment (append + chunk kernels), minus the same
+    append timed alone, both cold (medians).  Returns TFLOP/s over the
+    causal-visible flops."""
+    from workloads import Step, Workload  # noqa: F401  (types only)
+    from workloads.drive import make_engine, place_history, to_device
+    st = w.steps[0]
+    seg_i = next(i for i, s in enumerate(st.segments) if s.n > 1)
+    r0 = sum(s.n for s in st.segments[:seg_i])
+    seg = st.segments[seg_i]
+    eng = make_engine(pk.PagedKVEngine, w, device=dev)
+    place_history(eng, w, device=dev)
+    rows = slice(r0, r0 + seg.n)
+    k_new = to_device(st.k_new[rows], w.dtype, dev)
+    v_new = to_device(st.v_new[rows], w.dtype, dev)
+    q = to_device(st.q[rows], w.dtype, dev)
+    prep = eng.prepare_fused([(seg.slot, seg.n)], k_new, v_new, q, w.scale)
+    for _ in range(3):
+        eng.run_prepared(prep)
+    stream = torch.cuda.current_stream()
+    meta = prep.meta
+    t_step = _cold_times(torch, stream, lambda: eng.run_prepared(prep), reps, flush)
+    t_app = _cold_times(torch, stream, lambda: pk.kv_append(meta.slot_mapping, k_new, v_new, eng.pool), reps, flush)
+    L = int(meta.host["context_lens"][seg.slot])
+    fl = chunk_flops(w, [seg], [L])
+    t_chunk = t_step[len(t_step) // 2] - t_app[len(t_app) // 2]
+    del eng, prep
+    torch.cuda.empty_cache()
+    return {"kernel": "pkv chunk_kernel (+ its key-range merge when the segment is cut)",
+            "workload": f"config {w.name}'s {seg.n}-row chunk at offset {L - seg.n} (context {L}), alone",
+            "causal_gflop": round(fl / 1e9, 2), "ms": round(t_chunk * 1e3, 4),
+            "step_ms_cold": round(t_step[len(t_step) // 2] * 1e3, 4),
+            "append_ms_cold": round(t_app[len(t_app) // 2] * 1e3, 4),
+            "tflops": round(fl / t_chunk / 1e12, 1),
+            "frac_bf16_peak": round(fl / t_chunk / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
+def append_kernel_stats(w, step, pk, torch, dev, reps, flush):
+    """kv_append alone on one step's new tokens (idempotent: the same rows to
+    the same positions), cold median: algorithmic GB/s."""
+    from workloads.drive import apply_ops, make_engine, place_history, run_step, step_tensors
+    eng = make_engine(pk.PagedKVEngine, w, device=dev)
+    place_history(eng, w, device=dev)
+    for i in range(step):
+        run_step(eng, w, i, device=dev)
+    st = w.steps[step]
+    apply_ops(eng, st.ops)
+    k_new, v_new, _ = step_tensors(w, step, device=dev)
+    meta = eng.lower([(s.slot, s.n) for s in st.segments])
+    for _ in range(3):
+        pk.kv_append(meta.slot_mapping, k_new, v_new, eng.pool)
+    stream = torch.cuda.current_stream()
+    t = _cold_times(torch, stream, lambda: pk.kv_append(meta.slot_mapping, k_new, v_new, eng.pool), reps, flush)
+    med = t[len(t) // 2]
+    nb = append_bytes(w, meta.total_q)
+    del eng
+    torch.cuda.empty_cache()
+    return {"kernel": "pkv kv_append_kernel", "tokens": meta.total_q, "bytes": nb, "ms_cold": round(med * 1e3, 4),
+            "gbs": round(nb / med / 1e9, 1), "frac_hbm_peak": round(nb / med / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def run_mixed(args, w, pk, torch, dev):
@@ -138,13 +292,14 @@ def run_mixed(args, w, pk, torch, dev):
     att_cold = sorted(a_.elapsed_time(b_) for a_, b_ in cold_ev)[len(cold_ev) // 2] / 1e3
     lens = [int(meta.host["context_lens"][s.slot]) for s in st.segments]
     dec_lens = [L for s, L in zip(st.segments, lens) if s.n == 1]
-    kv, alg = decode_bytes(w, dec_lens, w.elem_bytes)
+    kv, _ = decode_bytes(w, dec_lens, w.elem_bytes)
     fl = chunk_flops(w, st.segments, lens)
     # K and V of every cached token of the multi-row segments, once
     row = w.head_dim + 4 if getattr(w, "kv_quant", "") == "q8" else w.head_dim * w.elem_bytes
     mr_kv = sum(2 * L * w.num_kv_heads * row for seg, L in zip(st.segments, lens) if seg.n > 1)
+    t_roof, parts = step_roofline(w, st.segments, lens)
     name = w.name if args.step == 0 else f"{w.name} step {args.step + 1}"
-    return {"metric": f"mixed-step latency, config {name}", "value": round(wall / args.steps * 1e3, 4),
+    line = {"metric": f"mixed-step latency, config {name}", "value": round(wall / args.steps * 1e3, 4),
             "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(wall / args.steps * 1e3, 4), "step_gpu_ms_avg": round(att * 1e3, 4),
             "step_gpu_ms_cold_p50": round(att_cold * 1e3, 4),
@@ -154,7 +309,43 @@ def run_mixed(args, w, pk, torch, dev):
             "decode_kv_bytes": kv, "chunk_causal_flops": fl, "multi_row_kv_bytes": mr_kv,
             "step_kv_gbs": round((kv + mr_kv) / att / 1e9, 1),
             "step_tflops_if_all_chunk": round(fl / att / 1e12, 2),
-            "roofline_step_ms": round((alg / HBM_PEAK_GBS / 1e9 + fl / BF16_PEAK_TFLOPS / 1e12) * 1e3, 4)}
+            # sum over the step's kernels of max(bytes / 8 TB/s, flops / 2.5 PF)
+            "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 4),
+                              "frac_cold": round(t_roof / att_cold, 4), "frac_warm": round(t_roof / att, 4),
+                              "parts_ms": {k: round(v * 1e3, 4) for k, v in parts.items() if k.endswith("_s")},
+                              "multirow_bound": parts["multirow_bound"]}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_step(w, args.step, 1 if fl > 50e9 else 3)
+    return line
+
+
+def cpu_baseline_step(w, step, repeats):
+    """The oracle on one whole step of a workload (numpy fp64), best of
+    `repeats`, setup excluded: step time and the same step's algorithmic rate."""
+    from oracle.block_pool import BlockPool
+    from oracle.step import append_kv, apply_ops, attend_step, copy_kv, place_history, poisoned_pool
+    alloc = BlockPool(w.num_blocks, w.block_size, w.max_slots, w.max_blocks_per_seq, w.free_order)
+    pk_, pv_ = place_history(w, alloc, poisoned_pool(w), poisoned_pool(w))
+    for i, st in enumerate(w.steps[:step + 1]):
+        apply_ops(alloc, st.ops)
+        meta = alloc.lower_step([(s.slot, s.n) for s in st.segments])
+        pk_, pv_ = copy_kv(w, pk_, pv_, meta["copy_src"], meta["copy_dst"])
+        pk_, pv_ = append_kv(w, pk_, pv_, meta["slot_mapping"], st.k_new, st.v_new)
+        if i < step:
+            continue
+        dt = float("inf")
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            attend_step(w, st, pk_, pv_, meta)
+            dt = min(dt, time.perf_counter() - t0)
+    st = w.steps[step]
+    lens = [int(meta["context_lens"][s.slot]) for s in st.segments]
+    kv = decode_bytes(w, [L for s, L in zip(st.segments, lens) if s.n == 1], w.elem_bytes)[0] + \
+        multirow_bytes(w, st.segments, lens)
+    host = _host_description()
+    return {"value": round(dt * 1e3, 2), "unit": "ms per step", "cores": host["blas_threads"] or host["os_cpu_count"],
+            "kind": "oracle", "sample": f"numpy fp64 oracle over the whole step, best of {repeats}",
+            "kv_gbs": round(kv / dt / 1e9, 4), **host}
 
 
 def _event_time(torch, stream, fn, reps):
@@ -340,6 +531,100 @@ def cpu_baseline(w, sample_rows, repeats):
                       f"({sum(lens)} cached tokens), best of {repeats}: {dt:.2f} s"}
 
 
+def _host_description():
+    """CPU model, logical CPU count and the BLAS numpy uses (with its threads)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')}"
+                threads = i.get("num_threads")
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas": blas, "blas_threads": threads}
+
+
+def cpu_baseline_configs():
+    """The oracle (numpy fp64: block-table walk + attention) on the mixed-step
+    configs, timed over attention only (setup excluded): best of 3 for the
+    small configs 1, 2 and 5, one run for 4a and 4b; configs 1 and 2 also
+    with BLAS held to one thread.  Effective rates use the same algorithmic
+    bytes and flops as the GPU lines."""
+    from threadpoolctl import threadpool_limits
+    from oracle.block_pool import BlockPool
+    from oracle.step import append_kv, attend_step, place_history, poisoned_pool
+    from workloads import make_workload
+    rows = {}
+
+    def prepared(name):
+        w = make_workload(name)
+        alloc = BlockPool(w.num_blocks, w.block_size, w.max_slots, w.max_blocks_per_seq, w.free_order)
+        pk_, pv_ = place_history(w, alloc, poisoned_pool(w), poisoned_pool(w))
+        st = w.steps[0]
+        meta = alloc.lower_step([(s.slot, s.n) for s in st.segments])
+        pk_, pv_ = append_kv(w, pk_, pv_, meta["slot_mapping"], st.k_new, st.v_new)
+        return w, st, pk_, pv_, meta
+
+    for name, repeats, one_thread in (("1", 3, True), ("2", 3, True), ("5", 3, False), ("4b", 1, False),
+                                      ("4a", 1, False)):
+        w, st, pk_, pv_, meta = prepared(name)
+        lens = [int(meta["context_lens"][s.slot]) for s in st.segments]
+        kv = decode_bytes(w, [L for s, L in zip(st.segments, lens) if s.n == 1], w.elem_bytes)[0] + \
+            multirow_bytes(w, st.segments, lens)
+        fl = chunk_flops(w, st.segments, lens)
+
+        def best(n):
+            dt = float("inf")
+            for _ in range(n):
+                t0 = time.perf_counter()
+                attend_step(w, st, pk_, pv_, meta)
+                dt = min(dt, time.perf_counter() - t0)
+            return dt
+        dt = best(repeats)
+        row = {"seconds": round(dt, 4), "repeats": repeats, "kv_gbs": round(kv / dt / 1e9, 4),
+               "gflops_causal": round(fl / dt / 1e9, 2) if fl else None}
+        if one_thread:
+            with threadpool_limits(limits=1):
+                dt1 = best(repeats)
+            row["seconds_1_thread"] = round(dt1, 4)
+        rows[f"config {name}"] = row
+    return {"kind": "oracle", **_host_description(), "per_config": rows}
+
+
+def run_extras(pk, torch, dev, args):
+    """The second target and the mixed steps, on the same run as the
+    headline: config 4a's chunk kernel alone (TFLOP/s against bf16 peak),
+    each chunk-bearing config's whole one-call step against its roofline,
+    and the append kernel's rate."""
+    from workloads import make_workload
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    reps = 10
+    out = {"chunk_kernel": chunk_kernel_stats(make_workload("4a"), pk, torch, dev, reps, flush)}
+    steps = {}
+    for name, step in (("2", 0), ("4a", 0), ("4b", 0), ("5", 0), ("5", 1)):
+        label = f"config {name}" + (f" step {step + 1}" if step else "")
+        steps[label] = mixed_step_stats(make_workload(name), step, pk, torch, dev, reps, flush)
+    out["mixed_steps"] = steps
+    out["append_kernel"] = {
+        "config 5 step 2": append_kernel_stats(make_workload("5"), 1, pk, torch, dev, reps, flush),
+        "config 4a": append_kernel_stats(make_workload("4a"), 0, pk, torch, dev, reps, flush),
+        "config 3": append_kernel_stats(make_workload("3"), 0, pk, torch, dev, reps, flush)}
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -476,8 +761,13 @@ def main():
                      "kernel": ("pkv decode_q8_kernel" if q8 else "pkv decode_mfma_kernel")
                      + " + reduce_kernel (one paged_attend launch)"},
     }
+    if not args.no_extras:
+        line["extras"] = run_extras(pk, torch, dev, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows, args.cpu_repeats)
+        line["cpu_baseline"].update(_host_description())
+        if not args.no_extras:
+            line["cpu_baseline_configs"] = cpu_baseline_configs()
     print(json.dumps(line), flush=True)
 
 

@@ -204,10 +204,10 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   const int wave_pos0 = mw < mtot ? L - n + mw / G : -1;
 
   // Q operand (B of S^T = K Q^T): lane holds dims 16 ks + 8 hh .. + 7 of
-  // its M-row, the query's own bf16 values (the scale is applied in fp32 to
-  // each score, so Q carries no rounding beyond its input's).
+  // its M-row, the query's own bf16 values: the score accumulators hold the
+  // raw q . k, and the scale is applied in fp32 to each score.
   const float c_log2 = a.scale_log2;
-  const float slack_raw = PKV_CHUNK_RESCALE_SLACK / c_log2;   // the slack in raw score units
+  const float slack_raw = PKV_CHUNK_RESCALE_SLACK / c_log2;    // the slack in raw score units
   const int m = mw + l32;
   const bool valid = m < mtot;
   const int qi = valid ? m / G : 0;
@@ -226,16 +226,14 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     }
   }
 
-  // Online softmax state of the lane's M-row, in raw score units (q . k):
-  // running max m_run, and the reference r_ref that the score accumulators
-  // start from (-r_ref), so that a tile's accumulators hold q . k - r_ref and
-  // its weights are exp2(scale log2(e) x accumulator).  r_ref follows m_run
-  // once the row has seen an unmasked key (0 before).  lsum: this half's row
-  // sum.
-  float m_run = -FLT_MAX, r_ref = 0.f, lsum = 0.f;
-  floatx16_t negr;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) negr[i] = 0.f;
+  // Online softmax state of the lane's M-row: running max m_run (raw q . k
+  // units) and the reference the weights are taken against, ref = m_run x
+  // scale log2(e) as one fp32 value (0 before the row has seen a key): a
+  // score s weighs exp2(fma(s, scale log2(e), -ref)).  The score
+  // accumulators start from zero (the MFMA's inline constant).  lsum: this
+  // half's row sum.
+  float m_run = -FLT_MAX, ref = 0.f, lsum = 0.f;
+  const floatx16_t zero16 = {};
   floatx16_t o[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -335,10 +333,10 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     const unsigned char *kl = lds + st * 2 * kStageBytes;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      sc[tt] = negr;
 #pragma unroll
       for (int ks = 0; ks < kQS; ++ks)
-        sc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kl, tt, ks), qv[ks], sc[tt], 0, 0, 0);
+        sc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kl, tt, ks), qv[ks], ks == 0 ? zero16 : sc[tt],
+                                                         0, 0, 0);
     }
   };
   // Causal mask of tile rt; only tiles reaching past the wave's first row.
@@ -351,12 +349,12 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
           if (rt * T + tt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) > pos) sc[tt][i] = -INFINITY;
     }
   };
-  // Row max of a tile (raw units) over both halves: the candidate new
+  // Row max of a tile (accumulator units) over both halves: the candidate new
   // running max, and whether it exceeds the current one by more than the
   // allowed slack (the rescale vote).
   auto finish_max = [&](float part, float &mnew) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-    const float mx = r_ref + vmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const float mx = vmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     mnew = vmaxf(m_run, mx);
     return mx > m_run + slack_raw;
   };
@@ -366,22 +364,17 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     for (int w = 2; w < 16 * kTT; w += 2) acc = vmaxf(vmaxf(acc, sc[w / 16][w % 16]), sc[w / 16][w % 16 + 1]);
     return finish_max(acc, mnew);
   };
-  // Move O and l to the new running max when any row of the wave asked, and
-  // re-base the pending tile's accumulators `cur` to the new reference.
-  auto rescale = [&](float mnew, bool raise, floatx16_t(&cur)[kTT]) {
+  // Move O and l to the new reference when any row of the wave asked (a row
+  // that has seen no key yet holds O = l = 0: factor 0).
+  auto rescale = [&](float mnew, bool raise) {
     if (__ballot(raise) != 0) {
-      const float alpha = fast_exp2((m_run - mnew) * c_log2);
+      const float nref = mnew > -FLT_MAX ? mnew * c_log2 : ref;
+      const float alpha = m_run > -FLT_MAX ? fast_exp2(ref - nref) : 0.f;
       m_run = mnew;
+      ref = nref;
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) o[dt] *= alpha;
-      const float nr = mnew > -FLT_MAX ? mnew : r_ref;
-      const float d = nr - r_ref;
-      r_ref = nr;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) negr[i] = -nr;
-#pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) cur[tt] -= d;
     }
   };
   // V^T operand of PV step ps, dimension tile dt: lane (16-lane group
@@ -414,8 +407,6 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     constexpr int kSteps = kPairs + kLead;
     constexpr int kScores = 16 * kTT;
     bf16x8_t ka[kPairs];
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) nxt[tt] = negr;
     float p[kScores];
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
@@ -423,11 +414,12 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       if (i < kPairs) ka[i] = k_operand(kl, i / kQS, i % kQS);
       if (i >= kLead) {
         const int j = i - kLead;
-        nxt[j / kQS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qv[j % kQS], nxt[j / kQS], 0, 0, 0);
+        nxt[j / kQS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qv[j % kQS],
+                                                               j % kQS == 0 ? zero16 : nxt[j / kQS], 0, 0, 0);
       }
 #pragma unroll
       for (int w = i * kScores / kSteps; w < (i + 1) * kScores / kSteps; ++w) {
-        p[w] = fast_exp2(cur[w / 16][w % 16] * c_log2);
+        p[w] = fast_exp2(fmaf(cur[w / 16][w % 16], c_log2, -ref));
         if (w % 8 == 7) {
           const float *q8 = p + (w - 7);
           pb[w / 8] = bf16x8_t{static_cast<__bf16>(q8[0]), static_cast<__bf16>(q8[1]), static_cast<__bf16>(q8[2]),
@@ -493,7 +485,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 3)) : "memory");
       __syncthreads();
       issue_ph(static_cast<int>(static_cast<unsigned>(rt - pass0 + S - 1) % S), min(rt + S - 1, pass1 - 1), ph_next);
-      rescale(mnew, raise, cur);
+      rescale(mnew, raise);
       bf16x8_t pb[kPS];
       bf16x8_t va[kDT][kPS];
       // Phase A: the weights of tile rt while the matrix cores form the
@@ -547,7 +539,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
         *reinterpret_cast<float4 *>(pa + dt * 32 + 8 * r + 4 * hh) =
             make_float4(o[dt][4 * r], o[dt][4 * r + 1], o[dt][4 * r + 2], o[dt][4 * r + 3]);
     // the merge takes the reference in log2 units
-    if (hh == 0) *reinterpret_cast<float2 *>(pa + D) = make_float2(m_run * c_log2, lt);
+    if (hh == 0) *reinterpret_cast<float2 *>(pa + D) = make_float2(ref, lt);
     return;
   }
   const float inv = 1.f / lt;

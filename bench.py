@@ -14,8 +14,9 @@ Each timed step is a real decode step: every sequence grows by one token.
 Prints one JSON line:
   value        = decode KV bytes read per step x steps / wall time  (GB/s)
   ms_per_step  = wall time / steps (host lowering included)
-  step_gpu_ms  = each timed step's GPU work (append + attention) between HIP
-                 events on the stream, p10 / p50 / p90
+  step_gpu_ms  = each step's GPU work (append + attention) between HIP events
+                 on the stream, p10 / p50 / p90, in as many steps run after
+                 the timed ones (the timed steps record no events)
   host_ms_per_step = host time inside the step calls (lowering, the library
                  call, staging-ring waits)
   roofline     = the attention launch (decode kernel + partition reduce),
@@ -657,7 +658,8 @@ def main():
     if any(s.n != 1 for s in st.segments) or args.step:
         print(json.dumps(run_mixed(args, w, pk, torch, dev)), flush=True)
         return
-    total_steps = args.warmup + args.steps
+    # warmup, the timed steps, then as many again with per-step events
+    total_steps = args.warmup + 2 * args.steps
     w.max_blocks_per_seq += -(-total_steps // 16) + 1
     eng = make_engine(pk.PagedKVEngine, w, device=dev)
     place_history(eng, w, device=dev)
@@ -678,21 +680,26 @@ def main():
         one_step()
     torch.cuda.synchronize()
     metas = []
-    # each timed step's GPU work (append + attention) bracketed by HIP events
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
     gc.collect()
     gc.disable()            # no collector pauses inside the timed region
     host = 0.0
     t0 = time.perf_counter()
     for i in range(args.steps):
         h0 = time.perf_counter()
-        step_ev[i][0].record(stream)
         metas.append(one_step())
-        step_ev[i][1].record(stream)
         host += time.perf_counter() - h0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Each step's GPU work (append + attention) bracketed by HIP events, in
+    # as many further steps after the timed ones: an event record costs the
+    # stream several microseconds, so the timed steps carry none.
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_ev[i][0].record(stream)
+        one_step()
+        step_ev[i][1].record(stream)
+    torch.cuda.synchronize()
     gc.enable()
     step_gpu = sorted(a_.elapsed_time(b_) for a_, b_ in step_ev)
     for meta in metas:

@@ -82,7 +82,7 @@ class _Staging:
 
 class PagedKVEngine:
     STAGING_RING = 16
-    STEP_GROUP = 4          # one-call steps per completion event (<= STAGING_RING / 2)
+    STEP_GROUP = 8          # one-call steps per completion event (<= STAGING_RING / 2)
     use_aux_stream = True   # lend pkv_mixed_step a second stream (decode beside chunks)
 
     def __init__(self, *, num_blocks, num_kv_heads, num_q_heads, head_dim, dtype, max_slots,

@@ -463,7 +463,10 @@ int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t 
     st = head_dim == 128 ? dispatch_g<float, 128>(a, G, items_bound, stream)
                          : dispatch_g<float, 64>(a, G, items_bound, stream);
   }
-  if (st != PKV_OK || a.part_max <= 1 || !need_reduce) return st;
+  // (a whole-context ablation build writes every bf16 decode row directly)
+  if (st != PKV_OK || a.part_max <= 1 || !need_reduce ||
+      (PKV_DECODE_WHOLE_CONTEXT && dtype == PKV_BF16 && !a.multirow && PKV_DECODE_MFMA))
+    return st;
   const unsigned grid = static_cast<unsigned>(a.num_segments) * static_cast<unsigned>(a.num_q_heads);
   const size_t lds = static_cast<size_t>(a.part_max) * sizeof(float);
   if (head_dim == 128)

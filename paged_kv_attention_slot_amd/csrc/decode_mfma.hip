@@ -59,13 +59,21 @@ struct MGeo {
   }
 };
 
+// Ablation builds only (both 0 in the library): kNoShare gives every query
+// head its own wavefront, which reads the group's K/V tiles again (GQA
+// sharing off); kWholeContext walks each row's whole context in one
+// wavefront (split-context partitions off; the block table is then read in
+// slices of 64 entries).
+constexpr bool kNoShare = PKV_DECODE_NO_GQA_SHARE;
+constexpr bool kWholeContext = PKV_DECODE_WHOLE_CONTEXT;
+
 __device__ __forceinline__ int num_parts_m(int L) {
-  return (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
+  return kWholeContext ? 1 : (L + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
 }
 
-__device__ __forceinline__ int decode_units(const AttendArgs &a, int b) {
+__device__ __forceinline__ int decode_units(const AttendArgs &a, int b, int G) {
   const SegInfo s = seg_info(a, b);
-  return s.ok && s.n == 1 ? num_parts_m(s.L) : 0;
+  return s.ok && s.n == 1 ? num_parts_m(s.L) * (kNoShare ? G : 1) : 0;
 }
 
 template <int D, int S>
@@ -83,10 +91,10 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
   const int lg = lane >> 4;
 
   const SegInfo mine = seg_info(a, lane);
-  const int u0 = mine.ok && mine.n == 1 ? num_parts_m(mine.L) : 0;
+  const int u0 = mine.ok && mine.n == 1 ? num_parts_m(mine.L) * (kNoShare ? G : 1) : 0;
   const int incl0 = wave_inclusive_scan(u0);
   int total = __shfl(incl0, kWave - 1);
-  if (a.num_segments > kWave) total = count_units(a.num_segments, [&](int b) { return decode_units(a, b); });
+  if (a.num_segments > kWave) total = count_units(a.num_segments, [&](int b) { return decode_units(a, b, G); });
   const int64_t items = static_cast<int64_t>(total) * a.num_kv_heads;
   const float c_log2 = a.scale_log2;
 
@@ -105,25 +113,35 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
       si.row0 = __builtin_amdgcn_readlane(mine.row0, b);
       si.ok = true;
     } else {
-      b = find_unit(a.num_segments, unit, [&](int bb) { return decode_units(a, bb); }, &part);
+      b = find_unit(a.num_segments, unit, [&](int bb) { return decode_units(a, bb, G); }, &part);
       si = seg_info(a, b);
       if (!si.ok) continue;
     }
+    int hsel = 0;                            // kNoShare: this wavefront's query head of the group
+    if constexpr (kNoShare) {
+      hsel = part % G;
+      part /= G;
+    }
     const int np = num_parts_m(si.L);
     const int row = si.row0;
-    const int tok0 = part * PT;
-    const int tok1 = min(si.L, tok0 + PT);
+    const int tok0 = kWholeContext ? 0 : part * PT;
+    const int tok1 = kWholeContext ? si.L : min(si.L, tok0 + PT);
     const int j0 = tok0 / kBlockTokens;
     const int nb = (tok1 + kBlockTokens - 1) / kBlockTokens - j0;
-    const int head = l16;                    // MFMA column = query head of the group
-    const bool hv = head < G;
+    const int head = kNoShare ? hsel : l16;  // MFMA column = query head of the group
+    const bool hv = kNoShare ? l16 == 0 : head < G;
     const int hq = g * G + (hv ? head : 0);
 
     int phys_lane = 0;
-    if (lane < nb) {
-      phys_lane = a.block_tables[static_cast<int64_t>(si.slot) * a.max_blocks + j0 + lane];
-      phys_lane = min(max(phys_lane, 0), a.num_blocks - 1);
-    }
+    int slice = 0;                           // kWholeContext: the 64-entry table slice held
+    auto load_slice = [&](int sl) {
+      phys_lane = 0;
+      if (lane + sl * kWave < nb) {
+        phys_lane = a.block_tables[static_cast<int64_t>(si.slot) * a.max_blocks + j0 + sl * kWave + lane];
+        phys_lane = min(max(phys_lane, 0), a.num_blocks - 1);
+      }
+    };
+    load_slice(0);
     // Q^T operand: lane holds dims 32 kk + 8 lg .. + 7 of its head.
     bf16x8_t qb[M::kKSteps];
     {
@@ -153,6 +171,15 @@ __global__ __launch_bounds__(64, kDecodeMfmaMinWaves) void decode_mfma_kernel(At
     // tell the tile in flight from the tile being read, does not wait on them
     // - the explicit s_waitcnt counts below do.
     auto issue = [&](int stage, int jj) {
+      if constexpr (kWholeContext) {
+        if ((jj >> 6) != slice) {
+          slice = jj >> 6;
+          load_slice(slice);
+          // drains the tile loads too, so every count below stays exact
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        jj &= kWave - 1;
+      }
       const int phys = __builtin_amdgcn_readlane(phys_lane, jj);
       const int64_t off = (static_cast<int64_t>(phys) * a.num_kv_heads + g) * M::kTile;
       unsigned char *kd = stage == 0 ? k0 : (stage == 1 ? k1 : k2);

@@ -36,6 +36,15 @@ constexpr int32_t kDecodePartitionTokens = PKV_DECODE_PARTITION_TOKENS;
 #define PKV_DECODE_MFMA_MIN_WAVES 3
 #endif
 constexpr int kDecodeMfmaMinWaves = PKV_DECODE_MFMA_MIN_WAVES;
+// Ablation knobs of the MFMA decode kernel (measurement builds only): one
+// wavefront per query head instead of per GQA group, and one wavefront per
+// row's whole context instead of split-context partitions.
+#ifndef PKV_DECODE_NO_GQA_SHARE
+#define PKV_DECODE_NO_GQA_SHARE 0
+#endif
+#ifndef PKV_DECODE_WHOLE_CONTEXT
+#define PKV_DECODE_WHOLE_CONTEXT 0
+#endif
 #ifndef PKV_STREAM_LOADS
 #define PKV_STREAM_LOADS 1
 #endif

@@ -24,6 +24,7 @@ struct AppendArgs {
   uint4 *pool_v;
   int32_t num_tokens;
   int32_t num_kv_heads;
+  int32_t heads_shift;         // log2(num_kv_heads) when it is a power of two, else -1
   int64_t pool_slots;
   // Optional: copy stage_len int32 of step metadata from stage_src (pinned
   // host memory the device can read) to stage_dst (device) in the same pass.
@@ -32,18 +33,23 @@ struct AppendArgs {
   int32_t stage_len;
 };
 
+// (token, head) of source row r: a shift for power-of-two head counts, else
+// one 32-bit division (the host keeps T x Hkv x row units below 2^31).
+__device__ __forceinline__ uint32_t token_of_row(uint32_t r, int32_t heads, int32_t heads_shift) {
+  return heads_shift >= 0 ? r >> heads_shift : r / static_cast<uint32_t>(heads);
+}
+
 template <int ROW16>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = tid; i < a.stage_len; i += nthreads) a.stage_dst[i] = a.stage_src[i];
-  const int64_t per_token = static_cast<int64_t>(a.num_kv_heads) * ROW16;
-  const int64_t total = per_token * a.num_tokens;
-  for (int64_t c = tid; c < total; c += nthreads) {
-    const int64_t t = c / per_token;
-    const int64_t rem = c - t * per_token;
-    const int64_t h = rem / ROW16;
-    const int64_t w = rem - h * ROW16;
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t nthreads = gridDim.x * blockDim.x;
+  for (uint32_t i = tid; i < static_cast<uint32_t>(a.stage_len); i += nthreads) a.stage_dst[i] = a.stage_src[i];
+  const uint32_t total = static_cast<uint32_t>(a.num_tokens) * static_cast<uint32_t>(a.num_kv_heads) * ROW16;
+  for (uint32_t c = tid; c < total; c += nthreads) {
+    const uint32_t r = c / ROW16;                                // (token, head) row
+    const uint32_t w = c - r * ROW16;
+    const uint32_t t = token_of_row(r, a.num_kv_heads, a.heads_shift);
+    const uint32_t h = r - t * static_cast<uint32_t>(a.num_kv_heads);
     const int64_t s = a.slot_mapping[t];
     if (s < 0 || s >= a.pool_slots) continue;
     const int64_t blk = s / kBlockTokens;
@@ -71,6 +77,7 @@ struct Q8AppendArgs {
   float *scale_v;
   int32_t num_tokens;
   int32_t num_kv_heads;
+  int32_t heads_shift;         // log2(num_kv_heads) when it is a power of two, else -1
   int64_t pool_slots;
   const int32_t *stage_src;
   int32_t *stage_dst;
@@ -112,22 +119,27 @@ __device__ __forceinline__ void quantize_row8(const uint4 in, int li, uint2 *cod
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_q8_kernel(Q8AppendArgs a) {
   constexpr int R = D / 8;                    // lanes per row
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = tid; i < a.stage_len; i += nthreads) a.stage_dst[i] = a.stage_src[i];
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t nthreads = gridDim.x * blockDim.x;
+  for (uint32_t i = tid; i < static_cast<uint32_t>(a.stage_len); i += nthreads) a.stage_dst[i] = a.stage_src[i];
   const int li = static_cast<int>(tid % R);
-  const int64_t rows = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads;
-  for (int64_t r = tid / R; r < rows; r += nthreads / R) {
-    const int64_t t = r / a.num_kv_heads;
-    const int64_t h = r - t * a.num_kv_heads;
+  const uint32_t rows = static_cast<uint32_t>(a.num_tokens) * static_cast<uint32_t>(a.num_kv_heads);
+  for (uint32_t r = tid / R; r < rows; r += nthreads / R) {
+    const uint32_t t = token_of_row(r, a.num_kv_heads, a.heads_shift);
+    const int64_t h = r - t * static_cast<uint32_t>(a.num_kv_heads);
     const int64_t s = a.slot_mapping[t];
     if (s < 0 || s >= a.pool_slots) continue;   // the whole row's lanes skip together
     const int64_t blk = s / kBlockTokens;
     const int64_t off = s - blk * kBlockTokens;
     const int64_t drow = (blk * a.num_kv_heads + h) * kBlockTokens + off;
-    quantize_row8<R>(a.k_new[r * R + li], li, a.codes_k + drow * R + li, a.scale_k + drow);
-    quantize_row8<R>(a.v_new[r * R + li], li, a.codes_v + drow * R + li, a.scale_v + drow);
+    const int64_t src = static_cast<int64_t>(r) * R + li;
+    quantize_row8<R>(a.k_new[src], li, a.codes_k + drow * R + li, a.scale_k + drow);
+    quantize_row8<R>(a.v_new[src], li, a.codes_v + drow * R + li, a.scale_v + drow);
   }
+}
+
+static int32_t heads_shift(int32_t heads) {
+  return heads > 0 && (heads & (heads - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(heads)) : -1;
 }
 
 int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void *v_new, int32_t num_tokens,
@@ -144,11 +156,13 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
     a.scale_v = pool.v_scale;
     a.num_tokens = num_tokens;
     a.num_kv_heads = pool.num_kv_heads;
+    a.heads_shift = heads_shift(pool.num_kv_heads);
     a.pool_slots = static_cast<int64_t>(pool.num_blocks) * pool.block_size;
     a.stage_src = stage_src;
     a.stage_dst = stage_dst;
     a.stage_len = stage_src && stage_dst ? stage_len : 0;
     const int64_t lanes = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * (pool.head_dim / 8);
+    if (lanes >= (int64_t{1} << 31)) return PKV_ERR_UNSUPPORTED;
     int64_t blocks = ((lanes > a.stage_len ? lanes : a.stage_len) + 255) / 256;
     if (blocks < 1) blocks = 1;
     if (blocks > 65536) blocks = 65536;
@@ -162,6 +176,7 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
   }
   const int row16 = pool.head_dim * (pool.dtype == PKV_F32 ? 4 : 2) / 16;
   const int64_t units = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * row16;
+  if (units >= (int64_t{1} << 31)) return PKV_ERR_UNSUPPORTED;   // 32-bit unit indices
   const int threads = 256;
   int64_t blocks = ((units > stage_len ? units : stage_len) + threads - 1) / threads;
   if (blocks < 1) blocks = 1;
@@ -174,6 +189,7 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
   a.pool_v = static_cast<uint4 *>(pool.v);
   a.num_tokens = num_tokens;
   a.num_kv_heads = pool.num_kv_heads;
+  a.heads_shift = heads_shift(pool.num_kv_heads);
   a.pool_slots = static_cast<int64_t>(pool.num_blocks) * pool.block_size;
   a.stage_src = stage_src;
   a.stage_dst = stage_dst;

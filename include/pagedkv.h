@@ -73,10 +73,12 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 } pkv_dtype;
  *
  * PKV_I8 is an 8-bit KV cache (the lucebox blog's R9700 DFlash2 section runs
  * its KV in an 8-bit format; the pages do not define one, so this is the
- * library's own).  k and v hold int8 codes in the layout above; k_scale and
- * v_scale hold one float32 per (block, KV head, position):
- * [num_blocks][num_kv_heads][block_size].  A stored row (the head_dim values
- * of one token and KV head) stands for code * scale.  Rows are written by
+ * library's own).  k and v hold int8 codes in the layout above; scales holds
+ * one float32 per (block, KV head, K or V, position):
+ * [num_blocks][num_kv_heads][2][block_size], the block's 16 K scales of a KV
+ * head followed by its 16 V scales, so one 128-byte run carries both halves
+ * of a tile's scales.  A stored row (the head_dim values of one token and KV
+ * head) stands for code * scale.  Rows are written by
  * pkv_kv_append from bf16 input:
  *   amax = max |x| over the row;  amax == 0 gives codes 0 and scale 0;
  *   otherwise inv = 127 / amax and scale = amax / 127 (float32, correctly
@@ -95,8 +97,8 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t dtype;        /* pkv_dtype */
-  float *k_scale;       /* PKV_I8 only: device [num_blocks][num_kv_heads][block_size] */
-  float *v_scale;       /* PKV_I8 only: same shape; NULL for other dtypes            */
+  float *scales;        /* PKV_I8 only: device [num_blocks][num_kv_heads][2][block_size]
+                           (index 0 = K, 1 = V); NULL for other dtypes              */
 } pkv_pool;
 
 /* ------------------------------------------------------------------ device */

@@ -38,7 +38,7 @@ _pi32 = ctypes.POINTER(ctypes.c_int32)
 class PoolDesc(ctypes.Structure):
     _fields_ = [("k", _p), ("v", _p), ("num_blocks", _i32), ("block_size", _i32),
                 ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32),
-                ("k_scale", _p), ("v_scale", _p)]
+                ("scales", _p)]
 
 
 class StepDesc(ctypes.Structure):
@@ -173,7 +173,8 @@ def _dptr(t):
 class KVPool:
     """The shared pool: K and V, each [num_blocks][num_kv_heads][16][head_dim].
     dtype torch.int8 makes an 8-bit pool: int8 codes plus float32 scales
-    k_scale / v_scale [num_blocks][num_kv_heads][16] (see pkv_pool).  Poison
+    [num_blocks][num_kv_heads][2][16] (K's 16 then V's 16 per block and head;
+    see pkv_pool); k_scale / v_scale are views of its two halves.  Poison
     fills unwritten positions with NaN (codes: -128, never a valid code)."""
 
     def __init__(self, num_blocks, num_kv_heads, head_dim, dtype, block_size=16, device="cuda", poison=True):
@@ -181,16 +182,16 @@ class KVPool:
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         self.k = torch.empty(shape, dtype=dtype, device=device)
         self.v = torch.empty(shape, dtype=dtype, device=device)
-        self.k_scale = self.v_scale = None
+        self.scales = self.k_scale = self.v_scale = None
         if dtype == torch.int8:
-            self.k_scale = torch.empty(shape[:3], dtype=torch.float32, device=device)
-            self.v_scale = torch.empty(shape[:3], dtype=torch.float32, device=device)
+            self.scales = torch.empty((num_blocks, num_kv_heads, 2, block_size), dtype=torch.float32, device=device)
+            self.k_scale = self.scales[:, :, 0]
+            self.v_scale = self.scales[:, :, 1]
         if poison:
             if dtype == torch.int8:
                 self.k.fill_(-128)
                 self.v.fill_(-128)
-                self.k_scale.fill_(float("nan"))
-                self.v_scale.fill_(float("nan"))
+                self.scales.fill_(float("nan"))
             else:
                 self.k.fill_(float("nan"))
                 self.v.fill_(float("nan"))
@@ -198,8 +199,7 @@ class KVPool:
         self.dtype = dtype
         self._desc = PoolDesc(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.block_size,
                               self.num_kv_heads, self.head_dim, pkv_dtype_of(self.dtype),
-                              self.k_scale.data_ptr() if self.k_scale is not None else None,
-                              self.v_scale.data_ptr() if self.v_scale is not None else None)
+                              self.scales.data_ptr() if self.scales is not None else None)
         self._desc_ref = ctypes.byref(self._desc)
 
     def desc(self) -> PoolDesc:

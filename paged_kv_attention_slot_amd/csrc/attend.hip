@@ -20,7 +20,7 @@ namespace {
 bool pool_ok(const pkv_pool *p) {
   if (!p || !p->k || !p->v) return false;
   if (p->num_blocks <= 0 || p->num_kv_heads <= 0 || p->block_size <= 0 || p->head_dim <= 0) return false;
-  if (p->dtype == PKV_I8) return p->k_scale && p->v_scale;
+  if (p->dtype == PKV_I8) return p->scales != nullptr;
   return p->dtype == PKV_F32 || p->dtype == PKV_BF16;
 }
 
@@ -390,8 +390,7 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.k_scale = pool->dtype == PKV_I8 ? pool->k_scale : nullptr;
-  a.v_scale = pool->dtype == PKV_I8 ? pool->v_scale : nullptr;
+  a.scales = pool->dtype == PKV_I8 ? pool->scales : nullptr;
 
   // Multi-row segments on the chunk kernels, or on the verify kernel when
   // short (unless every multi-row segment goes row by row on the decode

@@ -192,8 +192,9 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     }
     // Direct-to-LDS sources: load x fills staging chunk x * 64 + lane.  K
     // chunk position (t, p) holds code chunk kswz(t, p) of row t; V chunks
-    // stay in order.  Scales: lanes 0-15 the K scales of tokens 0-15, lanes
-    // 16-31 the V scales, lanes 32-63 the same again (unused).
+    // stay in order.  Scales: the tile's 32-float run (K scales of tokens
+    // 0-15, then the V scales), one 128-byte line; lanes 32-63 load the same
+    // run again into the stage's unused upper half.
     int ksrc[M::kCodeLoads];
 #pragma unroll
     for (int x = 0; x < M::kCodeLoads; ++x) {
@@ -204,8 +205,7 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     }
     const char *kbase = static_cast<const char *>(a.k);
     const char *vbase = static_cast<const char *>(a.v);
-    const float *sbase = (lane & 16) ? a.v_scale : a.k_scale;
-    const int stok = lane & 15;
+    const float *sbase = a.scales + (lane & 31);
     // The loads are issued as inline assembly (M0 takes the LDS destination;
     // nothing else here uses M0); the explicit s_waitcnt counts below wait
     // on them.
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
                      ::"s"(ldsv), "v"(gv) : "memory");
       }
       const unsigned ldss = q8_lds_addr(st + 2 * M::kCodeTile);
-      const void *gs = sbase + th * kBlockTokens + stok;
+      const void *gs = sbase + th * (2 * kBlockTokens);
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off " PKV_LDS_DMA_HINT
                    ::"s"(ldss), "v"(gs) : "memory");
     };

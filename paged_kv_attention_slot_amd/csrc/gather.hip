@@ -34,10 +34,8 @@ struct GatherArgs {
   const uint4 *src_v;
   uint4 *dst_k;
   uint4 *dst_v;
-  const float *src_sk;   // 8-bit pools: per-row scales, [blocks][Hkv][16] (else null)
-  const float *src_sv;
-  float *dst_sk;
-  float *dst_sv;
+  const float *src_scales;  // 8-bit pools: per-row scales, [blocks][Hkv][2][16] (else null)
+  float *dst_scales;
   int32_t num_slots;
   int32_t max_blocks;
   int32_t src_blocks;
@@ -105,12 +103,10 @@ __device__ inline void gather_one(const GatherArgs &g, int b, int s, int j) {
       }
     }
   }
-  if (g.src_sk) {
-    const int64_t per_scales = static_cast<int64_t>(g.num_kv_heads) * kBlockTokens;
-    for (int64_t u = threadIdx.x; u < per_scales; u += 256) {
-      g.dst_sk[dst * per_scales + u] = g.src_sk[phys * per_scales + u];
-      g.dst_sv[dst * per_scales + u] = g.src_sv[phys * per_scales + u];
-    }
+  if (g.src_scales) {
+    const int64_t per_scales = static_cast<int64_t>(g.num_kv_heads) * 2 * kBlockTokens;
+    for (int64_t u = threadIdx.x; u < per_scales; u += 256)
+      g.dst_scales[dst * per_scales + u] = g.src_scales[phys * per_scales + u];
   }
 }
 
@@ -181,10 +177,8 @@ int launch_gather_window(const int32_t *row_to_slot, int32_t num_segments, const
   g.dst_blocks = dst.num_blocks;
   g.num_kv_heads = src.num_kv_heads;
   const bool q8 = src.dtype == PKV_I8;
-  g.src_sk = q8 ? src.k_scale : nullptr;
-  g.src_sv = q8 ? src.v_scale : nullptr;
-  g.dst_sk = q8 ? dst.k_scale : nullptr;
-  g.dst_sv = q8 ? dst.v_scale : nullptr;
+  g.src_scales = q8 ? src.scales : nullptr;
+  g.dst_scales = q8 ? dst.scales : nullptr;
   if (row16 != 4 && row16 != 8 && row16 != 16 && row16 != 32) return PKV_ERR_UNSUPPORTED;
   if (num_segments <= kGatherLdsSegments) {
     // a persistent grid, never more workgroups than blocks

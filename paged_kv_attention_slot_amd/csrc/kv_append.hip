@@ -73,8 +73,7 @@ struct Q8AppendArgs {
   const uint4 *v_new;
   uint2 *codes_k;              // [blocks][Hkv][16][D] int8, as 8-byte units
   uint2 *codes_v;
-  float *scale_k;              // [blocks][Hkv][16]
-  float *scale_v;
+  float *scales;               // [blocks][Hkv][2][16]: K's 16 scales, then V's
   int32_t num_tokens;
   int32_t num_kv_heads;
   int32_t heads_shift;         // log2(num_kv_heads) when it is a power of two, else -1
@@ -131,10 +130,12 @@ __global__ __launch_bounds__(256) void kv_append_q8_kernel(Q8AppendArgs a) {
     if (s < 0 || s >= a.pool_slots) continue;   // the whole row's lanes skip together
     const int64_t blk = s / kBlockTokens;
     const int64_t off = s - blk * kBlockTokens;
-    const int64_t drow = (blk * a.num_kv_heads + h) * kBlockTokens + off;
+    const int64_t tile = blk * a.num_kv_heads + h;
+    const int64_t drow = tile * kBlockTokens + off;
+    const int64_t srow = tile * (2 * kBlockTokens) + off;
     const int64_t src = static_cast<int64_t>(r) * R + li;
-    quantize_row8<R>(a.k_new[src], li, a.codes_k + drow * R + li, a.scale_k + drow);
-    quantize_row8<R>(a.v_new[src], li, a.codes_v + drow * R + li, a.scale_v + drow);
+    quantize_row8<R>(a.k_new[src], li, a.codes_k + drow * R + li, a.scales + srow);
+    quantize_row8<R>(a.v_new[src], li, a.codes_v + drow * R + li, a.scales + srow + kBlockTokens);
   }
 }
 
@@ -152,8 +153,7 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
     a.v_new = static_cast<const uint4 *>(v_new);
     a.codes_k = static_cast<uint2 *>(pool.k);
     a.codes_v = static_cast<uint2 *>(pool.v);
-    a.scale_k = pool.k_scale;
-    a.scale_v = pool.v_scale;
+    a.scales = pool.scales;
     a.num_tokens = num_tokens;
     a.num_kv_heads = pool.num_kv_heads;
     a.heads_shift = heads_shift(pool.num_kv_heads);
@@ -208,11 +208,11 @@ int launch_kv_append(const int32_t *slot_mapping, const void *k_new, const void 
 // into block dst[c].  Workgroup (x, c) copies 256 16-byte units of pair c's
 // [Hkv][block][row16] span; both sides are contiguous, so every access is
 // coalesced.  The ids may live in pinned host memory (read once per thread).
-// An 8-bit pool's scales ([Hkv][16] floats per block) travel with the codes.
+// An 8-bit pool's scales ([Hkv][2][16] floats per block) travel with the codes.
 template <int ROW16>
 __global__ __launch_bounds__(256) void kv_copy_blocks_kernel(const int32_t *src, const int32_t *dst, uint4 *pool_k,
-                                                             uint4 *pool_v, float *scale_k, float *scale_v,
-                                                             int32_t num_blocks, int32_t num_kv_heads) {
+                                                             uint4 *pool_v, float *scales, int32_t num_blocks,
+                                                             int32_t num_kv_heads) {
   const int64_t per_block = static_cast<int64_t>(num_kv_heads) * kBlockTokens * ROW16;
   const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (u >= per_block) return;
@@ -220,11 +220,8 @@ __global__ __launch_bounds__(256) void kv_copy_blocks_kernel(const int32_t *src,
   if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
   pool_k[d * per_block + u] = pool_k[s * per_block + u];
   pool_v[d * per_block + u] = pool_v[s * per_block + u];
-  const int64_t per_scales = static_cast<int64_t>(num_kv_heads) * kBlockTokens;
-  if (scale_k && u < per_scales) {
-    scale_k[d * per_scales + u] = scale_k[s * per_scales + u];
-    scale_v[d * per_scales + u] = scale_v[s * per_scales + u];
-  }
+  const int64_t per_scales = static_cast<int64_t>(num_kv_heads) * 2 * kBlockTokens;
+  if (scales && u < per_scales) scales[d * per_scales + u] = scales[s * per_scales + u];
 }
 
 int pool_row16(const pkv_pool &pool) {
@@ -240,14 +237,13 @@ int launch_copy_blocks(const int32_t *src, const int32_t *dst, int32_t num_copie
   const int64_t per_block = static_cast<int64_t>(pool.num_kv_heads) * kBlockTokens * row16;
   const dim3 grid(static_cast<unsigned>((per_block + 255) / 256), static_cast<unsigned>(num_copies));
   uint4 *k = static_cast<uint4 *>(pool.k), *v = static_cast<uint4 *>(pool.v);
-  float *sk = pool.dtype == PKV_I8 ? pool.k_scale : nullptr;
-  float *sv = pool.dtype == PKV_I8 ? pool.v_scale : nullptr;
+  float *sc = pool.dtype == PKV_I8 ? pool.scales : nullptr;
   const int nb = pool.num_blocks, hkv = pool.num_kv_heads;
   switch (row16) {
-    case 4: kv_copy_blocks_kernel<4><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
-    case 8: kv_copy_blocks_kernel<8><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
-    case 16: kv_copy_blocks_kernel<16><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
-    case 32: kv_copy_blocks_kernel<32><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sk, sv, nb, hkv); break;
+    case 4: kv_copy_blocks_kernel<4><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sc, nb, hkv); break;
+    case 8: kv_copy_blocks_kernel<8><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sc, nb, hkv); break;
+    case 16: kv_copy_blocks_kernel<16><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sc, nb, hkv); break;
+    case 32: kv_copy_blocks_kernel<32><<<grid, dim3(256), 0, stream>>>(src, dst, k, v, sc, nb, hkv); break;
     default: return PKV_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;

@@ -238,8 +238,7 @@ struct AttendArgs {
   int32_t out_bf16;
   float scale;          // softmax scale
   float scale_log2;     // scale * log2(e)
-  const float *k_scale; // 8-bit pools: [num_blocks][Hkv][16] per-row scales (else null)
-  const float *v_scale;
+  const float *scales;  // 8-bit pools: [num_blocks][Hkv][2][16] per-row scales, K then V (else null)
 };
 
 // KV append; optionally also copies stage_len int32 of step metadata from

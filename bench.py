@@ -22,7 +22,7 @@ Prints one JSON line:
   roofline     = the attention launch (decode kernel + partition reduce),
                  replayed 20 times on the last step's metadata after the timed
                  steps with the caches flushed before each call (a 1 GiB
-                 fill, outside the events), each call bracketed by HIP events
+                 read, outside the events), each call bracketed by HIP events
                  on its stream; algorithmic bytes per call / mean duration vs
                  8 TB/s (attend_ms_warm_avg: the same calls back to back)
   cpu_baseline = the CPU oracle on a bounded sample of the same step (with
@@ -79,6 +79,9 @@ def parse_args():
     ap.add_argument("--ablation", choices=["gather", "prefix"], default=None,
                     help="gather: block-table decode vs gather-then-attend; prefix: adopted vs cold "
                          "shared-prefix step")
+    ap.add_argument("--flush", choices=["read", "write"], default="read",
+                    help="how cold calls evict the caches: read 1 GiB (default) or fill it; a fill leaves dirty "
+                         "lines whose write-back lands inside the next call's timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (a plain copy of known size for counter scaling)")
     return ap.parse_args()
@@ -143,12 +146,28 @@ def step_roofline(w, segments, lens):
                                   mr_b / (HBM_PEAK_GBS * 1e9) else "hbm"}
 
 
+FLUSH_KIND = "read"
+
+
+def evict_caches(flush, i):
+    """Push the next call's inputs out of the L2s and the 256 MB Infinity
+    Cache by streaming the 1 GiB buffer `flush` through them, on the current
+    stream.  "read" sums it (one small result written); "write" fills it,
+    which leaves dirty lines behind whose write-back then runs inside the
+    next call's timing window."""
+    if FLUSH_KIND == "write":
+        flush.fill_(i & 0xFF)
+    else:
+        import torch
+        flush.view(torch.int64).sum()
+
+
 def _cold_times(torch, stream, fn, reps, flush):
     """Durations of fn() (seconds), each bracketed by HIP events on `stream`
-    with the caches flushed before it (a fill of `flush`, outside the events)."""
+    with the caches flushed before it (evict_caches, outside the events)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i, (a, b) in enumerate(ev):
-        flush.fill_(i & 0xFF)
+        evict_caches(flush, i)
         a.record(stream)
         fn()
         b.record(stream)
@@ -279,12 +298,12 @@ def run_mixed(args, w, pk, torch, dev):
     wall = time.perf_counter() - t0
     gc.enable()
     att = sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
-    # the same step with the caches flushed before each call (a 1 GiB fill,
+    # the same step with the caches flushed before each call (evict_caches,
     # outside the events)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
     for i, (a_, b_) in enumerate(cold_ev):
-        flush.fill_(i & 0xFF)
+        evict_caches(flush, i)
         a_.record(stream)
         eng.run_prepared(prep)
         b_.record(stream)
@@ -627,7 +646,9 @@ def run_extras(pk, torch, dev, args):
 
 
 def main():
+    global FLUSH_KIND
     args = parse_args()
+    FLUSH_KIND = args.flush
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
               "mode", file=sys.stderr)
@@ -710,7 +731,7 @@ def main():
     # Roofline of the attention launch (decode kernel + partition reduce):
     # replay it on the last step's metadata, each call bracketed by HIP events
     # recorded on the stream the kernels run on.  Cold: before each call a
-    # 1 GiB fill (4x the 256 MB Infinity Cache) evicts the caches, outside
+    # 1 GiB read (4x the 256 MB Infinity Cache) evicts the caches, outside
     # the events; the roofline uses the cold calls.  Warm: back to back.
     last = metas[-1]
     lens = last.host["context_lens"][last.host["row_to_slot"]].tolist()
@@ -722,7 +743,7 @@ def main():
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i, (a_, b_) in enumerate(ev):
             if cold:
-                flush.fill_(i & 0xFF)
+                evict_caches(flush, i)
             a_.record(stream)
             eng.attend(last, q, w.scale, out=out)
             b_.record(stream)
@@ -766,7 +787,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("pkv decode_q8_kernel" if q8 else "pkv decode_mfma_kernel")
-                     + " + reduce_kernel (one paged_attend launch)"},
+                     + " + reduce_kernel (one paged_attend launch)",
+                     "cold_flush": f"1 GiB {FLUSH_KIND} before each timed call"},
     }
     if not args.no_extras:
         line["extras"] = run_extras(pk, torch, dev, args)

@@ -77,6 +77,18 @@ def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str |
     return lib_path
 
 
+PROBE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "tile_read_probe.hip")
+
+
+def build_probe(out: str | None = None, verbose: bool = False) -> str:
+    """Compile the read-only tile probe (a standalone executable that times
+    the decode access pattern without arithmetic) and return its path."""
+    exe = out or os.path.join(BUILD_DIR, "tile_read_probe")
+    os.makedirs(os.path.dirname(exe), exist_ok=True)
+    _run([_hipcc(), *[f for f in HIP_FLAGS if f not in ("-fPIC", "-Wall")], "-o", exe, PROBE_SRC], verbose)
+    return exe
+
+
 if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser()
@@ -84,5 +96,9 @@ if __name__ == "__main__":
     ap.add_argument("-D", dest="defines", action="append", default=[], help="NAME=VALUE tuning override")
     ap.add_argument("--out", default=None, help="write the library here instead of the package")
     ap.add_argument("--build-dir", default=None)
+    ap.add_argument("--probe", action="store_true", help="build only the tile read probe executable")
     a = ap.parse_args()
-    print(build(verbose=a.verbose, defines=a.defines, out=a.out, build_dir=a.build_dir))
+    if a.probe:
+        print(build_probe(out=a.out, verbose=a.verbose))
+    else:
+        print(build(verbose=a.verbose, defines=a.defines, out=a.out, build_dir=a.build_dir))

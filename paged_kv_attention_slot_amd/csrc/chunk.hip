@@ -90,18 +90,16 @@ __host__ __device__ __forceinline__ ChunkShape chunk_shape(int n, int L, int G) 
 }
 
 template <int D>
-__device__ __forceinline__ int chunk_units(const AttendArgs &a, int b, int G) {
-  const SegInfo s = seg_info(a, b);
+__device__ __forceinline__ int chunk_units_of(const SegInfo &s, int G) {
   if (!s.ok || s.n < 2 || verify_segment(s.n, G, D)) return 0;
   const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.mtiles * c.splits;
 }
 
-// Partial slots (per KV head) of segment b: one per (M-row, key range) when
+// Partial slots (per KV head) of a segment: one per (M-row, key range) when
 // the segment is cut into key ranges, else none.
 template <int D>
-__device__ __forceinline__ int chunk_partial_slots(const AttendArgs &a, int b, int G) {
-  const SegInfo s = seg_info(a, b);
+__device__ __forceinline__ int chunk_partial_slots_of(const SegInfo &s, int G) {
   if (!s.ok || s.n < 2 || verify_segment(s.n, G, D)) return 0;
   const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.splits > 1 ? s.n * G * c.splits : 0;
@@ -168,16 +166,15 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  auto units_fn = [&](int b) { return chunk_units<D>(a, b, G); };
+  const auto map = make_unit_map(a, [&](const SegInfo &s) { return chunk_units_of<D>(s, G); },
+                                 [&](const SegInfo &s) { return chunk_partial_slots_of<D>(s, G); });
   const int hkv = a.num_kv_heads;
-  const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
-  if (static_cast<int64_t>(blockIdx.x) >= static_cast<int64_t>(total) * hkv) return;
+  if (static_cast<int64_t>(blockIdx.x) >= static_cast<int64_t>(map.total) * hkv) return;
   const int unit = blockIdx.x / hkv;
   const int g = blockIdx.x - unit * hkv;
-  int u;
-  const int b = __builtin_amdgcn_readfirstlane(find_unit(a.num_segments, unit, units_fn, &u));
-  u = __builtin_amdgcn_readfirstlane(u);
-  const SegInfo si = seg_info_uniform(a, b);
+  const UnitPlace place = map.place(unit);
+  const int u = place.rest;
+  const SegInfo si = place.si;
   if (!si.ok) return;
   const int n = si.n, L = si.L;
   const int mtot = n * G;
@@ -198,7 +195,7 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   int64_t part_base = 0;
   if (partial_out) {
     if (a.chunk_part == nullptr) return;
-    part_base = units_before(b, [&](int bb) { return chunk_partial_slots<D>(a, bb, G); });
+    part_base = place.slots_before;
     if (part_base + static_cast<int64_t>(mtot) * cs.splits > a.chunk_slots) return;   // bounds understated
   }
   const int wave_pos0 = mw < mtot ? L - n + mw / G : -1;
@@ -569,8 +566,7 @@ constexpr int kMergeRowsPerWave = 4;
 constexpr int kMergeWaves = 4;
 
 template <int D>
-__device__ __forceinline__ int merge_units(const AttendArgs &a, int b, int G) {
-  const SegInfo s = seg_info(a, b);
+__device__ __forceinline__ int merge_units_of(const SegInfo &s, int G) {
   if (!s.ok || s.n < 2 || verify_segment(s.n, G, D)) return 0;
   const ChunkShape c = chunk_shape<D>(s.n, s.L, G);
   return c.splits > 1 ? (s.n * G + kMergeRowsPerWave - 1) / kMergeRowsPerWave : 0;
@@ -586,17 +582,16 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void chunk_merge_kernel(Attend
   const int hkv = a.num_kv_heads;
   const int wg = blockIdx.x / hkv;
   const int g = blockIdx.x - wg * hkv;                // same head-to-workgroup order as the chunk kernel
-  auto units_fn = [&](int b) { return merge_units<D>(a, b, G); };
-  const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
+  const auto map = make_unit_map(a, [&](const SegInfo &s) { return merge_units_of<D>(s, G); },
+                                 [&](const SegInfo &s) { return chunk_partial_slots_of<D>(s, G); });
   const int unit = wg * kMergeWaves + wave;
-  if (unit >= total) return;
-  int u;
-  const int b = __builtin_amdgcn_readfirstlane(find_unit(a.num_segments, unit, units_fn, &u));
-  u = __builtin_amdgcn_readfirstlane(u);
-  const SegInfo si = seg_info_uniform(a, b);
+  if (unit >= map.total) return;
+  const UnitPlace place = map.place(unit);
+  const int u = place.rest;
+  const SegInfo si = place.si;
   if (!si.ok) return;
   const ChunkShape cs = chunk_shape<D>(si.n, si.L, G);
-  const int64_t part_base = units_before(b, [&](int bb) { return chunk_partial_slots<D>(a, bb, G); });
+  const int64_t part_base = place.slots_before;
   if (part_base + static_cast<int64_t>(si.n) * G * cs.splits > a.chunk_slots) return;
   const int m = u * kMergeRowsPerWave + (lane >> 4);
   if (m >= si.n * G) return;                          // no cross-group exchange below

@@ -185,4 +185,81 @@ __device__ __forceinline__ int find_unit(int num_segments, int unit, F units_fn,
   return -1;
 }
 
+// Where a work unit falls: its segment b (-1 past the last unit), its index
+// within the segment, the segment's metadata, and the sum of the partial
+// slots of the segments before b.  All uniform over the wavefront.
+struct UnitPlace {
+  int b, rest;
+  int64_t slots_before;
+  SegInfo si;
+};
+
+// Work units and partial slots per segment, from units_of(SegInfo) and
+// slots_of(SegInfo) (both 0 for a segment that fails its checks).  When every
+// segment fits one wavefront the metadata is read once, lane b holding
+// segment b, so locating a unit costs one round of dependent loads and no
+// more; past that, each question walks the segments again.
+template <typename FU, typename FS>
+struct UnitMap {
+  const AttendArgs &a;
+  FU units_of;
+  FS slots_of;
+  bool in_lanes;
+  SegInfo mine;        // segment `lane` (in_lanes only)
+  int units, incl;     // its units and the inclusive scan over lanes
+  int total;           // units over all segments (uniform)
+
+  __device__ __forceinline__ UnitMap(const AttendArgs &args, FU fu, FS fs)
+      : a(args), units_of(fu), slots_of(fs), in_lanes(args.num_segments <= kWave) {
+    if (in_lanes) {
+      mine = seg_info(a, static_cast<int>(threadIdx.x & (kWave - 1)));
+      units = units_of(mine);
+      incl = wave_inclusive_scan(units);
+      total = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1));
+    } else {
+      mine = SegInfo{0, 0, 0, 0, false};
+      units = incl = 0;
+      total = __builtin_amdgcn_readfirstlane(
+          count_units(a.num_segments, [&](int b) { return units_of(seg_info(a, b)); }));
+    }
+  }
+
+  __device__ __forceinline__ UnitPlace place(int unit) const {
+    UnitPlace p;
+    p.b = -1;
+    p.rest = 0;
+    p.slots_before = 0;
+    p.si = SegInfo{0, 0, 0, 0, false};
+    if (unit < 0 || unit >= total) return p;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (in_lanes) {
+      const int bl = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(__ballot(incl > unit))) - 1);
+      p.b = bl;
+      p.rest = unit - (__builtin_amdgcn_readlane(incl, bl) - __builtin_amdgcn_readlane(units, bl));
+      p.si.slot = __builtin_amdgcn_readlane(mine.slot, bl);
+      p.si.L = __builtin_amdgcn_readlane(mine.L, bl);
+      p.si.n = __builtin_amdgcn_readlane(mine.n, bl);
+      p.si.row0 = __builtin_amdgcn_readlane(mine.row0, bl);
+      p.si.ok = true;                                   // a segment with units passed its checks
+      long long sb = lane < bl ? static_cast<long long>(slots_of(mine)) : 0;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) sb += __shfl_xor(sb, d);
+      p.slots_before = sb;
+      return p;
+    }
+    int r;
+    p.b = __builtin_amdgcn_readfirstlane(
+        find_unit(a.num_segments, unit, [&](int b) { return units_of(seg_info(a, b)); }, &r));
+    p.rest = __builtin_amdgcn_readfirstlane(r);
+    p.si = seg_info_uniform(a, p.b);
+    p.slots_before = units_before(p.b, [&](int b) { return slots_of(seg_info(a, b)); });
+    return p;
+  }
+};
+
+template <typename FU, typename FS>
+__device__ __forceinline__ UnitMap<FU, FS> make_unit_map(const AttendArgs &a, FU units_of, FS slots_of) {
+  return UnitMap<FU, FS>(a, units_of, slots_of);
+}
+
 }  // namespace pkv

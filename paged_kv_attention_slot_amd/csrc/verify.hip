@@ -75,15 +75,13 @@ __device__ __forceinline__ int vgroups(int n, int G) {
 }
 
 template <int D, int NC>
-__device__ __forceinline__ int verify_units(const AttendArgs &a, int b, int G) {
-  const SegInfo s = seg_info(a, b);
+__device__ __forceinline__ int verify_units_of(const SegInfo &s, int G) {
   return s.ok && verify_segment(s.n, G, D) ? vnum_parts(s.L) * vgroups<NC>(s.n, G) : 0;
 }
 
 // Rows of segment b in the verify partials (all of a verify segment's rows).
 template <int D>
-__device__ __forceinline__ int verify_partial_rows(const AttendArgs &a, int b, int G) {
-  const SegInfo s = seg_info(a, b);
+__device__ __forceinline__ int verify_partial_rows_of(const SegInfo &s, int G) {
   return s.ok && verify_segment(s.n, G, D) ? s.n : 0;
 }
 
@@ -101,17 +99,16 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
   const int lg = lane >> 4;
   const float c_log2 = a.scale_log2;
 
-  auto units_fn = [&](int b) { return verify_units<D, NC>(a, b, G); };
-  const int total = __builtin_amdgcn_readfirstlane(count_units(a.num_segments, units_fn));
-  const int64_t items = static_cast<int64_t>(total) * a.num_kv_heads;
+  const auto map = make_unit_map(a, [&](const SegInfo &s) { return verify_units_of<D, NC>(s, G); },
+                                 [&](const SegInfo &s) { return verify_partial_rows_of<D>(s, G); });
+  const int64_t items = static_cast<int64_t>(map.total) * a.num_kv_heads;
 
   for (int64_t f = blockIdx.x; f < items; f += gridDim.x) {
     const int unit = static_cast<int>(f / a.num_kv_heads);
     const int g = static_cast<int>(f - static_cast<int64_t>(unit) * a.num_kv_heads);
-    int u;
-    const int b = __builtin_amdgcn_readfirstlane(find_unit(a.num_segments, unit, units_fn, &u));
-    u = __builtin_amdgcn_readfirstlane(u);
-    const SegInfo si = seg_info_uniform(a, b);
+    const UnitPlace place = map.place(unit);
+    const int u = place.rest;
+    const SegInfo si = place.si;
     if (!si.ok) continue;
     const int ngr = vgroups<NC>(si.n, G);
     const int part = u / ngr;
@@ -124,7 +121,7 @@ __global__ __launch_bounds__(64, NC == 1 ? 3 : 2) void verify_kernel(AttendArgs 
     const int nb = (tok1 + kBlockTokens - 1) / kBlockTokens - j0;
     const int first_pos = si.L - si.n;          // position of row 0
     // first row of this segment in the verify partials (uniform)
-    const int64_t vrow0 = np > 1 ? units_before(b, [&](int bb) { return verify_partial_rows<D>(a, bb, G); }) : 0;
+    const int64_t vrow0 = np > 1 ? place.slots_before : 0;
 
     // Column tile c of this group: pair m = (cg * NC + c) * 16 + l16.
     int pos[NC];
@@ -364,7 +361,7 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(AttendArgs a, int G, i
   const SegInfo si = seg_info(a, b);
   if (!si.ok || !verify_segment(si.n, G, D) || a.verify_acc == nullptr || i >= si.n) return;
   if (vnum_parts(si.L) <= 1) return;
-  const int64_t vrow0 = units_before(b, [&](int bb) { return verify_partial_rows<D>(a, bb, G); });
+  const int64_t vrow0 = units_before(b, [&](int bb) { return verify_partial_rows_of<D>(seg_info(a, bb), G); });
   if (vrow0 + si.n > a.verify_rows) return;
   constexpr int DPL = D / kWave;
   const int pos = si.L - si.n + i;

@@ -604,6 +604,38 @@ def test_random_mixed_steps(seed, gpu_available):
         assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
 
 
+def _many_segments(d, hq, hkv, seed):
+    """100 segments, more than one wavefront holds: decode rows, then prompt
+    chunks (cut into key ranges), then short drafts, then decode rows again,
+    so that the chunk, merge and verify kernels find their segments and
+    partial slots past the first 64 segments."""
+    rng = np.random.default_rng(seed)
+    seqs = []
+    for s in range(60):
+        seqs.append((s, int(rng.integers(0, 700)), 1))
+    for s in range(60, 70):
+        seqs.append((s, int(rng.integers(1500, 3000)), int(rng.integers(20, 81))))
+    for s in range(70, 85):
+        seqs.append((s, int(rng.integers(0, 1200)), int(rng.integers(2, 9))))
+    for s in range(85, 100):
+        seqs.append((s, int(rng.integers(0, 1100)), 1))
+    order = rng.permutation(30) + 55          # shuffle the middle, across the 64-segment boundary
+    seqs[55:85] = [seqs[i] for i in order]
+    return make_custom(seqs, dtype="bf16", hq=hq, hkv=hkv, d=d, seed=seed, max_slots=128)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+@pytest.mark.parametrize("d,hq,hkv", [(128, 32, 8), (64, 40, 8)])
+def test_many_segments_beyond_one_wavefront(d, hq, hkv, fused, gpu_available):
+    _log(f"100 segments D{d} {hq}/{hkv} fused={fused}")
+    w = _many_segments(d, hq, hkv, seed=4242 + d)
+    eng, outs = _run_gpu(w, fused=fused)
+    res, (ok, ov) = run_workload(w)
+    _check_close(f"100 segments D{d}", outs[0][0], res[0]["out"], TOL["bf16"])
+    assert np.array_equal(_pool_bits(eng.pool.k), _oracle_bits(ok))
+    assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
+
+
 @pytest.mark.parametrize("name", ["1", "2", "3", "3v", "4a", "4b", "5", "3q", "5q", "prefix"])
 def test_one_call_step_equals_split_calls_bitwise(name, gpu_available):
     """pkv_mixed_step picks prefetch depths, column tiles, skipped launches

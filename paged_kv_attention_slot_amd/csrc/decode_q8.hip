@@ -239,9 +239,12 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
 #pragma unroll
     for (int dt = 0; dt < M::kDTiles; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Staged codes of one tile -> K operands (registers), the fp16 V tile
-    // (LDS) and this lane's four K and V scales (tokens 4 lg .. + 3).
-    auto convert = [&](int stage, halfx8_t (&ka)[M::kKSteps], floatx4_t &ks, floatx4_t &vs) {
+    // Staged codes of one tile -> K operands (registers), this lane's V code
+    // chunks (registers, for the fp16 V tile) and its four K and V scales
+    // (tokens 4 lg .. + 3).  Reads only: once they have landed the stage can
+    // be refilled.
+    auto read_stage = [&](int stage, halfx8_t (&ka)[M::kKSteps], uint4 (&vraw)[M::kChunksPerLane], floatx4_t &ks,
+                          floatx4_t &vs) {
       const unsigned char *st = stg + stage * kStage;
 #pragma unroll
       for (int kk = 0; kk < M::kKSteps; ++kk) {
@@ -251,11 +254,21 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
         ka[kk] = __builtin_bit_cast(halfx8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
       }
 #pragma unroll
+      for (int i = 0; i < M::kChunksPerLane; ++i)
+        vraw[i] = *reinterpret_cast<const uint4 *>(st + M::kCodeTile + (i * kWave + lane) * 16);
+      ks = *reinterpret_cast<const floatx4_t *>(st + 2 * M::kCodeTile + lg * 16);
+      vs = *reinterpret_cast<const floatx4_t *>(st + 2 * M::kCodeTile + 64 + lg * 16);
+    };
+    // The V code chunks -> the fp16 V tile in LDS (the transposed reads'
+    // layout).  The wave's earlier reads of the previous tile are ordered
+    // before these writes.
+    auto write_vt = [&](const uint4 (&vraw)[M::kChunksPerLane]) {
+#pragma unroll
       for (int i = 0; i < M::kChunksPerLane; ++i) {
         const int P = i * kWave + lane;
         const int t = P / M::kCodeCPR;
         const int p = P - t * M::kCodeCPR;
-        const uint4 w = *reinterpret_cast<const uint4 *>(st + M::kCodeTile + P * 16);
+        const uint4 w = vraw[i];
         const uint2 a0 = codes_to_f16x4(w.x), a1 = codes_to_f16x4(w.y);
         const uint2 a2 = codes_to_f16x4(w.z), a3 = codes_to_f16x4(w.w);
         const uint4 lo = make_uint4(a0.x, a0.y, a1.x, a1.y);
@@ -263,8 +276,6 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
         *reinterpret_cast<uint4 *>(vt + t * M::kRowBytes + M::swz(t, 2 * p) * 16) = lo;
         *reinterpret_cast<uint4 *>(vt + t * M::kRowBytes + M::swz(t, 2 * p + 1) * 16) = hi;
       }
-      ks = *reinterpret_cast<const floatx4_t *>(st + 2 * M::kCodeTile + lg * 16);
-      vs = *reinterpret_cast<const floatx4_t *>(st + 2 * M::kCodeTile + 64 + lg * 16);
     };
 
     auto compute = [&](const halfx8_t (&ka)[M::kKSteps], const floatx4_t &ks, const floatx4_t &vs, int jj,
@@ -333,13 +344,15 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
         if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(M::kPerIssue) : "memory");
         if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * M::kPerIssue) : "memory");
         halfx8_t ka[M::kKSteps];
+        uint4 vraw[M::kChunksPerLane];
         floatx4_t ks, vs;
-        convert(st, ka, ks, vs);
-        // every LDS access of the conversion has completed: the staging
-        // stage can be refilled and the V tile is in place
+        read_stage(st, ka, vraw, ks, vs);
+        // every read of the stage has completed: it can be refilled while
+        // the V tile is converted and the tile's arithmetic runs
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if constexpr (S > 1) issue(st, min(jj + st + S, nb - 1));
         else if (jj + 1 < nb) issue(0, jj + 1);
+        write_vt(vraw);
         if ((j0 + jj + st + 1) * kBlockTokens > tok_full)
           compute(ka, ks, vs, jj + st, std::true_type{});
         else

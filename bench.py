@@ -45,6 +45,7 @@ from __future__ import annotations
 
 import argparse
 import gc
+import ctypes
 import hashlib
 import itertools
 import json
@@ -82,6 +83,9 @@ def parse_args():
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="how cold calls evict the caches: read 1 GiB (default) or fill it; a fill leaves dirty "
                          "lines whose write-back lands inside the next call's timing")
+    ap.add_argument("--event-fence", choices=["none", "system"], default="none",
+                    help="timing events: fence-free HIP events (default) or torch's events, whose record adds a "
+                         "system-scope cache writeback to the timed interval")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (a plain copy of known size for counter scaling)")
     return ap.parse_args()
@@ -147,6 +151,53 @@ def step_roofline(w, segments, lens):
 
 
 FLUSH_KIND = "read"
+EVENT_FENCE = "none"     # timing events: "none" (fence-free HIP events) or "system" (torch's default)
+_HIP = None
+
+
+class TimingEvent:
+    """A HIP event made only for timing (hipEventDisableSystemFence): its
+    record performs no system-scope cache writeback and invalidate, a cost
+    that would otherwise land inside the interval it brackets and slow the
+    work after it.  Same interface as torch.cuda.Event(enable_timing=True);
+    read it only after a synchronize."""
+
+    def __init__(self):
+        global _HIP
+        if _HIP is None:
+            import torch
+            torch.cuda.init()
+            path = [ln.split()[-1] for ln in open("/proc/self/maps").read().splitlines()
+                    if "libamdhip64" in ln][0]
+            _HIP = ctypes.CDLL(path)       # the runtime torch loaded: the same stream handles
+            _HIP.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            _HIP.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            _HIP.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            _HIP.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip = _HIP
+        self.handle = ctypes.c_void_p()
+        if _HIP.hipEventCreateWithFlags(ctypes.byref(self.handle), 0x20000000) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self._hip.hipEventRecord(self.handle, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self.handle:
+            self._hip.hipEventDestroy(self.handle)
+
+
+def timing_event(torch):
+    return TimingEvent() if EVENT_FENCE == "none" else torch.cuda.Event(enable_timing=True)
+
+
 
 
 def evict_caches(flush, i):
@@ -165,7 +216,7 @@ def evict_caches(flush, i):
 def _cold_times(torch, stream, fn, reps, flush):
     """Durations of fn() (seconds), each bracketed by HIP events on `stream`
     with the caches flushed before it (evict_caches, outside the events)."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    ev = [(timing_event(torch), timing_event(torch)) for _ in range(reps)]
     for i, (a, b) in enumerate(ev):
         evict_caches(flush, i)
         a.record(stream)
@@ -283,7 +334,7 @@ def run_mixed(args, w, pk, torch, dev):
     prep = eng.prepare_fused([(s.slot, s.n) for s in st.segments], k_new, v_new, q, w.scale)
     meta = prep.meta
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [(timing_event(torch), timing_event(torch)) for _ in range(args.steps)]
     for _ in range(args.warmup):
         eng.run_prepared(prep)
     torch.cuda.synchronize()
@@ -301,7 +352,7 @@ def run_mixed(args, w, pk, torch, dev):
     # the same step with the caches flushed before each call (evict_caches,
     # outside the events)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    cold_ev = [(timing_event(torch), timing_event(torch)) for _ in range(10)]
     for i, (a_, b_) in enumerate(cold_ev):
         evict_caches(flush, i)
         a_.record(stream)
@@ -371,7 +422,7 @@ def cpu_baseline_step(w, step, repeats):
 def _event_time(torch, stream, fn, reps):
     """Mean duration of fn() over reps calls, each bracketed by HIP events on
     `stream` (seconds)."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    ev = [(timing_event(torch), timing_event(torch)) for _ in range(reps)]
     for a, b in ev:
         a.record(stream)
         fn()
@@ -646,9 +697,10 @@ def run_extras(pk, torch, dev, args):
 
 
 def main():
-    global FLUSH_KIND
+    global FLUSH_KIND, EVENT_FENCE
     args = parse_args()
     FLUSH_KIND = args.flush
+    EVENT_FENCE = args.event_fence
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
               "mode", file=sys.stderr)
@@ -714,7 +766,7 @@ def main():
     # Each step's GPU work (append + attention) bracketed by HIP events, in
     # as many further steps after the timed ones: an event record costs the
     # stream several microseconds, so the timed steps carry none.
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    step_ev = [(timing_event(torch), timing_event(torch))
                for _ in range(args.steps)]
     for i in range(args.steps):
         step_ev[i][0].record(stream)
@@ -740,7 +792,7 @@ def main():
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def replay(cold):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        ev = [(timing_event(torch), timing_event(torch)) for _ in range(reps)]
         for i, (a_, b_) in enumerate(ev):
             if cold:
                 evict_caches(flush, i)
@@ -788,7 +840,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("pkv decode_q8_kernel" if q8 else "pkv decode_mfma_kernel")
                      + " + reduce_kernel (one paged_attend launch)",
-                     "cold_flush": f"1 GiB {FLUSH_KIND} before each timed call"},
+                     "cold_flush": f"1 GiB {FLUSH_KIND} before each timed call",
+                     "timing_events": "HIP events without the system-scope fence" if EVENT_FENCE == "none"
+                     else "torch events (system-scope fence on record)"},
     }
     if not args.no_extras:
         line["extras"] = run_extras(pk, torch, dev, args)

@@ -77,6 +77,9 @@ def parse_args():
                     help="skip the chunk-kernel, mixed-step and append lines after the headline")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--sdpa-reference", action="store_true",
+                    help="only time torch's flash-attention backend on contiguous dense shapes like the "
+                         "prompt-chunk configs (context for the chunk kernel's TFLOP/s)")
     ap.add_argument("--ablation", choices=["gather", "prefix"], default=None,
                     help="gather: block-table decode vs gather-then-attend; prefix: adopted vs cold "
                          "shared-prefix step")
@@ -696,6 +699,39 @@ def run_extras(pk, torch, dev, args):
     return out
 
 
+def sdpa_reference(torch, dev, reps=20):
+    """torch's scaled_dot_product_attention, flash backend only (no fallback),
+    on contiguous bf16 Q, K, V with every query head's K/V expanded: dense
+    shapes like the prompt-chunk configs, and two causal ones.  Flops count
+    the visible pairs (4 D per pair per head); median of `reps` calls, each
+    bracketed by timing-only HIP events."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    shapes = [("dense 2048 x 8192, D 64 (config 4a's rows and keys)", 32, 2048, 8192, 64, False),
+              ("dense 512 x 8192, D 64 (config 4b)", 32, 512, 8192, 64, False),
+              ("dense 512 x 1536, D 128 (config 2)", 32, 512, 1536, 128, False),
+              ("causal 8192 x 8192, D 64", 32, 8192, 8192, 64, True),
+              ("causal 3000 x 3000, D 128, 40 heads (config 5 step 2's prompt)", 40, 3000, 3000, 128, True)]
+    stream = torch.cuda.current_stream()
+    out = {"kind": "torch SDPBackend.FLASH_ATTENTION on contiguous K/V (not paged)", "torch": torch.__version__}
+    for name, hq, lq, lk, d, causal in shapes:
+        g = torch.Generator(device=dev).manual_seed(1)
+        q, k, v = (torch.randn(1, hq, n, d, device=dev, dtype=torch.bfloat16, generator=g) for n in (lq, lk, lk))
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for _ in range(3):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+            ev = [(timing_event(torch), timing_event(torch)) for _ in range(reps)]
+            for a, b in ev:
+                a.record(stream)
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+                b.record(stream)
+            torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2] / 1e3
+        flops = 4 * d * hq * (lq * (lq + 1) // 2 if causal else lq * lk)
+        out[name] = {"ms": round(t * 1e3, 4), "tflops": round(flops / t / 1e12, 1),
+                     "frac_bf16_peak": round(flops / t / (BF16_PEAK_TFLOPS * 1e12), 4)}
+    return out
+
+
 def main():
     global FLUSH_KIND, EVENT_FENCE
     args = parse_args()
@@ -720,6 +756,9 @@ def main():
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if args.sdpa_reference:
+        print(json.dumps(sdpa_reference(torch, dev)), flush=True)
+        return
     if args.ablation == "gather":
         print(json.dumps(run_gather_ablation(args, pk, torch, dev)), flush=True)
         return

@@ -604,6 +604,36 @@ def test_random_mixed_steps(seed, gpu_available):
         assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
 
 
+@functools.lru_cache(maxsize=2)
+def _long_contexts(kind):
+    """Contexts past 32768 tokens, where a row has more than one wavefront's
+    worth (64) of 512-token partitions: decode rows at ~33K, 40K and 70K
+    (up to 137 partitions), a 3-row draft at 45K (verify path on bf16) and a
+    40-row chunk at 36K (16 key ranges on bf16); on an 8-bit pool all of
+    them run on the 8-bit decode kernel."""
+    seqs = [(0, 40000, 1), (1, 70000, 1), (2, 45000, 3), (3, 36000, 40), (4, 33000, 1)]
+    w = make_custom(seqs, dtype="bf16", hq=32, hkv=8, d=128, seed=77)
+    if kind == "q8":
+        w.kv_quant = "q8"
+    res, pools = run_workload(w)
+    return w, res, pools
+
+
+@pytest.mark.parametrize("kind,fused", [("bf16", False), ("bf16", True), ("q8", True)],
+                         ids=["bf16-separate", "bf16-mixed_step", "q8-mixed_step"])
+def test_long_contexts_past_64_partitions(kind, fused, gpu_available):
+    _log(f"long contexts {kind} fused={fused}")
+    w, res, pools = _long_contexts(kind)
+    eng, outs = _run_gpu(w, fused=fused)
+    _check_close(f"long contexts {kind}", outs[0][0], res[0]["out"], TOL["bf16"])
+    if kind == "q8":
+        _q8_pool_check(eng, pools)
+    else:
+        ok, ov = pools
+        assert np.array_equal(_pool_bits(eng.pool.k), _oracle_bits(ok))
+        assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
+
+
 def _many_segments(d, hq, hkv, seed):
     """100 segments, more than one wavefront holds: decode rows, then prompt
     chunks (cut into key ranges), then short drafts, then decode rows again,

@@ -99,6 +99,30 @@ def test_kv_append_skips_out_of_pool_entries_and_empty(gpu_available):
     assert set(map(tuple, changed[:, :3].tolist())) == {(0, 0, 5), (0, 1, 5)}
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+def test_empty_step_changes_nothing(fused, gpu_available):
+    """A step with no segments (nothing appended, nothing attended) returns
+    an empty output and leaves the pool bit for bit as it was."""
+    import torch
+    w = make_custom([(0, 20, 1), (1, 40, 1)], dtype="bf16", hq=4, hkv=2, d=64)
+    eng = make_engine(pk.PagedKVEngine, w)
+    place_history(eng, w)
+    torch.cuda.synchronize()
+    before_k, before_v = _pool_bits(eng.pool.k).copy(), _pool_bits(eng.pool.v).copy()
+    e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    if fused:
+        out, _ = eng.fused_step([], e, e, q, 0.125)
+    else:
+        meta = eng.lower([])
+        eng.append(meta, e, e)
+        out = eng.attend(meta, q, 0.125)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 4, 64)
+    assert np.array_equal(_pool_bits(eng.pool.k), before_k)
+    assert np.array_equal(_pool_bits(eng.pool.v), before_v)
+
+
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
 @pytest.mark.parametrize("name", ["1", "1+1", "3", "3v", "2", "4a", "4b", "5"])

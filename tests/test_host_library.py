@@ -89,6 +89,22 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
                                 None, 0, None) == pk.binding.PKV_ERR_WORKSPACE
 
 
+def test_empty_calls_return_ok_without_touching_the_device():
+    """An append of no tokens and an attention over no segments or no rows
+    succeed before any launch, with NULL pointers for the empty arrays."""
+    lib = pk.lib()
+    d = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, 1)
+    assert lib.pkv_kv_append(None, None, None, 0, ctypes.byref(d), None) == pk.binding.PKV_OK
+    # no segments
+    assert lib.pkv_paged_attend(None, 0, 4, None, None, None, 0, None, None, 1, 1, 0, 0, ctypes.byref(d), 0.125,
+                                None, 0, None, 0, None) == pk.binding.PKV_OK
+    # segments but no rows
+    assert lib.pkv_paged_attend(None, 0, 4, None, None, None, 3, None, None, 1, 1, 0, 0, ctypes.byref(d), 0.125,
+                                None, 0, None, 0, None) == pk.binding.PKV_OK
+    assert lib.pkv_paged_attend_noalloc(None, 0, 4, None, None, None, 0, None, None, 1, 1, 0, 0, ctypes.byref(d),
+                                        0.125, None, 0, None) == pk.binding.PKV_OK
+
+
 def test_workspace_sizing():
     d = pk.binding.PoolDesc(16, 16, 10, 16, 8, 128, 1)
     lib = pk.lib()

@@ -628,6 +628,31 @@ def test_random_mixed_steps(seed, gpu_available):
         assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+def test_pool_past_4gib_equals_small_pool_bitwise(fused, gpu_available):
+    """K and V tensors of more than 4 GiB each, with the step's blocks at the
+    top of the pool (the allocator hands them out from the end): tile
+    addresses no longer fit 32 bits, and the chunk kernel takes its 64-bit
+    form.  A prompt chunk, decode rows and a draft give the same bits as on
+    a small pool, and match the oracle."""
+    import copy
+    seqs = [(0, 3000, 200), (1, 2000, 1), (2, 1500, 3), (3, 5000, 1)]
+    w = make_custom(seqs, dtype="bf16", hq=32, hkv=8, d=128, seed=91)
+    _, small = _run_gpu(w, fused=fused)
+    per_block = w.num_kv_heads * 16 * w.head_dim * 2
+    wb = copy.copy(w)
+    wb.num_blocks = (1 << 32) // per_block + w.num_blocks + 64
+    assert wb.num_blocks * per_block > (1 << 32)
+    _log(f"pool past 4 GiB: {wb.num_blocks} blocks, {wb.num_blocks * per_block / 2**30:.2f} GiB per tensor")
+    order = np.arange(wb.num_blocks - 1, -1, -1, dtype=np.int32)
+    big, outs = _run_gpu(wb, fused=fused, free_order=order)
+    assert int(big.d_block_tables.max()) * per_block >= (1 << 32)   # tiles past 4 GiB are in use
+    assert np.array_equal(outs[0][0].cpu().numpy().view(np.int32), small[0][0].cpu().numpy().view(np.int32))
+    res, _ = run_workload(w)
+    _check_close("pool past 4 GiB", outs[0][0], res[0]["out"], TOL["bf16"])
+    del big, outs
+
+
 @functools.lru_cache(maxsize=2)
 def _long_contexts(kind):
     """Contexts past 32768 tokens, where a row has more than one wavefront's

@@ -376,7 +376,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   const int np = min(num_parts(si.L), a.part_max);
   const int rows = a.multirow ? si.n : 1;
   constexpr int DPL = D / kWave;
-  for (int i = 0; i < rows; ++i) {
+  // grid y spreads a multi-row segment's rows over workgroups
+  for (int i = blockIdx.y; i < rows; i += gridDim.y) {
     const int row = si.row0 + i;
     const int prow = a.multirow ? row : b;
     const int64_t base = (static_cast<int64_t>(prow) * a.num_q_heads + hq) * a.part_max;
@@ -467,12 +468,15 @@ int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t 
   if (st != PKV_OK || a.part_max <= 1 || !need_reduce ||
       (PKV_DECODE_WHOLE_CONTEXT && dtype == PKV_BF16 && !a.multirow && PKV_DECODE_MFMA))
     return st;
+  // x: (segment, query head); y: rows of multi-row segments (one each up to
+  // 65535, then strided)
   const unsigned grid = static_cast<unsigned>(a.num_segments) * static_cast<unsigned>(a.num_q_heads);
+  const unsigned grid_rows = a.multirow ? static_cast<unsigned>(std::min(std::max(a.max_query, 1), 65535)) : 1u;
   const size_t lds = static_cast<size_t>(a.part_max) * sizeof(float);
   if (head_dim == 128)
-    reduce_kernel<128><<<dim3(grid), dim3(kWave), lds, stream>>>(a);
+    reduce_kernel<128><<<dim3(grid, grid_rows), dim3(kWave), lds, stream>>>(a);
   else
-    reduce_kernel<64><<<dim3(grid), dim3(kWave), lds, stream>>>(a);
+    reduce_kernel<64><<<dim3(grid, grid_rows), dim3(kWave), lds, stream>>>(a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

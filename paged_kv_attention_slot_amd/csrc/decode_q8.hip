@@ -140,9 +140,12 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
       si = seg_info(a, b);
       if (!si.ok) continue;
     }
+    // A partition's column groups are consecutive units, so they run side
+    // by side on one XCD and share its L2 for the partition's tiles.
+    const int ngroups = q8_groups(si.n, G);
     const int np = q8_parts(si.L);
-    const int cg = rest / np;                          // column group
-    const int part = rest - cg * np;
+    const int part = rest / ngroups;
+    const int cg = rest - part * ngroups;              // column group
     // MFMA column l16 = (row, head) pair cg * 16 + l16 of the segment
     const int pair = cg * 16 + l16;
     const bool hv = pair < si.n * G;

@@ -77,16 +77,26 @@ def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str |
     return lib_path
 
 
-PROBE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "tile_read_probe.hip")
+PROBE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes")
+# Standalone measurement executables (not part of the library): the decode
+# access pattern's HBM read rate, and the softmax instructions' issue cost
+# beside the matrix cores.
+PROBES = ("tile_read_probe", "valu_mfma_cost_probe")
 
 
-def build_probe(out: str | None = None, verbose: bool = False) -> str:
-    """Compile the read-only tile probe (a standalone executable that times
-    the decode access pattern without arithmetic) and return its path."""
-    exe = out or os.path.join(BUILD_DIR, "tile_read_probe")
-    os.makedirs(os.path.dirname(exe), exist_ok=True)
-    _run([_hipcc(), *[f for f in HIP_FLAGS if f not in ("-fPIC", "-Wall")], "-o", exe, PROBE_SRC], verbose)
-    return exe
+def build_probe(out: str | None = None, verbose: bool = False, name: str | None = None) -> list[str]:
+    """Compile the probe executables (all of them, or `name`; `out` names the
+    executable when one is built) under the build directory and return their
+    paths."""
+    names = [name] if name else list(PROBES)
+    exes = []
+    for n in names:
+        exe = out if (out and len(names) == 1) else os.path.join(BUILD_DIR, n)
+        os.makedirs(os.path.dirname(exe), exist_ok=True)
+        _run([_hipcc(), *[f for f in HIP_FLAGS if f not in ("-fPIC", "-Wall")], "-o", exe,
+              os.path.join(PROBE_DIR, n + ".hip")], verbose)
+        exes.append(exe)
+    return exes
 
 
 if __name__ == "__main__":
@@ -96,9 +106,9 @@ if __name__ == "__main__":
     ap.add_argument("-D", dest="defines", action="append", default=[], help="NAME=VALUE tuning override")
     ap.add_argument("--out", default=None, help="write the library here instead of the package")
     ap.add_argument("--build-dir", default=None)
-    ap.add_argument("--probe", action="store_true", help="build only the tile read probe executable")
+    ap.add_argument("--probe", action="store_true", help="build only the probe executables")
     a = ap.parse_args()
     if a.probe:
-        print(build_probe(out=a.out, verbose=a.verbose))
+        print("\n".join(build_probe(out=a.out, verbose=a.verbose)))
     else:
         print(build(verbose=a.verbose, defines=a.defines, out=a.out, build_dir=a.build_dir))

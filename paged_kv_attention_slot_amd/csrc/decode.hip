@@ -171,6 +171,10 @@ __global__ __launch_bounds__(64) void decode_kernel(AttendArgs a) {
     const int part = a.multirow ? rest - i * np : rest;
     const int row = si.row0 + i;
     const int limit = si.L - si.n + i + 1;             // tokens visible to this row
+    // Partitions past the row's own position hold none of its keys: no item
+    // (a decode row sees all of its segment's partitions).
+    const int np_row = num_parts(limit);
+    if (part >= np_row) continue;
     const int tok0 = part * PT;
     const int tok1 = min(limit, tok0 + PT);
     const int hq0 = g * G;
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(64) void decode_kernel(AttendArgs a) {
       }
     }
 
-    const bool direct = (np == 1);
+    const bool direct = (np_row == 1);
     const int prow = a.multirow ? row : b;
     // A host bound smaller than the truth leaves no room for this partial.
     if (!direct && (a.part_acc == nullptr || part >= a.part_max)) continue;
@@ -373,12 +377,16 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   const SegInfo si = seg_info(a, b);
   if (!si.ok || (!a.multirow && si.n != 1)) return;
   if (a.part_acc == nullptr || num_parts(si.L) <= 1) return;
-  const int np = min(num_parts(si.L), a.part_max);
   const int rows = a.multirow ? si.n : 1;
   constexpr int DPL = D / kWave;
   // grid y spreads a multi-row segment's rows over workgroups
   for (int i = blockIdx.y; i < rows; i += gridDim.y) {
     const int row = si.row0 + i;
+    // Row i of the segment has partials for the partitions up to its own
+    // position (all of them for a decode row); one partition: written
+    // directly by the decode kernel.
+    const int np = min(num_parts(si.L - si.n + i + 1), a.part_max);
+    if (np <= 1) continue;
     const int prow = a.multirow ? row : b;
     const int64_t base = (static_cast<int64_t>(prow) * a.num_q_heads + hq) * a.part_max;
     const float *ml = a.part_ml + base * 2;

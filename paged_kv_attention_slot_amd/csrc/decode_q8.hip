@@ -143,7 +143,6 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     // A partition's column groups are consecutive units, so they run side
     // by side on one XCD and share its L2 for the partition's tiles.
     const int ngroups = q8_groups(si.n, G);
-    const int np = q8_parts(si.L);
     const int part = rest / ngroups;
     const int cg = rest - part * ngroups;              // column group
     // MFMA column l16 = (row, head) pair cg * 16 + l16 of the segment
@@ -161,6 +160,9 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     const int tok1 = min(si.L - si.n + ri_hi + 1, tok0 + PT);   // tok0 >= tok1: an empty partition
     const int tok_full = min(si.L - si.n + ri_lo + 1, tok1);    // every column sees keys below this
     const int lim = hv ? min(limit, tok1) : tok1;
+    // No column of the group reaches this partition: nothing to do (a
+    // column's row has partials only for the partitions up to its position).
+    if (tok0 >= tok1) continue;
     const int j0 = tok0 / kBlockTokens;
     const int nb = tok1 > tok0 ? (tok1 + kBlockTokens - 1) / kBlockTokens - j0 : 0;
 
@@ -375,7 +377,9 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
 #pragma unroll
     for (int dt = 0; dt < M::kDTiles; ++dt) o[dt] -= ct;
     if (!hv) continue;
-    const bool direct = (np == 1);
+    const int np_row = q8_parts(limit);               // partitions this column's row sees
+    if (part >= np_row) continue;
+    const bool direct = (np_row == 1);
     if (!direct && (a.part_acc == nullptr || part >= a.part_max)) continue;
     if (direct) {
       const float inv = 1.f / lt;

@@ -414,7 +414,8 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
       r = launch_verify(a, pool->head_dim, verify_ctx, need_merge, facts.known ? facts.max_verify_pairs : -1,
                         facts.known ? facts.verify_parts * pool->num_kv_heads : -1, st);
     if (r == PKV_OK && run_decode)
-      r = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves, st);
+      r = launch_decode(a, pool->dtype, pool->head_dim, decode_ctx, need_reduce, work_waves,
+                        facts.known ? facts.decode_rows : -1, st);
     return r;
   };
   if (run_chunk && (run_decode || run_verify) && facts.known && aux && PKV_CONCURRENT_DECODE) {

@@ -451,7 +451,7 @@ int dispatch_g(const AttendArgs &a, int G, int64_t items_bound, hipStream_t stre
 }  // namespace
 
 int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len, bool need_reduce,
-                  int64_t work_waves, hipStream_t stream) {
+                  int64_t work_waves, int32_t decode_rows, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
   const int64_t rows = a.multirow ? static_cast<int64_t>(a.total_q) : a.num_segments;
@@ -460,7 +460,7 @@ int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t 
   if (dtype == PKV_I8) {
     const int stages =
         work_waves >= 0 && work_waves < PKV_DECODE_FEW_WAVES ? PKV_DECODE_Q8_STAGES_FEW : PKV_DECODE_Q8_STAGES;
-    st = launch_decode_q8(a, head_dim, max_context_len, stages, stream);
+    st = launch_decode_q8(a, head_dim, max_context_len, stages, decode_rows, stream);
   } else if (dtype == PKV_BF16 && !a.multirow && PKV_DECODE_MFMA) {
     const int stages =
         work_waves >= 0 && work_waves < PKV_DECODE_FEW_WAVES ? PKV_DECODE_MFMA_STAGES_FEW : kDecodeMfmaStages;

@@ -11,7 +11,11 @@
 // row; for a multi-row segment (prompt chunk, drafts) up to 16 pairs of
 // consecutive rows per wavefront, each column with its own causal limit
 // (row i sees keys 0 .. L - n + i), so the codes are read once per column
-// group rather than once per row.
+// group rather than once per row.  Multi-row segments run PKV_DECODE_Q8_GROUP_W
+// column groups of one partition per workgroup, one per wavefront: a tile is
+// staged and its V codes converted once for all of them (two barriers per
+// tile), and each wavefront stops at its own rows' last key.  A row keeps
+// partials only for the partitions up to its own position.
 //   * the K and V code tiles (16 x head_dim bytes each) and their 2 x 16
 //     scales go from HBM straight into LDS staging (global_load_lds_dwordx4
 //     for codes, one global_load_lds_dword for the scales), S tiles in
@@ -46,6 +50,16 @@ typedef short shortx4_t __attribute__((ext_vector_type(4)));
 
 // fp16 value of the pattern 0x6400 | (code + 128).
 constexpr float kCodeBias = 1152.f;
+
+// Column groups per workgroup for multi-row segments, and their tiles in
+// flight (one wavefront issues a workgroup's loads).
+#ifndef PKV_DECODE_Q8_GROUP_W
+#define PKV_DECODE_Q8_GROUP_W 2
+#endif
+#ifndef PKV_DECODE_Q8_GROUP_STAGES
+#define PKV_DECODE_Q8_GROUP_STAGES 3
+#endif
+constexpr int kQ8GroupW = PKV_DECODE_Q8_GROUP_W;
 
 __device__ __forceinline__ unsigned q8_lds_addr(const unsigned char *p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)(p)));
@@ -92,32 +106,48 @@ __device__ __forceinline__ int q8_parts(int L) {
 // 16-wide MFMA column groups of a segment's (row, head) pairs.
 __device__ __forceinline__ int q8_groups(int n, int G) { return (n * G + 15) / 16; }
 
-// Work units of segment b: its column groups times its partitions (decode
-// rows: one group of G heads).  Without multi-row mode only decode rows
-// count.
-__device__ __forceinline__ int q8_units(const AttendArgs &a, int b, int G) {
-  const SegInfo s = seg_info(a, b);
-  if (!s.ok || (!a.multirow && s.n != 1)) return 0;
-  return q8_groups(s.n, G) * q8_parts(s.L);
+// Work units of a segment.  One wavefront per workgroup (W = 1): its column
+// groups times its partitions (a decode row: one group of its G heads), for
+// every segment the launch serves (decode rows; in multi-row mode every
+// segment, or with SINGLE only the decode rows).  W wavefronts per
+// workgroup (multi-row segments only): W consecutive column groups of one
+// partition per unit, so the partition's tiles are staged once for them.
+template <int W, bool SINGLE>
+__device__ __forceinline__ int q8_units(const SegInfo &s, bool multirow, int G) {
+  if constexpr (W == 1) {
+    if (!s.ok || (SINGLE ? s.n != 1 : (!multirow && s.n != 1))) return 0;
+    return q8_groups(s.n, G) * q8_parts(s.L);
+  } else {
+    if (!s.ok || !multirow || s.n < 2) return 0;
+    return (q8_groups(s.n, G) + W - 1) / W * q8_parts(s.L);
+  }
 }
 
-template <int D, int S>
-__global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(AttendArgs a, int G) {
+template <int D, int S, int W, bool SINGLE>
+__global__ __launch_bounds__(64 * W, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(AttendArgs a, int G) {
   using M = QGeo<D>;
   static_assert(S >= 1 && S <= 3, "1 to 3 tiles in flight");
+  static_assert(W == 1 || !SINGLE, "decode rows take one wavefront per workgroup");
   constexpr int PT = kDecodePartitionTokens;
   constexpr int kStage = 2 * M::kCodeTile + M::kScaleBytes;   // K codes | V codes | scales
+  // V code chunks (16 bytes) of a tile, and per lane: W = 1 converts them
+  // all, W > 1 spreads them over the workgroup's first wavefronts.
+  constexpr int kVChunks = M::kCodeTile / 16;
+  constexpr int kCPL = W == 1 ? M::kChunksPerLane : (kVChunks + kWave * W - 1) / (kWave * W);
   __shared__ __align__(16) unsigned char stg[S * kStage];
   __shared__ __align__(16) unsigned char vt[M::kTile];
-  const int lane = threadIdx.x;
+  const int lane = W == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x & (kWave - 1));
+  const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const bool loader = W == 1 || wave == 0;              // issues the tile loads
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
   const SegInfo mine = seg_info(a, lane);
-  const int u0 = mine.ok && (a.multirow || mine.n == 1) ? q8_groups(mine.n, G) * q8_parts(mine.L) : 0;
+  const int u0 = q8_units<W, SINGLE>(mine, a.multirow, G);
   const int incl0 = wave_inclusive_scan(u0);
   int total = __shfl(incl0, kWave - 1);
-  if (a.num_segments > kWave) total = count_units(a.num_segments, [&](int b) { return q8_units(a, b, G); });
+  if (a.num_segments > kWave)
+    total = count_units(a.num_segments, [&](int b) { return q8_units<W, SINGLE>(seg_info(a, b), a.multirow, G); });
   const int64_t items = static_cast<int64_t>(total) * a.num_kv_heads;
   const float c_log2 = a.scale_log2;
 
@@ -136,18 +166,30 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
       si.row0 = __builtin_amdgcn_readlane(mine.row0, b);
       si.ok = true;
     } else {
-      b = find_unit(a.num_segments, unit, [&](int bb) { return q8_units(a, bb, G); }, &rest);
+      b = find_unit(a.num_segments, unit, [&](int bb) { return q8_units<W, SINGLE>(seg_info(a, bb), a.multirow, G); },
+                    &rest);
       si = seg_info(a, b);
       if (!si.ok) continue;
     }
     // A partition's column groups are consecutive units, so they run side
     // by side on one XCD and share its L2 for the partition's tiles.
     const int ngroups = q8_groups(si.n, G);
-    const int part = rest / ngroups;
-    const int cg = rest - part * ngroups;              // column group
+    int part, cg, cg_last;                             // this wavefront's column group; the workgroup's last
+    if constexpr (W == 1) {
+      part = rest / ngroups;
+      cg = rest - part * ngroups;
+      cg_last = cg;
+    } else {
+      const int nblk = (ngroups + W - 1) / W;
+      part = rest / nblk;
+      const int cb = rest - part * nblk;
+      cg = cb * W + wave;
+      cg_last = min(cb * W + W - 1, ngroups - 1);
+    }
+    const bool wave_cols = W == 1 || cg < ngroups;     // the wavefront has a column group
     // MFMA column l16 = (row, head) pair cg * 16 + l16 of the segment
     const int pair = cg * 16 + l16;
-    const bool hv = pair < si.n * G;
+    const bool hv = wave_cols && pair < si.n * G;
     const int ri = hv ? pair / G : 0;
     const int hq = g * G + (hv ? pair - ri * G : 0);
     const int row = si.row0 + ri;
@@ -157,17 +199,21 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     const int ri_hi = min(si.n - 1, (cg * 16 + 15) / G);
     const int ri_lo = min(si.n - 1, (cg * 16) / G);
     const int tok0 = part * PT;
-    const int tok1 = min(si.L - si.n + ri_hi + 1, tok0 + PT);   // tok0 >= tok1: an empty partition
+    const int tok1 = wave_cols ? min(si.L - si.n + ri_hi + 1, tok0 + PT) : tok0;   // tok0 >= tok1: nothing here
     const int tok_full = min(si.L - si.n + ri_lo + 1, tok1);    // every column sees keys below this
     const int lim = hv ? min(limit, tok1) : tok1;
-    // No column of the group reaches this partition: nothing to do (a
-    // column's row has partials only for the partitions up to its position).
-    if (tok0 >= tok1) continue;
+    // Keys the workgroup stages: those its last column group sees.
+    int tok1_wg = tok1;
+    if constexpr (W > 1) tok1_wg = min(si.L - si.n + min(si.n - 1, (cg_last * 16 + 15) / G) + 1, tok0 + PT);
+    // No column reaches this partition: nothing to do (a column's row has
+    // partials only for the partitions up to its position).
+    if (tok0 >= tok1_wg) continue;
     const int j0 = tok0 / kBlockTokens;
-    const int nb = tok1 > tok0 ? (tok1 + kBlockTokens - 1) / kBlockTokens - j0 : 0;
+    const int nb = (tok1_wg + kBlockTokens - 1) / kBlockTokens - j0;               // tiles staged
+    const int nb_w = tok1 > tok0 ? (tok1 + kBlockTokens - 1) / kBlockTokens - j0 : 0;   // tiles this wavefront uses
 
     int phys_lane = 0;
-    if (lane < nb) {
+    if (loader && lane < nb) {
       phys_lane = a.block_tables[static_cast<int64_t>(si.slot) * a.max_blocks + j0 + lane];
       phys_lane = min(max(phys_lane, 0), a.num_blocks - 1);
     }
@@ -248,7 +294,7 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     // chunks (registers, for the fp16 V tile) and its four K and V scales
     // (tokens 4 lg .. + 3).  Reads only: once they have landed the stage can
     // be refilled.
-    auto read_stage = [&](int stage, halfx8_t (&ka)[M::kKSteps], uint4 (&vraw)[M::kChunksPerLane], floatx4_t &ks,
+    auto read_stage = [&](int stage, halfx8_t (&ka)[M::kKSteps], uint4 (&vraw)[kCPL], floatx4_t &ks,
                           floatx4_t &vs) {
       const unsigned char *st = stg + stage * kStage;
 #pragma unroll
@@ -259,18 +305,21 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
         ka[kk] = __builtin_bit_cast(halfx8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
       }
 #pragma unroll
-      for (int i = 0; i < M::kChunksPerLane; ++i)
-        vraw[i] = *reinterpret_cast<const uint4 *>(st + M::kCodeTile + (i * kWave + lane) * 16);
+      for (int i = 0; i < kCPL; ++i) {
+        const int P = (i * W + wave) * kWave + lane;
+        if (W == 1 || P < kVChunks) vraw[i] = *reinterpret_cast<const uint4 *>(st + M::kCodeTile + P * 16);
+      }
       ks = *reinterpret_cast<const floatx4_t *>(st + 2 * M::kCodeTile + lg * 16);
       vs = *reinterpret_cast<const floatx4_t *>(st + 2 * M::kCodeTile + 64 + lg * 16);
     };
     // The V code chunks -> the fp16 V tile in LDS (the transposed reads'
     // layout).  The wave's earlier reads of the previous tile are ordered
     // before these writes.
-    auto write_vt = [&](const uint4 (&vraw)[M::kChunksPerLane]) {
+    auto write_vt = [&](const uint4 (&vraw)[kCPL]) {
 #pragma unroll
-      for (int i = 0; i < M::kChunksPerLane; ++i) {
-        const int P = i * kWave + lane;
+      for (int i = 0; i < kCPL; ++i) {
+        const int P = (i * W + wave) * kWave + lane;
+        if (W > 1 && P >= kVChunks) continue;
         const int t = P / M::kCodeCPR;
         const int p = P - t * M::kCodeCPR;
         const uint4 w = vraw[i];
@@ -335,11 +384,16 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
     // S tiles in flight.  Past the last tile the prefetch re-reads the last
     // tile (a cache hit) so every wait below has a static count.  An empty
     // partition loads nothing and leaves m = -FLT_MAX, l = 0, O = 0.
-    if (nb > 0) {
+    if (nb > 0 && loader) {
       issue(0, 0);
       if constexpr (S > 1) issue(1, min(1, nb - 1));
       if constexpr (S > 2) issue(2, min(2, nb - 1));
     }
+    // W > 1: the loader waits for a tile, and a barrier hands it to every
+    // wavefront (which by then are done with the previous V tile); they read
+    // the stage and convert their share of the V codes; a second barrier
+    // marks the stage read and the V tile whole, and the loader refills the
+    // stage.  nb and the trip counts are uniform over the workgroup.
     for (int jj = 0; jj < nb; jj += S) {
 #pragma unroll
       for (int st = 0; st < S; ++st) {
@@ -348,20 +402,32 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
         if constexpr (S == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(M::kPerIssue) : "memory");
         if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * M::kPerIssue) : "memory");
+        if constexpr (W > 1) __syncthreads();
         halfx8_t ka[M::kKSteps];
-        uint4 vraw[M::kChunksPerLane];
+        uint4 vraw[kCPL];
         floatx4_t ks, vs;
         read_stage(st, ka, vraw, ks, vs);
-        // every read of the stage has completed: it can be refilled while
-        // the V tile is converted and the tile's arithmetic runs
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if constexpr (S > 1) issue(st, min(jj + st + S, nb - 1));
-        else if (jj + 1 < nb) issue(0, jj + 1);
-        write_vt(vraw);
-        if ((j0 + jj + st + 1) * kBlockTokens > tok_full)
-          compute(ka, ks, vs, jj + st, std::true_type{});
-        else
-          compute(ka, ks, vs, jj + st, std::false_type{});
+        if constexpr (W == 1) {
+          // every read of the stage has completed: it can be refilled while
+          // the V tile is converted and the tile's arithmetic runs
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if constexpr (S > 1) issue(st, min(jj + st + S, nb - 1));
+          else if (jj + 1 < nb) issue(0, jj + 1);
+          write_vt(vraw);
+        } else {
+          write_vt(vraw);
+          __syncthreads();
+          if (loader) {
+            if constexpr (S > 1) issue(st, min(jj + st + S, nb - 1));
+            else if (jj + 1 < nb) issue(0, jj + 1);
+          }
+        }
+        if (W == 1 || jj + st < nb_w) {
+          if ((j0 + jj + st + 1) * kBlockTokens > tok_full)
+            compute(ka, ks, vs, jj + st, std::true_type{});
+          else
+            compute(ka, ks, vs, jj + st, std::false_type{});
+        }
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -406,26 +472,51 @@ __global__ __launch_bounds__(64, PKV_DECODE_Q8_MIN_WAVES) void decode_q8_kernel(
   }
 }
 
-template <int D>
-int launch_q8_d(const AttendArgs &a, int G, int64_t grid, int stages, hipStream_t stream) {
-  const dim3 g(static_cast<unsigned>(grid)), b(kWave);
-  if (stages >= 3) decode_q8_kernel<D, 3><<<g, b, 0, stream>>>(a, G);
-  else if (stages == 2) decode_q8_kernel<D, 2><<<g, b, 0, stream>>>(a, G);
-  else decode_q8_kernel<D, 1><<<g, b, 0, stream>>>(a, G);
+template <int D, int W, bool SINGLE>
+int launch_q8_w(const AttendArgs &a, int G, int64_t grid, int stages, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>(grid)), b(kWave * W);
+  if (stages >= 3) decode_q8_kernel<D, 3, W, SINGLE><<<g, b, 0, stream>>>(a, G);
+  else if (stages == 2) decode_q8_kernel<D, 2, W, SINGLE><<<g, b, 0, stream>>>(a, G);
+  else decode_q8_kernel<D, 1, W, SINGLE><<<g, b, 0, stream>>>(a, G);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+template <int D>
+int launch_q8_d(const AttendArgs &a, int G, int64_t parts, int stages, int32_t decode_rows, hipStream_t stream) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * kDecodeWavesPerCU;
+  const int64_t hkv = a.num_kv_heads;
+  if (!a.multirow) {
+    const int64_t items_bound = static_cast<int64_t>(a.num_segments) * parts * hkv;
+    const int64_t grid = items_bound < cap ? items_bound : cap;
+    return grid > 0 ? launch_q8_w<D, 1, false>(a, G, grid, stages, stream) : PKV_OK;
+  }
+  // Multi-row mode: decode rows (unless the host knows there are none) one
+  // wavefront per item, multi-row segments kQ8GroupW column groups per
+  // workgroup.  Both write the same partials; one reduce follows.
+  int st = PKV_OK;
+  if (decode_rows != 0) {
+    const int64_t items_bound = static_cast<int64_t>(a.num_segments) * parts * hkv;
+    const int64_t grid = items_bound < cap ? items_bound : cap;
+    if (grid > 0) st = launch_q8_w<D, 1, true>(a, G, grid, stages, stream);
+  }
+  constexpr int W = kQ8GroupW;
+  const int64_t groups_bound = (static_cast<int64_t>(a.total_q) * G + 15) / 16 + a.num_segments;
+  const int64_t items_bound = ((groups_bound + W - 1) / W + a.num_segments) * parts * hkv;
+  const int64_t cap_w = cap / W > 0 ? cap / W : 1;
+  const int64_t grid = items_bound < cap_w ? items_bound : cap_w;
+  if (st == PKV_OK && grid > 0) st = launch_q8_w<D, W, false>(a, G, grid, PKV_DECODE_Q8_GROUP_STAGES, stream);
+  return st;
 }
 
 }  // namespace
 
-int launch_decode_q8(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages, hipStream_t stream) {
+int launch_decode_q8(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages, int32_t decode_rows,
+                     hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int64_t parts = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
-  const int64_t rows = a.multirow ? static_cast<int64_t>(a.total_q) : a.num_segments;
-  const int64_t items_bound = rows * (parts > 0 ? parts : 1) * a.num_kv_heads;
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * kDecodeWavesPerCU;
-  const int64_t grid = items_bound < cap ? items_bound : cap;
-  if (grid <= 0) return PKV_OK;
-  return head_dim == 128 ? launch_q8_d<128>(a, G, grid, stages, stream) : launch_q8_d<64>(a, G, grid, stages, stream);
+  int64_t parts = (static_cast<int64_t>(max_context_len) + kDecodePartitionTokens - 1) / kDecodePartitionTokens;
+  if (parts < 1) parts = 1;
+  return head_dim == 128 ? launch_q8_d<128>(a, G, parts, stages, decode_rows, stream)
+                         : launch_q8_d<64>(a, G, parts, stages, decode_rows, stream);
 }
 
 }  // namespace pkv

@@ -274,12 +274,16 @@ int launch_verify(const AttendArgs &a, int32_t head_dim, int32_t max_context_len
 // reduce.  `max_context_len` sizes the grid only.
 // `work_waves` is the launch's exact count of (row, KV head, partition)
 // items when the host knows it, else -1.
+// `decode_rows`: the count of query_len == 1 segments when the host knows
+// it, else -1.
 int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_context_len, bool need_reduce,
-                  int64_t work_waves, hipStream_t stream);
+                  int64_t work_waves, int32_t decode_rows, hipStream_t stream);
 
-// Decode rows over an 8-bit pool (codes + per-row scales).
+// Decode rows over an 8-bit pool (codes + per-row scales); in multi-row
+// mode also the multi-row segments.  `decode_rows`: the launch's count of
+// query_len == 1 segments when the host knows it, else -1.
 int launch_decode_q8(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
-                     hipStream_t stream);
+                     int32_t decode_rows, hipStream_t stream);
 int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
                        hipStream_t stream);
 

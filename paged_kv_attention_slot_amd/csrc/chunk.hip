@@ -37,6 +37,12 @@
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
+// Unmasked tiles four at a time (one turn of the 4-stage ring), so that each
+// tile's stage, and with it every LDS address of the tile, is a constant.
+#ifndef PKV_CHUNK_STATIC_STAGES
+#define PKV_CHUNK_STATIC_STAGES 1
+#endif
+
 namespace pkv {
 namespace {
 
@@ -255,12 +261,21 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   const char *kbase = static_cast<const char *>(a.k);
   const char *vbase = static_cast<const char *>(a.v);
   const int lane_row = lane / kCPR;
-  unsigned voff[kPer], col_off[kPer];
+  // voff: a tile's offsets within its block; toff: those of the tile that
+  // holds the sequence's last token (rows past it read the last token).
+  unsigned voff[kPer], toff[kPer];
+  {
+    const int rt_last = (L - 1) / T;
+    const int row0 = rt_last * T + wave * kR;
+    const int blk = static_cast<int>(static_cast<unsigned>(min(row0, L - 1)) / kBlockTokens);
 #pragma unroll
-  for (int x = 0; x < kPer; ++x) {
-    const int t = wave * kR + x * kRowsW + lane_row;              // row within the stage
-    col_off[x] = static_cast<unsigned>(ring_swz<D>(t, lane - lane_row * kCPR) * 16);
-    voff[x] = static_cast<unsigned>((t % kBlockTokens) * kRowBytes) + col_off[x];
+    for (int x = 0; x < kPer; ++x) {
+      const int t = wave * kR + x * kRowsW + lane_row;            // row within the stage
+      const unsigned col_off = static_cast<unsigned>(ring_swz<D>(t, lane - lane_row * kCPR) * 16);
+      voff[x] = static_cast<unsigned>((t % kBlockTokens) * kRowBytes) + col_off;
+      toff[x] = static_cast<unsigned>((min(row0 + x * kRowsW + lane_row, L - 1) - blk * kBlockTokens) * kRowBytes) +
+                col_off;
+    }
   }
   const int64_t head_off = static_cast<int64_t>(g) * kBlockBytes;
   const int64_t blk_stride = static_cast<int64_t>(hkv) * kBlockBytes;
@@ -281,15 +296,10 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   auto issue_loads = [&](int stage, int rt, int phys, auto stream_tag) {
     unsigned char *kd = lds + stage * 2 * kStageBytes;
     unsigned char *vd = kd + kStageBytes;
-    const bool tail = rt * T + T > L;                // uniform
-    const int row0 = rt * T + wave * kR;             // wavefront's first row
-    const int blk = static_cast<int>(static_cast<unsigned>(min(row0, L - 1)) / kBlockTokens);
+    const bool tail = rt * T + T > L;                // uniform; only the tile that holds token L - 1
 #pragma unroll
     for (int x = 0; x < kPer; ++x) {
-      unsigned off = voff[x];
-      if (tail)
-        off = static_cast<unsigned>((min(row0 + x * kRowsW + lane_row, L - 1) - blk * kBlockTokens) * kRowBytes) +
-              col_off[x];
+      unsigned off = tail ? toff[x] : voff[x];
       const unsigned dst = lds_addr32(kd) + (wave * kR + x * kRowsW) * kRowBytes;
       const unsigned dstv = lds_addr32(vd) + (wave * kR + x * kRowsW) * kRowBytes;
       const char *gk, *gv;
@@ -474,14 +484,18 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     int ph_next = lookup(min(pass0 + S - 1, pass1 - 1));
 
     // One iteration: tile rt's scores are in `cur`, tile rt + 1's go to `nxt`.
-    auto iter = [&](int rt, floatx16_t(&cur)[kTT], floatx16_t(&nxt)[kTT], auto masked_next) {
-      const int st = static_cast<int>(static_cast<unsigned>(rt - pass0) % S);
-      const int st_next = static_cast<int>(static_cast<unsigned>(rt + 1 - pass0) % S);
+    // `stage_tag`: tile rt's ring stage when known at compile time (the LDS
+    // addresses then fold into the instructions' offsets), else -1.
+    auto iter = [&](int rt, floatx16_t(&cur)[kTT], floatx16_t(&nxt)[kTT], auto masked_next, auto stage_tag) {
+      constexpr int kSt = decltype(stage_tag)::value;
+      const int st = kSt >= 0 ? kSt : static_cast<int>(static_cast<unsigned>(rt - pass0) % S);
+      const int st_next = kSt >= 0 ? (kSt + 1) % S : static_cast<int>(static_cast<unsigned>(rt + 1 - pass0) % S);
+      const int st_fill = kSt >= 0 ? (kSt + S - 1) % S : static_cast<int>(static_cast<unsigned>(rt - pass0 + S - 1) % S);
       // Tile rt + 1 has landed (at most S - 3 newer tiles outstanding); past
       // the barrier every wave is done with tile rt - 1, whose stage refills.
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 3)) : "memory");
       __syncthreads();
-      issue_ph(static_cast<int>(static_cast<unsigned>(rt - pass0 + S - 1) % S), min(rt + S - 1, pass1 - 1), ph_next);
+      issue_ph(st_fill, min(rt + S - 1, pass1 - 1), ph_next);
       rescale(mnew, raise);
       bf16x8_t pb[kPS];
       bf16x8_t va[kDT][kPS];
@@ -502,19 +516,29 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     // and every wave runs pass1 - pass0 of them.
     const int unmasked_end = wave_pos0 >= 0 ? (wave_pos0 + 1) / T : 0;
     const int split_at = max(pass0, min(pass1, unmasked_end - 1));
+    using dyn = std::integral_constant<int, -1>;
     int rt = pass0;
+    if constexpr (PKV_CHUNK_STATIC_STAGES && S == 4) {
+      // a whole turn of the ring per trip: every stage index is a constant
+      for (; rt + 3 < split_at; rt += 4) {
+        iter(rt, s0, s1, std::false_type{}, std::integral_constant<int, 0>{});
+        iter(rt + 1, s1, s0, std::false_type{}, std::integral_constant<int, 1>{});
+        iter(rt + 2, s0, s1, std::false_type{}, std::integral_constant<int, 2>{});
+        iter(rt + 3, s1, s0, std::false_type{}, std::integral_constant<int, 3>{});
+      }
+    }
     for (; rt + 1 < split_at; rt += 2) {
-      iter(rt, s0, s1, std::false_type{});
-      iter(rt + 1, s1, s0, std::false_type{});
+      iter(rt, s0, s1, std::false_type{}, dyn{});
+      iter(rt + 1, s1, s0, std::false_type{}, dyn{});
     }
     if (rt < split_at) {
-      iter(rt, s0, s1, std::false_type{});
+      iter(rt, s0, s1, std::false_type{}, dyn{});
 #pragma unroll
       for (int tt = 0; tt < kTT; ++tt) s0[tt] = s1[tt];
       ++rt;
     }
     for (; rt < pass1; ++rt) {
-      iter(rt, s0, s1, std::true_type{});
+      iter(rt, s0, s1, std::true_type{}, dyn{});
 #pragma unroll
       for (int tt = 0; tt < kTT; ++tt) s0[tt] = s1[tt];
     }

@@ -315,6 +315,47 @@ def test_chunk_batch_composition_invariance_bitwise(gpu_available):
     assert torch.equal(a[17:317], b[0:300]) and torch.equal(a[0:16], b[300:316])
 
 
+@pytest.mark.parametrize("kind", ["f32", "q8"])
+def test_decode_path_multirow_composition_invariance_bitwise(kind, gpu_available):
+    """Multi-row segments that take the decode path (fp32 and 8-bit pools)
+    give the same bits whatever else shares the step, and match the oracle.
+    Their rows straddle a partition edge (512), so some rows are written
+    directly and others merged from per-row partials; on the 8-bit pool the
+    column groups share workgroups (one segment has an odd number of them)
+    while the decode rows take a launch of their own."""
+    import torch
+    if kind == "f32":
+        base = [(0, 505, 12), (1, 50, 1), (2, 1000, 7), (3, 2000, 1)]
+        rows = {0: slice(0, 12), 2: slice(13, 20)}
+        hq, hkv, d = 8, 2, 64
+    else:
+        base = [(0, 480, 40), (1, 50, 1), (2, 1000, 23), (3, 2000, 1)]
+        rows = {0: slice(0, 40), 2: slice(41, 64)}
+        hq, hkv, d = 40, 8, 128
+
+    def build():
+        w = make_custom(base, dtype="f32" if kind == "f32" else "bf16", hq=hq, hkv=hkv, d=d, seed=83)
+        if kind == "q8":
+            w.kv_quant = "q8"
+        return w
+
+    w1 = build()
+    _, o1 = _run_gpu(w1)
+    res, _ = run_workload(w1)
+    _check_close(f"decode-path multi-row {kind}", o1[0][0], res[0]["out"], TOL["f32"] if kind == "f32" else TOL["bf16"])
+    w2 = build()
+    st = w2.steps[0]
+    keep = [2, 0]
+    st.segments = [st.segments[i] for i in keep]
+    st.q = np.concatenate([st.q[rows[i]] for i in keep])
+    st.k_new = np.concatenate([st.k_new[rows[i]] for i in keep])
+    st.v_new = np.concatenate([st.v_new[rows[i]] for i in keep])
+    _, o2 = _run_gpu(w2)
+    a, b = o1[0][0].cpu(), o2[0][0].cpu()
+    n2 = rows[2].stop - rows[2].start
+    assert torch.equal(a[rows[2]], b[0:n2]) and torch.equal(a[rows[0]], b[n2:n2 + rows[0].stop - rows[0].start])
+
+
 def test_block_permutation_invariance_bitwise(gpu_available):
     import torch
     w = make_custom([(0, 900, 1), (1, 40, 1), (2, 1500, 1)], dtype="bf16", hq=32, hkv=8, d=128, seed=71)
@@ -713,6 +754,21 @@ def test_many_segments_beyond_one_wavefront(d, hq, hkv, fused, gpu_available):
     _check_close(f"100 segments D{d}", outs[0][0], res[0]["out"], TOL["bf16"])
     assert np.array_equal(_pool_bits(eng.pool.k), _oracle_bits(ok))
     assert np.array_equal(_pool_bits(eng.pool.v), _oracle_bits(ov))
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
+def test_many_segments_beyond_one_wavefront_q8(fused, gpu_available):
+    """The same 100-segment step over an 8-bit pool: the multi-row segments
+    take the workgroup form of the 8-bit decode kernel and the decode rows
+    the one-wavefront form, both finding their units past the first 64
+    segments."""
+    _log(f"100 segments q8 fused={fused}")
+    w = _many_segments(128, 40, 8, seed=4343)
+    w.kv_quant = "q8"
+    eng, outs = _run_gpu(w, fused=fused)
+    res, pools = run_workload(w)
+    _check_close("100 segments q8", outs[0][0], res[0]["out"], TOL["bf16"])
+    _q8_pool_check(eng, pools)
 
 
 @pytest.mark.parametrize("name", ["1", "2", "3", "3v", "4a", "4b", "5", "3q", "5q", "prefix"])

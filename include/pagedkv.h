@@ -259,8 +259,10 @@ int pkv_paged_attend_noalloc(const void *q_packed, int32_t total_q, int32_t num_
  *                 makes `stream` wait on that, so all of the step's work is
  *                 still ordered before later work on `stream`.  The choice
  *                 changes no result bit.  Calls that share these objects must
- *                 not run concurrently from several host threads.  NULL: one
- *                 stream.
+ *                 not run concurrently from several host threads.  The events
+ *                 only order the two streams; they may be created with
+ *                 hipEventDisableSystemFence, which spares each record a
+ *                 system-scope cache writeback.  NULL: one stream.
  * Other arguments as for pkv_kv_append and pkv_paged_attend; same status codes.
  * Argument errors (a bad scale included) are returned before anything is
  * appended. */

@@ -166,6 +166,39 @@ def current_stream_handle(device=None):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+_HIP_RT = None
+
+
+class StreamEvent:
+    """A HIP event for ordering one stream after another on the same GPU:
+    created with hipEventDisableTiming | hipEventDisableSystemFence, so a
+    record takes no system-scope cache writeback and invalidate (the device
+    work that waits on it still follows the recorded work, and sees its
+    writes).  Not for host-side waits on the work it records.  Made on the
+    HIP runtime PyTorch loaded, so torch stream handles apply."""
+
+    _FLAGS = 0x2 | 0x20000000   # hipEventDisableTiming | hipEventDisableSystemFence
+
+    def __init__(self):
+        global _HIP_RT
+        if _HIP_RT is None:
+            _torch().cuda.init()
+            path = [ln.split()[-1] for ln in open("/proc/self/maps").read().splitlines()
+                    if "libamdhip64" in ln][0]
+            rt = ctypes.CDLL(path)
+            rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_p), ctypes.c_uint]
+            rt.hipEventDestroy.argtypes = [_p]
+            _HIP_RT = rt
+        self._rt = _HIP_RT
+        self.handle = _p()
+        if self._rt.hipEventCreateWithFlags(ctypes.byref(self.handle), self._FLAGS) != 0:
+            raise PagedKVError("hipEventCreateWithFlags failed")
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self._rt.hipEventDestroy(self.handle)
+
+
 def _dptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 

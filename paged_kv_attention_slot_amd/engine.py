@@ -167,17 +167,18 @@ class PagedKVEngine:
     def _aux_handles(self):
         """Handles of the second stream (default priority) and the two events
         that pkv_mixed_step uses to run a step's decode and draft kernels
-        beside its chunk kernels.  Created once per engine; recording each
-        event once makes torch create it."""
+        beside its chunk kernels.  Created once per engine.  The events only
+        order the two streams on this GPU, so they are made without the
+        system-scope fence a default event record pays (a cache writeback
+        of the whole device between the append and the attention kernels)."""
         if self._aux is None:
             torch = self.torch
-            s = torch.cuda.Stream(device=self.device)
-            fork, join = torch.cuda.Event(), torch.cuda.Event()
-            fork.record(s)
-            join.record(s)
+            with torch.cuda.device(self.device):
+                s = torch.cuda.Stream(device=self.device)
+                fork, join = B.StreamEvent(), B.StreamEvent()
             self._aux = (s, fork, join)
         s, fork, join = self._aux
-        return s.cuda_stream, fork.cuda_event, join.cuda_event
+        return s.cuda_stream, fork.handle.value, join.handle.value
 
     def _lower_host(self, entries):
         """Lower the step into the next pinned staging buffer (host only)."""

@@ -74,8 +74,9 @@ WorkspaceLayout workspace_layout(int32_t num_segments, int32_t total_q, int32_t 
                                         static_cast<int64_t>(total_q) * group * max_splits);
       w.chunk_bytes = align256(static_cast<size_t>(kv_heads * w.chunk_slots) * (head_dim + 4) * sizeof(float));
     }
-    // Partition partials of the rows of verify segments (see verify.hip).
-    if (w.part_max > 1) {
+    // Partition partials of the rows of verify segments (see verify.hip;
+    // bf16 pools only).
+    if (w.part_max > 1 && dtype == PKV_BF16) {
       w.verify_rows = std::min<int64_t>(total_q, multi_segs * verify_rows_cap(group, head_dim));
       const int64_t n = w.verify_rows * num_q_heads * w.part_max;
       w.vacc_bytes = align256(static_cast<size_t>(n) * head_dim * sizeof(float));
@@ -299,7 +300,7 @@ int pkv_mixed_step(const pkv_step_desc *d, const pkv_pool *pool, void *stream) {
       }
     } else if (hq[b] > 1) {
       const int32_t G = d->num_q_heads / pool->num_kv_heads;
-      if (verify_segment(hq[b], G, pool->head_dim)) {
+      if (pool->dtype == PKV_BF16 && verify_segment(hq[b], G, pool->head_dim)) {
         ++f.verify_segments;
         if (hq[b] * G > f.max_verify_pairs) f.max_verify_pairs = hq[b] * G;
         if (hs[b] >= 0 && hs[b] < d->num_slots) {
@@ -401,7 +402,8 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
   // stream, the HBM-bound kernels run on it beside the chunk kernels.
   const bool multi = max_query_len > 1 && !multirow;
   const bool run_chunk = multi && (!facts.known || facts.chunk_segments > 0);
-  const bool run_verify = multi && (!facts.known || facts.verify_segments > 0);
+  // (the verify kernel reads bf16 pools; other pools' short segments take the chunk kernel)
+  const bool run_verify = multi && pool->dtype == PKV_BF16 && (!facts.known || facts.verify_segments > 0);
   const bool run_decode = !facts.known || multirow || facts.decode_rows > 0;
   const int32_t decode_ctx = facts.known && !multirow ? facts.max_decode_context : max_context_len;
   const bool need_reduce = decode_ctx > kDecodePartitionTokens;
@@ -425,12 +427,13 @@ int attend(const void *q_packed, int32_t total_q, int32_t num_q_heads, const int
     // the join is recorded even after a failed launch, so `s` never waits
     // on a stale event
     if (hipEventRecord(aux->join, aux->stream) != hipSuccess) return PKV_ERR_HIP;
-    const int sc = launch_chunk(a, pool->head_dim, max_query_len, max_context_len, facts.chunk_split > 0, s);
+    const int sc =
+        launch_chunk(a, pool->dtype, pool->head_dim, max_query_len, max_context_len, facts.chunk_split > 0, s);
     if (hipStreamWaitEvent(s, aux->join, 0) != hipSuccess) return PKV_ERR_HIP;
     return sd != PKV_OK ? sd : sc;
   }
   if (run_chunk) {
-    const int st = launch_chunk(a, pool->head_dim, max_query_len, max_context_len,
+    const int st = launch_chunk(a, pool->dtype, pool->head_dim, max_query_len, max_context_len,
                                 !facts.known || facts.chunk_split > 0, s);
     if (st != PKV_OK) return st;
   }

@@ -295,7 +295,7 @@ bool chunk_supported(int32_t dtype, int32_t head_dim, int32_t group);
 // ranges (whose partials the merge launch combines).  need_merge false
 // skips that launch: the caller knows that no segment of the step is cut.
 bool chunk_segment_splits(int32_t n, int32_t L, int32_t G, int32_t head_dim);
-int launch_chunk(const AttendArgs &a, int32_t head_dim, int32_t max_query_len, int32_t max_context_len,
+int launch_chunk(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t max_query_len, int32_t max_context_len,
                  bool need_merge, hipStream_t stream);
 
 int device_cu_count();

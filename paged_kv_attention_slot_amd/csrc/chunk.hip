@@ -1,4 +1,6 @@
-// Multi-row segments (prompt chunks, speculative drafts) on bf16 MFMA tiles.
+// Multi-row segments (prompt chunks, speculative drafts) on MFMA tiles: bf16
+// pools directly, 8-bit pools through fp16 tiles converted in LDS (the
+// "8-bit pools" section below).
 //
 // "Continuous batching: Qwen3.8-27B at 301 tok/s ..." (lucebox blog):
 // §Chunked prefill is a slot phase - a prompt advances by a bounded chunk

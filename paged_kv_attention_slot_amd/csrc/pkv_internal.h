@@ -280,14 +280,15 @@ int launch_decode(const AttendArgs &a, int32_t dtype, int32_t head_dim, int32_t 
                   int64_t work_waves, int32_t decode_rows, hipStream_t stream);
 
 // Decode rows over an 8-bit pool (codes + per-row scales); in multi-row
-// mode also the multi-row segments.  `decode_rows`: the launch's count of
+// mode also the multi-row segments that the chunk kernel does not take.  `decode_rows`: the launch's count of
 // query_len == 1 segments when the host knows it, else -1.
 int launch_decode_q8(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
                      int32_t decode_rows, hipStream_t stream);
 int launch_decode_mfma(const AttendArgs &a, int32_t head_dim, int32_t max_context_len, int stages,
                        hipStream_t stream);
 
-// Multi-row segments (query_len > 1) on bf16 MFMA tiles.  chunk_supported()
+// Multi-row segments (query_len > 1) on MFMA tiles (bf16 pools, and 8-bit
+// pools through fp16 tiles converted in LDS).  chunk_supported()
 // tells whether this shape is built; otherwise multi-row segments take the
 // decode path row by row.
 bool chunk_supported(int32_t dtype, int32_t head_dim, int32_t group);

@@ -317,12 +317,13 @@ def test_chunk_batch_composition_invariance_bitwise(gpu_available):
 
 @pytest.mark.parametrize("kind", ["f32", "q8"])
 def test_decode_path_multirow_composition_invariance_bitwise(kind, gpu_available):
-    """Multi-row segments that take the decode path (fp32 and 8-bit pools)
-    give the same bits whatever else shares the step, and match the oracle.
-    Their rows straddle a partition edge (512), so some rows are written
-    directly and others merged from per-row partials; on the 8-bit pool the
-    column groups share workgroups (one segment has an odd number of them)
-    while the decode rows take a launch of their own."""
+    """Multi-row segments of fp32 and 8-bit pools give the same bits
+    whatever else shares the step, and match the oracle.  On the fp32 pool
+    they take the decode path and their rows straddle a partition edge
+    (512), so some rows are written directly and others merged from per-row
+    partials; on the 8-bit pool they take the chunk kernel's 8-bit form
+    (200 and 115 (row, head) pairs: two row tiles and one, the second tile
+    partly empty) while the decode rows take the 8-bit decode kernel."""
     import torch
     if kind == "f32":
         base = [(0, 505, 12), (1, 50, 1), (2, 1000, 7), (3, 2000, 1)]

@@ -51,6 +51,15 @@
 #define PKV_CHUNK_STATIC_STAGES 1
 #endif
 
+// K and V of a tile refilled at different iterations: a tile's K is read one
+// iteration before its V (the next tile's scores are formed while the current
+// tile's weights are), so its K slot frees an iteration earlier.  Refilling
+// each slot as soon as it frees loads K one tile further ahead with the same
+// LDS (0: both slots of a stage refilled together).
+#ifndef PKV_CHUNK_SPLIT_RING
+#define PKV_CHUNK_SPLIT_RING 0
+#endif
+
 namespace pkv {
 namespace {
 
@@ -302,7 +311,9 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
   };
   // One tile's loads, with or without the streaming hint (a compile-time
   // string in the instruction): the choice is one uniform branch per tile.
-  auto issue_loads = [&](int stage, int rt, int phys, auto stream_tag) {
+  // `parts`: 1 = K only, 2 = V only, 3 = both.
+  auto issue_loads = [&](int stage, int rt, int phys, auto stream_tag, auto parts) {
+    constexpr int kParts = decltype(parts)::value;
     unsigned char *kd = lds + stage * 2 * kStageBytes;
     unsigned char *vd = kd + kStageBytes;
     const bool tail = rt * T + T > L;                // uniform; only the tile that holds token L - 1
@@ -322,19 +333,26 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
         gv = vbase + boff;
       }
       if constexpr (decltype(stream_tag)::value) {
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(dst), "v"(off), "s"(gk) : "memory");
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(dstv), "v"(off), "s"(gv) : "memory");
+        if constexpr (kParts & 1)
+          asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(dst), "v"(off), "s"(gk) : "memory");
+        if constexpr (kParts & 2)
+          asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(dstv), "v"(off), "s"(gv) : "memory");
       } else {
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(gk) : "memory");
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dstv), "v"(off), "s"(gv) : "memory");
+        if constexpr (kParts & 1)
+          asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(gk) : "memory");
+        if constexpr (kParts & 2)
+          asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dstv), "v"(off), "s"(gv) : "memory");
       }
     }
   };
-  auto issue_ph = [&](int stage, int rt, int phys) {
-    if (stream_tiles) issue_loads(stage, rt, phys, std::true_type{});
-    else issue_loads(stage, rt, phys, std::false_type{});
+  using kOnlyK = std::integral_constant<int, 1>;
+  using kOnlyV = std::integral_constant<int, 2>;
+  using kBoth = std::integral_constant<int, 3>;
+  auto issue_ph = [&](int stage, int rt, int phys, auto parts) {
+    if (stream_tiles) issue_loads(stage, rt, phys, std::true_type{}, parts);
+    else issue_loads(stage, rt, phys, std::false_type{}, parts);
   };
-  auto issue = [&](int stage, int rt) { issue_ph(stage, rt, lookup(rt)); };
+  auto issue = [&](int stage, int rt, auto parts) { issue_ph(stage, rt, lookup(rt), parts); };
   const int last_blk = (L - 1) / kBlockTokens;
   constexpr int kPassTiles = kTableWindow * kBlockTokens / T;
   static_assert(S >= 3, "V of tile t and K of tile t + 1 are resident together");
@@ -481,16 +499,33 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
     // Tile t of the pass sits in stage (t - pass0) % S.  Every iteration
     // issues exactly one tile's loads (the last ones repeat the final tile),
     // so "tile t has landed" is "at most k newer tiles are outstanding".
+    // Split ring: K of tiles pass0 .. pass0 + S - 1 and V of pass0 .. pass0
+    // + S - 2, issued as [K(p0)], then [K(p0 + i), V(p0 + i - 1)] per i, the
+    // grouping of the iterations' own loads.
+    if constexpr (PKV_CHUNK_SPLIT_RING) {
+      issue(0, pass0, kOnlyK{});
 #pragma unroll
-    for (int i = 0; i < S - 1; ++i) issue(i, min(pass0 + i, pass1 - 1));
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 2)) : "memory");
+      for (int i = 1; i < S; ++i) {
+        issue(i, min(pass0 + i, pass1 - 1), kOnlyK{});
+        issue(i - 1, min(pass0 + i - 1, pass1 - 1), kOnlyV{});
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 1)) : "memory");
+    } else {
+#pragma unroll
+      for (int i = 0; i < S - 1; ++i) issue(i, min(pass0 + i, pass1 - 1), kBoth{});
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 2)) : "memory");
+    }
     __syncthreads();
     floatx16_t s0[kTT], s1[kTT];
     float mnew;
     qk(0, s0);
     mask(pass0, s0);
     bool raise = rowmax(s0, mnew);
-    int ph_next = lookup(min(pass0 + S - 1, pass1 - 1));
+    // Block of the next iteration's K refill (tile rt + S with the split
+    // ring, rt + S - 1 otherwise) and of its V refill (tile rt + S - 1: the
+    // K refill of the iteration before).
+    int ph_next = lookup(min(pass0 + (PKV_CHUNK_SPLIT_RING ? S : S - 1), pass1 - 1));
+    int ph_v = PKV_CHUNK_SPLIT_RING ? lookup(min(pass0 + S - 1, pass1 - 1)) : 0;
 
     // One iteration: tile rt's scores are in `cur`, tile rt + 1's go to `nxt`.
     // `stage_tag`: tile rt's ring stage when known at compile time (the LDS
@@ -502,9 +537,20 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
       const int st_fill = kSt >= 0 ? (kSt + S - 1) % S : static_cast<int>(static_cast<unsigned>(rt - pass0 + S - 1) % S);
       // Tile rt + 1 has landed (at most S - 3 newer tiles outstanding); past
       // the barrier every wave is done with tile rt - 1, whose stage refills.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 3)) : "memory");
-      __syncthreads();
-      issue_ph(st_fill, min(rt + S - 1, pass1 - 1), ph_next);
+      // Split ring: K of tile rt + 1 and V of tile rt were issued S - 1
+      // iterations ago (S - 2 newer groups outstanding); past the barrier
+      // every wave is done with K of tile rt (its slot takes K of rt + S) and
+      // with V of tile rt - 1 (its slot takes V of rt + S - 1).
+      if constexpr (PKV_CHUNK_SPLIT_RING) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 2)) : "memory");
+        __syncthreads();
+        issue_ph(st, min(rt + S, pass1 - 1), ph_next, kOnlyK{});
+        issue_ph(st_fill, min(rt + S - 1, pass1 - 1), ph_v, kOnlyV{});
+      } else {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer * (S - 3)) : "memory");
+        __syncthreads();
+        issue_ph(st_fill, min(rt + S - 1, pass1 - 1), ph_next, kBoth{});
+      }
       rescale(mnew, raise);
       // A wavefront whose M-rows all lie past the segment only loads its
       // share of the tiles.
@@ -520,7 +566,12 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
         // tile rt + 1.
         raise = phase_b(pb, va, st, nxt, mnew) && rt + 1 < pass1;
       }
-      ph_next = lookup(min(rt + S, pass1 - 1));
+      if constexpr (PKV_CHUNK_SPLIT_RING) {
+        ph_v = ph_next;
+        ph_next = lookup(min(rt + 1 + S, pass1 - 1));
+      } else {
+        ph_next = lookup(min(rt + S, pass1 - 1));
+      }
     };
     // Tiles before `unmasked_end` need no causal mask for any row of this
     // wave.  Iterations whose next tile is among them run branch-free, two at

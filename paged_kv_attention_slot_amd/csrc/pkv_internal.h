@@ -130,11 +130,17 @@ constexpr int kDecodeMfmaStages = PKV_DECODE_MFMA_STAGES;
 #define PKV_VERIFY_MAX_PAIRS 1024
 #endif
 constexpr int kVerifyPartitionTokens = PKV_DECODE_PARTITION_TOKENS;
+// Column groups (wavefronts streaming the same partition) a verify segment
+// may take.
+#ifndef PKV_VERIFY_GROUPS
+#define PKV_VERIFY_GROUPS 1
+#endif
 // 16-wide (row, head) pair tiles per verify wavefront (register budget).
 __host__ __device__ constexpr int verify_col_tiles(int head_dim) { return head_dim == 64 ? 3 : 2; }
 __host__ __device__ constexpr int verify_max_pairs(int head_dim) {
-  return verify_col_tiles(head_dim) * 16 < PKV_VERIFY_MAX_PAIRS ? verify_col_tiles(head_dim) * 16
-                                                                 : PKV_VERIFY_MAX_PAIRS;
+  return verify_col_tiles(head_dim) * 16 * PKV_VERIFY_GROUPS < PKV_VERIFY_MAX_PAIRS
+             ? verify_col_tiles(head_dim) * 16 * PKV_VERIFY_GROUPS
+             : PKV_VERIFY_MAX_PAIRS;
 }
 __host__ __device__ constexpr bool verify_segment(int n, int G, int head_dim) {
   return n > 1 && n * G <= verify_max_pairs(head_dim);

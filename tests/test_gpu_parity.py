@@ -240,7 +240,9 @@ def test_bf16_output(name, gpu_available):
         want = r["out"]
         half_ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 9)
         err = np.abs(got - want)
-        _log(f"config {name} step {i} bf16: max-abs {err.max():.3e}")
+        err32 = np.abs(a.float().cpu().numpy().astype(np.float64) - want)
+        _log(f"config {name} step {i}: fp32 max-abs {err32.max():.3e} mean-abs {err32.mean():.3e}; "
+             f"bf16 max-abs {err.max():.3e}")
         assert (err <= 1e-2 + half_ulp).all(), f"step {i}: max-abs {err.max()}"
 
 

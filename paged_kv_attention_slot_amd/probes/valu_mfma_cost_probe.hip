@@ -17,6 +17,10 @@
 // Kinds: fma (v_fma_f32), exp (v_exp_f32), pack (v_cvt_pk_bf16_f32),
 // max3 (v_maximum3_f32), dot2 (v_dot2_f32_bf16 against (1, 1)), and
 // fma+exp (alternating).
+// "(agpr)" lines: the same MFMAs written in assembly with their
+// accumulators in AGPRs (the compiler's form keeps them in VGPRs); four
+// s_nop 7 after the loop cover the last MFMA's result latency before the
+// accumulators are read back.
 //
 // Build and run (one MI355X): `python -m paged_kv_attention_slot_amd.build
 // --probe` writes _build/valu_mfma_cost_probe; run it with no arguments.
@@ -64,7 +68,7 @@ __device__ __forceinline__ void vop(float (&x)[16], int i, float c) {
 // NM = 0: vector instructions alone (8 groups of NV); else NM MFMAs, each
 // followed by NV vector instructions.  out holds one value per lane, so
 // nothing is optimised away; it is never read.
-template <int NM, int K, int NV>
+template <int NM, int K, int NV, bool AG>
 __global__ __launch_bounds__(256, 2) void cost_kernel(float *out, float seed) {
   const int lane = threadIdx.x & 63;
   bf16x8_t a, b;
@@ -93,13 +97,17 @@ __global__ __launch_bounds__(256, 2) void cost_kernel(float *out, float seed) {
     } else {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
+        if constexpr (AG)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[m & 3]) : "v"(a), "v"(b));
+        else
+          acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
 #pragma unroll
         for (int v = 0; v < NV; ++v) vop<K>(x, (m * NV + v) & 15, c);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
+  if constexpr (AG) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -110,17 +118,17 @@ __global__ __launch_bounds__(256, 2) void cost_kernel(float *out, float seed) {
   out[static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x] = s;
 }
 
-template <int NM, int K, int NV>
+template <int NM, int K, int NV, bool AG = false>
 void run_case(int cus, float *out) {
   for (int per_simd = 1; per_simd <= 2; ++per_simd) {
     const int grid = cus * per_simd;   // out holds 2 * cus * 256 floats
-    cost_kernel<NM, K, NV><<<grid, 256>>>(out, 1.f);   // warm-up
+    cost_kernel<NM, K, NV, AG><<<grid, 256>>>(out, 1.f);   // warm-up
     CHECK(hipGetLastError());
     hipEvent_t e0, e1;
     CHECK(hipEventCreate(&e0));
     CHECK(hipEventCreate(&e1));
     CHECK(hipEventRecord(e0, nullptr));
-    cost_kernel<NM, K, NV><<<grid, 256>>>(out, 1.f);
+    cost_kernel<NM, K, NV, AG><<<grid, 256>>>(out, 1.f);
     CHECK(hipGetLastError());
     CHECK(hipEventRecord(e1, nullptr));
     CHECK(hipEventSynchronize(e1));
@@ -133,8 +141,8 @@ void run_case(int cus, float *out) {
       std::printf("%d wave/SIMD  %-8s alone        8 per group : %6.2f ns per group per SIMD\n", per_simd,
                   kNames[K], ns);
     else
-      std::printf("%d wave/SIMD  %-8s beside MFMA  %d per MFMA  : %6.2f ns per MFMA per SIMD\n", per_simd,
-                  NV ? kNames[K] : "(none)", NV, ns);
+      std::printf("%d wave/SIMD  %-8s beside MFMA%s %d per MFMA  : %6.2f ns per MFMA per SIMD\n", per_simd,
+                  NV ? kNames[K] : "(none)", AG ? "(agpr)" : "      ", NV, ns);
     std::fflush(stdout);
     CHECK(hipEventDestroy(e0));
     CHECK(hipEventDestroy(e1));
@@ -164,6 +172,14 @@ int main() {
   run_case<16, kDot2, 4>(cus, out);
   run_case<16, kFmaExp, 4>(cus, out);
   run_case<16, kFmaExp, 8>(cus, out);
+  run_case<16, kFma, 0, true>(cus, out);
+  run_case<16, kFma, 4, true>(cus, out);
+  run_case<16, kFma, 8, true>(cus, out);
+  run_case<16, kExp, 4, true>(cus, out);
+  run_case<16, kFmaExp, 8, true>(cus, out);
+  run_case<16, kPack, 4, true>(cus, out);
+  run_case<16, kMax3, 4, true>(cus, out);
+  run_case<16, kDot2, 4, true>(cus, out);
   CHECK(hipFree(out));
   std::printf("done\n");
   return 0;

@@ -16,7 +16,7 @@
 //
 // Kinds: fma (v_fma_f32), exp (v_exp_f32), pack (v_cvt_pk_bf16_f32),
 // max3 (v_maximum3_f32), dot2 (v_dot2_f32_bf16 against (1, 1)), and
-// fma+exp (alternating).
+// fma+exp (alternating), and exp_f16 (v_exp_f16, written in assembly).
 // "(agpr)" lines: the same MFMAs written in assembly with their
 // accumulators in AGPRs (the compiler's form keeps them in VGPRs); four
 // s_nop 7 after the loop cover the last MFMA's result latency before the
@@ -43,8 +43,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kIters = 512;
-enum Kind { kFma, kExp, kPack, kMax3, kDot2, kFmaExp };
-const char *const kNames[] = {"fma", "exp", "pack", "max3", "dot2", "fma+exp"};
+enum Kind { kFma, kExp, kPack, kMax3, kDot2, kFmaExp, kExp16 };
+const char *const kNames[] = {"fma", "exp", "pack", "max3", "dot2", "fma+exp", "exp_f16"};
 
 template <int K>
 __device__ __forceinline__ void vop(float (&x)[16], int i, float c) {
@@ -60,8 +60,12 @@ __device__ __forceinline__ void vop(float (&x)[16], int i, float c) {
   } else if constexpr (K == kDot2) {
     const bf16x2_t one2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
     x[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[(i + 3) & 15]), one2, x[i], false);
-  } else {
+  } else if constexpr (K == kFmaExp) {
     x[i] = (i & 1) ? __builtin_amdgcn_exp2f(x[i]) : __builtin_fmaf(x[i], c, -0.5f);
+  } else {
+    float r;   // the half-precision exp2 on the low half of the register
+    asm volatile("v_exp_f16 %0, %1" : "=v"(r) : "v"(x[i]));
+    x[i] = r;
   }
 }
 
@@ -160,6 +164,7 @@ int main() {
   run_case<0, kMax3, 8>(cus, out);
   run_case<0, kDot2, 8>(cus, out);
   run_case<0, kFmaExp, 8>(cus, out);
+  run_case<0, kExp16, 8>(cus, out);
   run_case<16, kFma, 0>(cus, out);
   run_case<16, kFma, 4>(cus, out);
   run_case<16, kFma, 8>(cus, out);
@@ -172,6 +177,7 @@ int main() {
   run_case<16, kDot2, 4>(cus, out);
   run_case<16, kFmaExp, 4>(cus, out);
   run_case<16, kFmaExp, 8>(cus, out);
+  run_case<16, kExp16, 4>(cus, out);
   run_case<16, kFma, 0, true>(cus, out);
   run_case<16, kFma, 4, true>(cus, out);
   run_case<16, kFma, 8, true>(cus, out);

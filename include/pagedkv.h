@@ -86,9 +86,11 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 } pkv_dtype;
  * Queries (q_packed) on an 8-bit pool are bf16 and are used as fp16 (exact
  * for |q| below 65504; magnitudes under 2^-14 keep fp16's subnormal
  * precision); output is float32 or bf16.
- * On an 8-bit pool, multi-row segments (prompt chunks, drafts) run row by
- * row on the decode path: correct for any segment, but each row reads its
- * own window, so long chunks cost far more HBM traffic than on bf16. */
+ * On an 8-bit pool, multi-row segments (prompt chunks, drafts) run on the
+ * prompt-chunk kernel's 8-bit form: each staged tile's codes are converted
+ * once per workgroup into fp16 tiles (code c as the fp16 value 1152 + c, the
+ * constant removed afterwards), so every (row, head) pair of a 128-pair row
+ * tile shares one read of the window. */
 typedef struct {
   void *k;              /* device [num_blocks][num_kv_heads][block_size][head_dim] */
   void *v;              /* device, same shape and dtype as k                        */

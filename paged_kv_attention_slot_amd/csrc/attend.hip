@@ -28,8 +28,9 @@ bool pool_supported(const pkv_pool *p) {
   return p->block_size == kBlockTokens && (p->head_dim == 64 || p->head_dim == 128);
 }
 
-// Multi-row segments go to the bf16 MFMA kernel when that shape is built;
-// otherwise (fp32 pools) they take the decode path row by row.
+// Multi-row segments go to the chunk kernels (bf16 pools, and 8-bit pools
+// through fp16 tiles) when that shape is built; otherwise (fp32 pools) they
+// take the decode path row by row.
 bool multirow_on_decode_path(int32_t dtype, int32_t head_dim, int32_t group, int32_t max_query_len) {
   return max_query_len > 1 && !chunk_supported(dtype, head_dim, group);
 }

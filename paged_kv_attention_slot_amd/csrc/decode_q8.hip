@@ -15,7 +15,10 @@
 // column groups of one partition per workgroup, one per wavefront: a tile is
 // staged and its V codes converted once for all of them (two barriers per
 // tile), and each wavefront stops at its own rows' last key.  A row keeps
-// partials only for the partitions up to its own position.
+// partials only for the partitions up to its own position.  (Default builds
+// give multi-row segments to chunk_q8_kernel in chunk.hip, which shares one
+// converted tile among 128 (row, head) pairs; this form serves them only
+// with PKV_CHUNK_Q8=0.)
 //   * the K and V code tiles (16 x head_dim bytes each) and their 2 x 16
 //     scales go from HBM straight into LDS staging (global_load_lds_dwordx4
 //     for codes, one global_load_lds_dword for the scales), S tiles in

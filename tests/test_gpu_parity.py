@@ -603,8 +603,8 @@ def test_q8_copy_on_write_and_gather(gpu_available):
 @pytest.mark.parametrize("case", [4, 5, 6])
 @pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 40, 8)])
 def test_q8_multirow_edge_cases(case, d, hq, hkv, gpu_available):
-    """Multi-row segments on an 8-bit pool (row by row on the decode path):
-    tiny prompts, drafts, and chunks whose rows span several partitions."""
+    """Multi-row segments on an 8-bit pool (the chunk kernel's 8-bit form):
+    tiny prompts, drafts, and chunks whose rows span several key ranges."""
     _log(f"q8 multirow case {case} D{d} {hq}/{hkv}")
     w = _q8_workload(EDGE_SEQS[case], d, hq, hkv, seed=70 + case)
     eng, outs = _run_gpu(w)
@@ -616,7 +616,7 @@ def test_q8_multirow_edge_cases(case, d, hq, hkv, gpu_available):
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "mixed_step"])
 def test_q8_config5(fused, gpu_available):
     """Config 5 on an 8-bit pool: 16-row drafts, then rollback, slot reuse
-    and a 3000-row prompt, all row by row."""
+    and a 3000-row prompt, all on the chunk kernel's 8-bit form."""
     _log(f"q8 config 5 fused={fused}")
     w = _workload("5q")
     eng, outs = _run_gpu(w, fused=fused)

@@ -60,8 +60,8 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
         step.num_slots = 1
         step.scale = bad
         assert lib.pkv_mixed_step(ctypes.byref(step), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
-    # 8-bit pools: scales required; multi-row segments go row by row, whose
-    # split-context partials need workspace
+    # 8-bit pools: scales required; a long multi-row segment's key-range
+    # partials need workspace
     d8 = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, pk.PKV_I8, 16)
     d8_noscale = pk.binding.PoolDesc(16, 16, 10, 16, 2, 64, pk.PKV_I8)
     assert lib.pkv_paged_attend(16, 4, 4, 16, 16, 16, 1, 16, 16, 1, 1000, 4, 5000, ctypes.byref(d8), 1.0, 16, 0,

@@ -111,6 +111,12 @@ def lib():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        # pkv_lower_step_cow once more with its arrays as plain addresses
+        # (a staging buffer's base plus offsets: no per-call pointer objects)
+        raw = handle["pkv_lower_step_cow"]
+        raw.restype = _i32
+        raw.argtypes = [_p, _i32, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _pi32]
+        handle.lower_step_cow_raw = raw
         _LIB = handle
     return _LIB
 
@@ -393,6 +399,18 @@ class BlockAllocator:
         out = np.zeros(max(info[1], 1), dtype=np.int32)
         _check(self._lib.pkv_slot_table(self._h, int(slot), _ptr_i32(out), len(out)), "pkv_slot_table")
         return out[:info[1]].tolist()
+
+    def lower_step_raw(self, n, slots_addr, news_addr, sm_addr, sm_len, qs_addr, ql_addr, rts_addr, cl_addr,
+                       csrc_addr, cdst_addr, copy_cap):
+        """pkv_lower_step_cow on raw host addresses of int32 arrays (no block
+        tables out): slots / news [n] in, slot_mapping [sm_len], query_start /
+        query_len / row_to_slot [n], context_lens [max_slots] and copy_src /
+        copy_dst [copy_cap] out.  Returns the number of copy pairs."""
+        ncopy = ctypes.c_int32(0)
+        _check(self._lib.lower_step_cow_raw(self._h, n, slots_addr, news_addr, sm_addr, sm_len, qs_addr, ql_addr,
+                                            rts_addr, cl_addr, None, csrc_addr, cdst_addr, copy_cap,
+                                            ctypes.byref(ncopy)), "pkv_lower_step_cow")
+        return ncopy.value
 
     def lower_step(self, entries, out=None):
         """entries: [(slot, n_new)] in packed order -> dict of host int32 arrays,

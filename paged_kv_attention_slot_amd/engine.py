@@ -38,22 +38,33 @@ import numpy as np
 from . import binding as B
 
 
+_DEV_FIELDS = ("slot_mapping", "query_start", "query_len", "row_to_slot", "context_lens", "copy_src", "copy_dst")
+
+
 @dataclass
 class StepMeta:
+    """A lowered step.  The device arrays - slot_mapping [T], query_start /
+    query_len / row_to_slot [B], context_lens [max_slots], copy_src /
+    copy_dst [num_copies] (copy-on-write pairs), all int32 - are views of the
+    staged device copy, made on first use (the one-call path never needs
+    them)."""
     host: dict                # host int32 arrays from the lowering
-    slot_mapping: object      # device int32 [T]
-    query_start: object       # device int32 [B]
-    query_len: object
-    row_to_slot: object
-    context_lens: object      # device int32 [max_slots]
-    copy_src: object          # device int32 [num_copies]: copy-on-write pairs
-    copy_dst: object
+    dev: object               # device int32 staging buffer holding the arrays
+    offs: tuple               # start of each array in `dev`, in _DEV_FIELDS order, then the end
     stream: object            # handle of the stream the step was lowered on
     total_q: int
     max_query_len: int
     max_context_len: int
     num_copies: int = 0
     copy_off: int = 0         # offset of copy_src in the staged metadata
+
+    def __getattr__(self, name):
+        if name in _DEV_FIELDS:
+            i = _DEV_FIELDS.index(name)
+            view = self.dev[self.offs[i]:self.offs[i + 1]]
+            setattr(self, name, view)
+            return view
+        raise AttributeError(name)
 
 
 @dataclass
@@ -75,6 +86,7 @@ class _Staging:
         self.host = torch.empty(n, dtype=torch.int32, pin_memory=True)
         self.dev = torch.empty(n, dtype=torch.int32, device=device)
         self.np = self.host.numpy()
+        self.addr = self.host.data_ptr()
         self.own = torch.cuda.Event()   # this buffer's event (split-call steps)
         self.copied = self.own          # the event that marks the buffer's last reader done
         self.used = False
@@ -107,6 +119,7 @@ class PagedKVEngine:
         self._ws_key = None
         self._ws_bytes = 0
         self._aux = None        # second stream and fork/join events lent to pkv_mixed_step
+        self._entries = None    # the last step plan, its int32 arrays and their addresses
 
     # -- slot lifecycle (host allocator) --------------------------------
     def acquire(self, slot):
@@ -180,43 +193,56 @@ class PagedKVEngine:
         s, fork, join = self._aux
         return s.cuda_stream, fork.handle.value, join.handle.value
 
+    def _plan_arrays(self, entries):
+        """The plan's slots and new-token counts as int32 arrays (reused while
+        the plan is unchanged, as on a run of decode steps) and their total."""
+        c = self._entries
+        if c is None or not isinstance(entries, list) or c[0] != entries:
+            slots = np.ascontiguousarray([e[0] for e in entries], dtype=np.int32)
+            news = np.ascontiguousarray([e[1] for e in entries], dtype=np.int32)
+            c = ([tuple(e) for e in entries], slots, news, int(news.sum()) if len(news) else 0,
+                 slots.ctypes.data, news.ctypes.data)
+            self._entries = c
+        return c[1], c[2], c[3], c[4], c[5]
+
     def _lower_host(self, entries):
         """Lower the step into the next pinned staging buffer (host only)."""
-        torch = self.torch
-        stream = torch.cuda.current_stream(self.device)
+        stream = self.torch.cuda.current_stream(self.device)
         nseg = len(entries)
-        t = int(sum(e[1] for e in entries))
+        slots, news, t, slots_addr, news_addr = self._plan_arrays(entries)
         # packed metadata: slot_mapping | query_start | query_len | row_to_slot | context_lens
         #                  | copy-on-write room (up to one pair per entry)
-        offs = [int(x) for x in np.cumsum([0, t, nseg, nseg, nseg, self.max_slots, 2 * nseg])]
-        st = self._stage(offs[-1])
+        o1 = t
+        o2 = o1 + nseg
+        o3 = o2 + nseg
+        o4 = o3 + nseg
+        o5 = o4 + self.max_slots
+        st = self._stage(o5 + 2 * nseg)
         h = st.np
-        host = dict(slot_mapping=h[offs[0]:offs[1]], query_start=h[offs[1]:offs[2]],
-                    query_len=h[offs[2]:offs[3]], row_to_slot=h[offs[3]:offs[4]],
-                    context_lens=h[offs[4]:offs[5]])
         free_before = self.alloc.free_blocks()
-        self.alloc.lower_step(entries, out=host)
+        a = st.addr
+        nc = self.alloc.lower_step_raw(nseg, slots_addr, news_addr, a, t, a + 4 * o1, a + 4 * o2,
+                                       a + 4 * o3, a + 4 * o4, a + 4 * o5, a + 4 * (o5 + nseg), nseg)
         if self.alloc.free_blocks() != free_before:
             self._tables_dirty = True     # new blocks, copy-on-write blocks included
-        nc = len(host["copy_src"])
-        cs, cd = offs[5], offs[5] + nc    # copy_src [nc] then copy_dst [nc]
-        h[cs:cd] = host["copy_src"]
-        h[cd:cd + nc] = host["copy_dst"]
-        offs[6] = offs[5] + 2 * nc
+        # copy_src [nc] then copy_dst [nc]
+        cs, cd = o5, o5 + nc
+        if nc:
+            h[cd:cd + nc] = h[o5 + nseg:o5 + nseg + nc].copy()
         if self._tables_dirty:
             self._refresh_tables()
-        d = st.dev
-        ql = host["query_len"]
-        ctx = host["context_lens"][host["row_to_slot"]] if nseg else np.zeros(0, np.int32)
-        snapshot = {k: np.array(v) for k, v in host.items()}
+        row_to_slot = h[o3:o4]
+        context_lens = h[o4:o5]
+        snapshot = dict(slot_mapping=h[:o1].copy(), query_start=h[o1:o2].copy(), query_len=h[o2:o3].copy(),
+                        row_to_slot=row_to_slot.copy(), context_lens=context_lens.copy(),
+                        copy_src=h[cs:cd].copy(), copy_dst=h[cd:cd + nc].copy())
         snapshot["block_tables"] = self.h_block_tables
-        meta = StepMeta(host=snapshot, slot_mapping=d[offs[0]:offs[1]], query_start=d[offs[1]:offs[2]],
-                        query_len=d[offs[2]:offs[3]], row_to_slot=d[offs[3]:offs[4]],
-                        context_lens=d[offs[4]:offs[5]], copy_src=d[cs:cd], copy_dst=d[cd:cd + nc],
-                        stream=B.ctypes.c_void_p(stream.cuda_stream),
-                        total_q=t, max_query_len=int(ql.max()) if nseg else 0,
-                        max_context_len=int(ctx.max()) if nseg else 0, num_copies=nc, copy_off=cs)
-        return meta, st, offs, stream
+        max_q = int(news.max()) if nseg else 0
+        max_ctx = int(context_lens[row_to_slot].max()) if nseg else 0
+        offs = (0, o1, o2, o3, o4, cs, cd, cd + nc)
+        meta = StepMeta(host=snapshot, dev=st.dev, offs=offs, stream=B.ctypes.c_void_p(stream.cuda_stream),
+                        total_q=t, max_query_len=max_q, max_context_len=max_ctx, num_copies=nc, copy_off=cs)
+        return meta, st, offs[:6] + (cd + nc,), stream
 
     def lower(self, entries) -> StepMeta:
         """Lower the step and copy its metadata to the device (stream order)."""

@@ -162,7 +162,27 @@ def test_mixed_step_rejects_understated_bounds_and_half_a_stream_pair():
     assert lib.pkv_mixed_step(ctypes.byref(st), ctypes.byref(d4), None) == pk.binding.PKV_ERR_INVALID_ARG
 
 
-def _random_ops(seed, n_ops=300, adopt=False):
+def _lower_raw(al, entries, max_slots):
+    """The engine's packed lowering (BlockAllocator.lower_step_raw into one
+    int32 buffer at plain addresses: slot_mapping | query_start | query_len |
+    row_to_slot | context_lens | copy_src room | copy_dst room), unpacked."""
+    n = len(entries)
+    slots = np.ascontiguousarray([e[0] for e in entries], dtype=np.int32)
+    news = np.ascontiguousarray([e[1] for e in entries], dtype=np.int32)
+    t = int(news.sum())
+    o = np.cumsum([0, t, n, n, n, max_slots, n, n])
+    buf = np.full(int(o[-1]) + 8, -7, dtype=np.int32)   # poisoned, with a tail that must stay untouched
+    a = buf.ctypes.data
+    nc = al.lower_step_raw(n, slots.ctypes.data, news.ctypes.data, a, t, *(a + 4 * int(x) for x in o[1:7]), n)
+    assert (buf[int(o[-1]):] == -7).all()
+    keys = ("slot_mapping", "query_start", "query_len", "row_to_slot", "context_lens")
+    got = {k: buf[o[i]:o[i + 1]].copy() for i, k in enumerate(keys)}
+    got["copy_src"] = buf[o[5]:o[5] + nc].copy()
+    got["copy_dst"] = buf[o[6]:o[6] + nc].copy()
+    return got
+
+
+def _random_ops(seed, n_ops=300, adopt=False, raw=False):
     rng = np.random.default_rng(seed)
     nb, bs, slots, maxb = 64, 16, 8, 12
     order = rng.permutation(nb).astype(np.int32)
@@ -220,13 +240,15 @@ def _random_ops(seed, n_ops=300, adopt=False):
                 ok = True
             except OracleNoSpace:
                 ok = False
+            lower = (lambda e: _lower_raw(ours, e, slots)) if raw else ours.lower_step
             if ok:
-                got = ours.lower_step(entries)
+                got = lower(entries)
                 for k in want:
-                    assert np.array_equal(got[k], want[k]), k
+                    if k in got or not raw:
+                        assert np.array_equal(got[k], want[k]), k
             else:
                 with pytest.raises(pk.NoSpace):
-                    ours.lower_step(entries)
+                    lower(entries)
         # full state comparison after every op
         assert ours.free_blocks() == ref.free_count()
         assert [ours.block_refs(b) for b in range(nb)] == ref.refs
@@ -248,6 +270,15 @@ def test_adoption_and_copy_on_write_match_oracle(seed):
     """Shared prefixes: adopt, reference counts, and the copy-on-write pairs
     of each lowering (compared key by key with the oracle's)."""
     _random_ops(100 + seed, adopt=True)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("adopt", [False, True], ids=["plain", "shared_prefixes"])
+def test_raw_address_lowering_matches_oracle(seed, adopt):
+    """The engine's lowering path (plain addresses into one packed buffer)
+    gives the oracle's arrays and copy-on-write pairs, and writes nothing
+    past its arrays."""
+    _random_ops(200 + seed, adopt=adopt, raw=True)
 
 
 def test_adoption_errors_and_plain_lowering_refuses_copies():

@@ -417,3 +417,22 @@ def test_noalloc_rejects_steps_beyond_its_scratch_without_gpu():
     # argument errors come first (a bad scale), as for pkv_paged_attend
     assert lib.pkv_paged_attend_noalloc(16, 1000, 32, 16, 16, 16, 1000, 16, 16, 1000, 2048, 1, 32768,
                                         ctypes.byref(d), -1.0, 16, 0, None) == pk.binding.PKV_ERR_INVALID_ARG
+
+
+def test_step_meta_device_views_follow_offsets():
+    """StepMeta's device arrays are views of the staged buffer at the offsets
+    the lowering recorded (made on first use)."""
+    import torch
+    from paged_kv_attention_slot_amd.engine import StepMeta
+    dev = torch.arange(40, dtype=torch.int32)
+    offs = (0, 3, 5, 7, 9, 17, 19, 21)      # T = 3, B = 2, 8 slots, 2 copy pairs
+    meta = StepMeta(host={}, dev=dev, offs=offs, stream=None, total_q=3, max_query_len=2, max_context_len=9,
+                    num_copies=2, copy_off=17)
+    names = ("slot_mapping", "query_start", "query_len", "row_to_slot", "context_lens", "copy_src", "copy_dst")
+    for i, name in enumerate(names):
+        view = getattr(meta, name)
+        assert view.tolist() == list(range(offs[i], offs[i + 1])), name
+        assert view.data_ptr() == dev.data_ptr() + 4 * offs[i]
+        assert getattr(meta, name) is view          # made once
+    with pytest.raises(AttributeError):
+        meta.not_a_field

@@ -180,8 +180,10 @@ class StreamEvent:
     created with hipEventDisableTiming | hipEventDisableSystemFence, so a
     record takes no system-scope cache writeback and invalidate (the device
     work that waits on it still follows the recorded work, and sees its
-    writes).  Not for host-side waits on the work it records.  Made on the
-    HIP runtime PyTorch loaded, so torch stream handles apply."""
+    writes).  Host-side waits on it (query, synchronize) tell that the
+    recorded work has finished, not that its device writes are visible to
+    the host.  Made on the HIP runtime PyTorch loaded, so torch stream
+    handles apply."""
 
     _FLAGS = 0x2 | 0x20000000   # hipEventDisableTiming | hipEventDisableSystemFence
 
@@ -194,6 +196,9 @@ class StreamEvent:
             rt = ctypes.CDLL(path)
             rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_p), ctypes.c_uint]
             rt.hipEventDestroy.argtypes = [_p]
+            rt.hipEventRecord.argtypes = [_p, _p]
+            rt.hipEventQuery.argtypes = [_p]
+            rt.hipEventSynchronize.argtypes = [_p]
             _HIP_RT = rt
         self._rt = _HIP_RT
         self.handle = _p()
@@ -203,6 +208,20 @@ class StreamEvent:
     def __del__(self):
         if getattr(self, "handle", None):
             self._rt.hipEventDestroy(self.handle)
+
+    # Host-side waits, for work that only reads host memory (a pinned staging
+    # buffer may be rewritten once the kernels that read it have finished;
+    # no device writes need to become visible to the host).
+    def record(self, stream):
+        if self._rt.hipEventRecord(self.handle, _p(stream.cuda_stream)) != 0:
+            raise PagedKVError("hipEventRecord failed")
+
+    def query(self):
+        return self._rt.hipEventQuery(self.handle) == 0       # hipSuccess: the recorded work is done
+
+    def synchronize(self):
+        if self._rt.hipEventSynchronize(self.handle) != 0:
+            raise PagedKVError("hipEventSynchronize failed")
 
 
 def _dptr(t):

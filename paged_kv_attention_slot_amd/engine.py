@@ -283,7 +283,7 @@ class PagedKVEngine:
         # recorded after this step or a later one on the same stream, completes
         if self._group_event is None or self._group_stream != prep.stream:
             self._close_group()
-            self._group_event = self.torch.cuda.Event()
+            self._group_event = B.StreamEvent()     # no system fence: the step's kernels only read the buffer
             self._group_stream = prep.stream
         prep.staging.copied = self._group_event
         prep.staging.used = True

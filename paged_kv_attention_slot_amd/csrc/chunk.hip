@@ -44,6 +44,12 @@
 #ifndef PKV_CHUNK_Q8
 #define PKV_CHUNK_Q8 1
 #endif
+// The 8-bit form's fp16 tiles hold the codes themselves (1: the constant
+// 1152 comes off each converted pair in fp16, exactly) or 1152 + code (0:
+// the constant comes off every score and off O at the end).
+#ifndef PKV_CHUNK_Q8_EXACT_CODES
+#define PKV_CHUNK_Q8_EXACT_CODES 1
+#endif
 
 // Unmasked tiles four at a time (one turn of the 4-stage ring), so that each
 // tile's stage, and with it every LDS address of the tile, is a constant.
@@ -651,16 +657,16 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
 // the work split, row tiles, key ranges and partials of chunk_kernel, with
 // each staged tile converted once per workgroup into fp16 tiles, exactly.
 // Code c becomes the fp16 value 1152 + c (the pattern 0x6400 | (c + 128), one
-// byte permute per two codes), so the products run on
-// v_mfma_f32_32x32x16_f16 with Q in fp16 (exact inside fp16's range), and
-// the constant comes out afterwards:
-//   * a score is (S - 1152 sum(q)) x k_scale of its key, formed before the
-//     row max;
+// byte permute per two codes) and then c itself (one packed fp16 subtract of
+// 1152 per two codes, exact), so the products run on v_mfma_f32_32x32x16_f16
+// with Q in fp16 (exact inside fp16's range):
+//   * a score is S x k_scale of its key, formed before the row max;
 //   * P' = fp16(p x v_scale) multiplies the V codes, so O weights the stored
 //     value code x v_scale by P' / v_scale; the row sum adds exactly that
-//     weight (P' times the reciprocal of v_scale), and O loses
-//     1152 x sum(P') at the end.  A zero V row (scale 0, codes 0) takes
-//     scale 1.
+//     weight (P' times the reciprocal of v_scale).  A zero V row (scale 0,
+//     codes 0) takes scale 1.
+// (With PKV_CHUNK_Q8_EXACT_CODES=0 the tiles keep 1152 + c: a score is then
+// (S - 1152 sum(q)) x k_scale and O loses 1152 x sum(P') at the end.)
 // Three raw stages (the tile's codes and its blocks' scale lines, direct to
 // LDS) feed three converted stages (fp16 K and V tiles and per-token scale
 // factors): while the scores of tile rt + 1 and the weights of tile rt are
@@ -668,11 +674,18 @@ __global__ __launch_bounds__(256, Ring<D>::kMinWaves) void chunk_kernel(AttendAr
 typedef _Float16 halfx8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx2_t __attribute__((ext_vector_type(2)));
 
-// Four int8 codes (one dword) -> two dwords of fp16 (1152 + code).
+// Four int8 codes (one dword) -> two dwords of fp16 (1152 + code, or the
+// code itself).
 __device__ __forceinline__ uint2 q8c_codes_to_f16x4(unsigned w) {
   const unsigned u = w ^ 0x80808080u;       // code + 128 as unsigned bytes
-  return make_uint2(__builtin_amdgcn_perm(0x64646464u, u, 0x05010400u),
-                    __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u));
+  uint2 r = make_uint2(__builtin_amdgcn_perm(0x64646464u, u, 0x05010400u),
+                       __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u));
+  if constexpr (PKV_CHUNK_Q8_EXACT_CODES) {
+    const halfx2_t bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
+    r.x = __builtin_bit_cast(unsigned, __builtin_bit_cast(halfx2_t, r.x) - bias);
+    r.y = __builtin_bit_cast(unsigned, __builtin_bit_cast(halfx2_t, r.y) - bias);
+  }
+  return r;
 }
 
 template <int D>
@@ -758,7 +771,7 @@ __global__ __launch_bounds__(256, 2) void chunk_q8_kernel(AttendArgs a, int G) {
   const bool wave_live = mw < mtot;                  // the wavefront has M-rows of the segment
 
   // Q operand in fp16: lane holds dims 16 ks + 8 hh .. + 7 of its M-row;
-  // qbias = 1152 x the sum of the row's fp16 values (both halves).
+  // with biased codes, qbias = 1152 x the sum of the row's fp16 values (both halves).
   const float c_log2 = a.scale_log2;
   const float slack_raw = PKV_CHUNK_RESCALE_SLACK / c_log2;
   const int m = mw + l32;
@@ -783,14 +796,14 @@ __global__ __launch_bounds__(256, 2) void chunk_q8_kernel(AttendArgs a, int G) {
         const _Float16 h1 = static_cast<_Float16>(__uint_as_float(ww[i] & 0xFFFF0000u));
         qv[ks][2 * i] = h0;
         qv[ks][2 * i + 1] = h1;
-        qbias += static_cast<float>(h0) + static_cast<float>(h1);
+        if constexpr (!PKV_CHUNK_Q8_EXACT_CODES) qbias += static_cast<float>(h0) + static_cast<float>(h1);
       }
     }
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(qbias), __float_as_uint(qbias), false, false);
     qbias = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * 1152.f;
   }
 
-  // Softmax state as in chunk_kernel; csum: this half's sum of the fp16 P'.
+  // Softmax state as in chunk_kernel; csum: this half's sum of the fp16 P' (biased codes only).
   float m_run = -FLT_MAX, ref = 0.f, lsum = 0.f, csum = 0.f;
   const floatx16_t zero16 = {};
   floatx16_t o[kDT];
@@ -916,10 +929,17 @@ __global__ __launch_bounds__(256, 2) void chunk_q8_kernel(AttendArgs a, int G) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 k4 = factor4(cslot, 0, tt, j);
-        sc[tt][4 * j] = (sc[tt][4 * j] - qbias) * k4.x;
-        sc[tt][4 * j + 1] = (sc[tt][4 * j + 1] - qbias) * k4.y;
-        sc[tt][4 * j + 2] = (sc[tt][4 * j + 2] - qbias) * k4.z;
-        sc[tt][4 * j + 3] = (sc[tt][4 * j + 3] - qbias) * k4.w;
+        if constexpr (PKV_CHUNK_Q8_EXACT_CODES) {
+          sc[tt][4 * j] *= k4.x;
+          sc[tt][4 * j + 1] *= k4.y;
+          sc[tt][4 * j + 2] *= k4.z;
+          sc[tt][4 * j + 3] *= k4.w;
+        } else {
+          sc[tt][4 * j] = (sc[tt][4 * j] - qbias) * k4.x;
+          sc[tt][4 * j + 1] = (sc[tt][4 * j + 1] - qbias) * k4.y;
+          sc[tt][4 * j + 2] = (sc[tt][4 * j + 2] - qbias) * k4.z;
+          sc[tt][4 * j + 3] = (sc[tt][4 * j + 3] - qbias) * k4.w;
+        }
       }
     if (masked && rt * T + T - 1 > wave_pos0) {
 #pragma unroll
@@ -1003,7 +1023,8 @@ __global__ __launch_bounds__(256, 2) void chunk_q8_kernel(AttendArgs a, int G) {
         const _Float16 ph = static_cast<_Float16>(fast_exp2(fmaf(cur[w / 16][w % 16], c_log2, -ref)) * vsk);
         hp[w] = ph;
         lsum = fmaf(static_cast<float>(ph), rvk, lsum);           // the weight P' / v_scale
-        if (w % 2 == 1) csum = __builtin_amdgcn_fdot2(halfx2_t{hp[w - 1], ph}, one2, csum, false);
+        if (!PKV_CHUNK_Q8_EXACT_CODES && w % 2 == 1)
+          csum = __builtin_amdgcn_fdot2(halfx2_t{hp[w - 1], ph}, one2, csum, false);
         if (w % 8 == 7)
           pb[w / 8] = halfx8_t{hp[w - 7], hp[w - 6], hp[w - 5], hp[w - 4], hp[w - 3], hp[w - 2], hp[w - 1], ph};
       }
@@ -1095,14 +1116,16 @@ __global__ __launch_bounds__(256, 2) void chunk_q8_kernel(AttendArgs a, int G) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain before the stages are reused
   }
 
-  // Both halves' sums; O loses 1152 x sum(P'); then normalise or store the
+  // Both halves' sums (and, with the biased codes, O loses 1152 x sum(P')); then normalise or store the
   // partial of this key range.
   const auto swl = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
   const float lt = __uint_as_float(swl[0]) + __uint_as_float(swl[1]);
-  const auto swc = __builtin_amdgcn_permlane32_swap(__float_as_uint(csum), __float_as_uint(csum), false, false);
-  const float ct = (__uint_as_float(swc[0]) + __uint_as_float(swc[1])) * 1152.f;
+  if constexpr (!PKV_CHUNK_Q8_EXACT_CODES) {
+    const auto swc = __builtin_amdgcn_permlane32_swap(__float_as_uint(csum), __float_as_uint(csum), false, false);
+    const float ct = (__uint_as_float(swc[0]) + __uint_as_float(swc[1])) * 1152.f;
 #pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) o[dt] -= ct;
+    for (int dt = 0; dt < kDT; ++dt) o[dt] -= ct;
+  }
   if (!valid) return;
   if (partial_out) {
     const int64_t pidx = static_cast<int64_t>(g) * a.chunk_slots + part_base + m * cs.splits + split;

@@ -88,9 +88,8 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 } pkv_dtype;
  * precision); output is float32 or bf16.
  * On an 8-bit pool, multi-row segments (prompt chunks, drafts) run on the
  * prompt-chunk kernel's 8-bit form: each staged tile's codes are converted
- * once per workgroup into fp16 tiles (code c as the fp16 value 1152 + c, the
- * constant removed afterwards), so every (row, head) pair of a 128-pair row
- * tile shares one read of the window. */
+ * once per workgroup into fp16 tiles holding the codes exactly, so every
+ * (row, head) pair of a 128-pair row tile shares one read of the window. */
 typedef struct {
   void *k;              /* device [num_blocks][num_kv_heads][block_size][head_dim] */
   void *v;              /* device, same shape and dtype as k                        */
